@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused VQ dequant-matmul on one MI355X.
+
+One step = the whole hot path over one batch of the dense MLP trio workload
+(gate/up [17408][5120], down [5120][17408], d=2, K=256, fp16 scale per 64
+weights = 4.25 bits per weight):
+  decode : vq_gemv on gate, up, down at T = 1 token
+  prefill: vq_gemm on gate, up, down at T = 2048 tokens
+Inputs are seeded synthetic tensors (codes uniform, codebook N(0, 0.02), scales
+U[0.5, 1.5], x N(0, 1)) already resident in HBM.  The weights are replicated
+so the per-step rotation touches >= 1 GiB and every call streams from HBM, not
+from the 256 MB Infinity Cache.
+
+Prints one JSON line.  `value` is the decode throughput (algorithmic bytes of
+codes + scales + codebook + x + y over the decode kernels' time); prefill
+TFLOP/s and both kernels' roofline fractions ride along.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
+
+WORKLOAD = "dense_mlp_5120x17408_d2k256"
+DECODE_T = 1
+PREFILL_T = 2048
+REPLICAS = 8
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=1024,
+                    help="rows of the gate matrix the CPU oracle sample covers")
+    return ap.parse_args()
+
+
+def tensor_bytes(spec, T):
+    """Algorithmic bytes of one dense call: packed codes + fp16 scales + fp16
+    codebook (once) + fp16 x + fp32 y.  Dequantized weights are never counted."""
+    return (spec.rows * spec.words * 4 + spec.rows * (spec.cols // spec.group) * 2
+            + spec.k * spec.d * 2 + T * spec.cols * 2 + T * spec.rows * 4)
+
+
+def cpu_baseline(arrs, spec, rows):
+    """The oracle as it stands, timed on the host on a bounded sample: the
+    first `rows` rows of the gate matrix at T = 1 (unpack, dequant, float64
+    matmul).  Reported in GB/s of the same algorithmic bytes."""
+    import numpy as np
+    from oracle import vq_oracle as O
+    from vq_dequant_matmul_gemv_amd import synth
+    x = synth.activations((1, spec.cols), "bench-cpu")
+    words = np.ascontiguousarray(arrs["codes"][0, :rows])
+    scales = np.ascontiguousarray(arrs["scales"][0, :rows])
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        O.gemv_ref(words, arrs["codebook"], scales, x, spec.cols, spec.d, spec.log2_k, spec.group)
+        reps += 1
+        if time.perf_counter() - t0 > 10.0 or reps >= 50:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    sub = synth.Spec(rows, spec.cols, spec.d, spec.log2_k, spec.group)
+    gbps = tensor_bytes(sub, 1) / dt / 1e9
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"gate matrix rows 0..{rows - 1} of 17408 (cols 5120, d=2 K=256 g=64), T=1: "
+                      f"unpack + fp16 dequant + float64 matmul, {reps} reps, {dt * 1e3:.1f} ms each"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
+              f"(this build runs on a single MI355X; multi-GPU sharding is design-only)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from vq_dequant_matmul_gemv_amd import binding, synth
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    wl = synth.WORKLOADS[WORKLOAD]
+    names = ["gate", "up", "down"]
+    specs = {n: wl["tensors"][n] for n in names}
+    host = {n: synth.tensor(specs[n], WORKLOAD, n) for n in names}
+    base = {n: binding.VQTensor.from_host(host[n], specs[n]) for n in names}
+    reps = []
+    for r in range(REPLICAS):
+        if r == 0:
+            reps.append(base)
+        else:
+            reps.append({n: binding.VQTensor(base[n].codes.clone(), base[n].codebook.clone(),
+                                             base[n].scales.clone(), specs[n].rows, specs[n].cols,
+                                             specs[n].d, specs[n].log2_k, specs[n].group)
+                         for n in names})
+    xd = {n: torch.from_numpy(synth.activations((DECODE_T, specs[n].cols), WORKLOAD, "xd", n)).to(dev)
+          for n in names}
+    xp = {n: torch.from_numpy(synth.activations((PREFILL_T, specs[n].cols), WORKLOAD, "xp", n)).to(dev)
+          for n in names}
+    yd = {n: torch.empty((DECODE_T, specs[n].rows), dtype=torch.float32, device=dev) for n in names}
+    yp = {n: torch.empty((PREFILL_T, specs[n].rows), dtype=torch.float32, device=dev) for n in names}
+    torch.cuda.synchronize()
+
+    dec_bytes = {n: tensor_bytes(specs[n], DECODE_T) for n in names}
+    pre_flops = {n: 2.0 * PREFILL_T * specs[n].rows * specs[n].cols for n in names}
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    # Each phase of each replica is captured once as a HIP graph, so the three
+    # launches of a phase run back to back on the GPU without host gaps.  A
+    # burst graph of BURST gate GEMVs (and GEMMs), rotating over the replicas,
+    # gives the per-launch kernel duration for the roofline.
+    BURST = 2 * REPLICAS
+
+    def capture(fn_calls):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for fn, w, x, y in fn_calls:
+                fn(w, x, y)
+        return g
+
+    for i in range(REPLICAS):              # warm every code path eagerly first
+        for n in names:
+            binding.gemv(reps[i][n], xd[n], yd[n])
+            binding.gemm(reps[i][n], xp[n], yp[n])
+    torch.cuda.synchronize()
+    g_dec = [capture([(binding.gemv, reps[i][n], xd[n], yd[n]) for n in names]) for i in range(REPLICAS)]
+    g_pre = [capture([(binding.gemm, reps[i][n], xp[n], yp[n]) for n in names]) for i in range(REPLICAS)]
+    g_burst_dec = capture([(binding.gemv, reps[i % REPLICAS]["gate"], xd["gate"], yd["gate"])
+                           for i in range(BURST)])
+    g_burst_pre = capture([(binding.gemm, reps[i % REPLICAS]["gate"], xp["gate"], yp["gate"])
+                           for i in range(REPLICAS)])
+    torch.cuda.synchronize()
+
+    def step(i, record):
+        marks = []
+        for phase, graphs in (("dec", g_dec), ("pre", g_pre)):
+            if record:
+                a, b = ev(), ev()
+                a.record()
+                graphs[i % REPLICAS].replay()
+                b.record()
+                marks.append((phase, a, b))
+            else:
+                graphs[i % REPLICAS].replay()
+        return marks
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+
+    all_marks = []
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        all_marks += step(args.warmup + i, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # per-launch durations of the dominant kernels (inside the timed process,
+    # same stream, back-to-back launches as in the steps)
+    bursts = {}
+    for key, g, count in (("dec", g_burst_dec, BURST), ("pre", g_burst_pre, REPLICAS)):
+        a, b = ev(), ev()
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        bursts[key] = a.elapsed_time(b) * 1e-3 / count
+
+    dec_time = sum(a.elapsed_time(b) * 1e-3 for p, a, b in all_marks if p == "dec")
+    pre_time = sum(a.elapsed_time(b) * 1e-3 for p, a, b in all_marks if p == "pre")
+    dec_gbps = sum(dec_bytes.values()) * args.steps / dec_time / 1e9
+    pre_tflops = sum(pre_flops.values()) * args.steps / pre_time / 1e12
+
+    gate_dec = bursts["dec"]
+    gate_pre = bursts["pre"]
+    achieved_gbps = dec_bytes["gate"] / gate_dec / 1e9
+    achieved_tflops = pre_flops["gate"] / gate_pre / 1e12
+
+    out = {
+        "metric": "VQ-GEMV effective HBM GB/s (% of peak) at batch 1; prefill VQ-GEMM TFLOP/s",
+        "value": round(dec_gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "decode_tokens": DECODE_T, "prefill_tokens": PREFILL_T,
+                   "tensors": "gate,up [17408x5120]; down [5120x17408]; d=2 K=256 group=64 (4.25 bpw)",
+                   "weight_replicas": REPLICAS, "parallelism": "single GPU"},
+        "pct_of_hbm_peak": round(100 * dec_gbps / HBM_PEAK_GBPS, 2),
+        "decode_ms_per_step": round(dec_time / args.steps * 1e3, 4),
+        "prefill": {"value": round(pre_tflops, 2), "unit": "TFLOP/s",
+                    "pct_of_fp16_mfma_peak": round(100 * pre_tflops / MFMA_F16_PEAK_TFLOPS, 2),
+                    "ms_per_step": round(pre_time / args.steps * 1e3, 4)},
+        "kernel_us": {"gemv_gate_T1": round(gate_dec * 1e6, 2), "gemm_gate_T2048": round(gate_pre * 1e6, 2)},
+        "roofline": {"bound": "hbm", "kernel": "vq_gemv (gate, T=1)",
+                     "achieved": round(achieved_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+        "roofline_prefill": {"bound": "mfma", "kernel": "vq_gemm (gate, T=2048)",
+                             "achieved": round(achieved_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(achieved_tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                             "traffic": None},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(host["gate"], specs["gate"], args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,224 @@
+"""GPU parity against the CPU oracle at sizes the oracle finishes in seconds.
+
+Every geometry (d in {2,4,8}, K in {256, 4096}, g in {64,128}), several tiles
+and a ragged tail in rows, tokens and columns; bit-exact dequant; outputs
+within 1e-3 (row-normalised); bit-identical outputs on exact-arithmetic
+inputs; routed experts with skipped and duplicate ids."""
+import numpy as np
+import pytest
+
+from oracle import vq_oracle as O
+from vq_dequant_matmul_gemv_amd import synth
+from tests.helpers import TOL, announce, row_rel_err, to_dev, upload
+
+pytestmark = pytest.mark.gpu
+
+GEOMS = [(d, b, g) for d in (2, 4, 8) for b in (8, 12) for g in (64, 128)]
+
+
+def _case(d, b, g, rows, cols, key, exact=False, experts=1, cbpe=False):
+    spec = synth.Spec(rows=rows, cols=cols, d=d, log2_k=b, group=g, experts=experts)
+    arrs = synth.tensor(spec, *key, exact=exact, codebook_per_expert=cbpe)
+    return spec, arrs, upload(arrs, spec, codebook_per_expert=cbpe)
+
+
+def _cols_for(d, g, blocks):
+    cols = 32 * d * blocks
+    while cols % g:
+        cols += 32 * d
+    return cols
+
+
+@pytest.mark.parametrize("d,b,g", GEOMS)
+def test_dequant_bit_exact(d, b, g):
+    from vq_dequant_matmul_gemv_amd import binding
+    rows, cols = 37, _cols_for(d, g, 5)
+    announce("dequant", d, b, g, rows, cols)
+    spec, arrs, w = _case(d, b, g, rows, cols, ("dq", d, b, g))
+    got = binding.dequant(w).cpu().numpy().view(np.uint16)
+    want = O.dequant(arrs["codes"][0], arrs["codebook"], arrs["scales"][0], cols, d, b, g).view(np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_dequant_subnormal_and_extreme_entries():
+    from vq_dequant_matmul_gemv_amd import binding
+    d, b, g, rows, cols = 2, 8, 64, 8, 256
+    spec = synth.Spec(rows=rows, cols=cols, d=d, log2_k=b, group=g)
+    arrs = synth.tensor(spec, "dq-sub")
+    cb = arrs["codebook"].view(np.uint16).copy()
+    cb[:64] = np.arange(1, 129, dtype=np.uint16).reshape(64, 2)          # subnormals
+    cb[64:80] = 0x7BFF                                                   # max finite
+    cb[80:96] = 0x8000                                                   # -0
+    arrs["codebook"] = cb.view(np.float16)
+    sc = arrs["scales"].view(np.uint16).copy()
+    sc[0, 0, :2] = [0x0001, 0x3C00]
+    sc[0, 1, :2] = [0x7BFF, 0x0400]
+    arrs["scales"] = sc.view(np.float16)
+    announce("dequant-subnormal")
+    w = upload(arrs, spec)
+    got = binding.dequant(w).cpu().numpy().view(np.uint16)
+    want = O.dequant(arrs["codes"][0], arrs["codebook"], arrs["scales"][0], cols, d, b, g).view(np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_dequant_expert_and_per_expert_codebook():
+    from vq_dequant_matmul_gemv_amd import binding
+    spec, arrs, w = _case(4, 12, 128, 20, 256, ("dq-e",), experts=3, cbpe=True)
+    for e in range(3):
+        announce("dequant-expert", e)
+        got = binding.dequant(w, expert=e).cpu().numpy().view(np.uint16)
+        want = O.dequant(arrs["codes"][e], arrs["codebook"][e], arrs["scales"][e], 256, 4, 12, 128)
+        assert np.array_equal(got, want.view(np.uint16))
+
+
+@pytest.mark.parametrize("fn", ["gemv", "gemm"])
+@pytest.mark.parametrize("d,b,g", GEOMS)
+def test_dense_all_geometries(fn, d, b, g):
+    from vq_dequant_matmul_gemv_amd import binding
+    rows, cols = 301, _cols_for(d, g, 7)
+    spec, arrs, w = _case(d, b, g, rows, cols, ("dense", d, b, g))
+    for T in (1, 3, 18):
+        x = synth.activations((T, cols), "dense", d, b, g, T)
+        announce(fn, d, b, g, rows, cols, T)
+        y = getattr(binding, fn)(w, to_dev(x)).cpu().numpy()
+        ref = O.gemv_ref(arrs["codes"][0], arrs["codebook"], arrs["scales"][0], x, cols, d, b, g)
+        err = row_rel_err(y, ref)
+        assert err <= TOL, (fn, T, err)
+
+
+@pytest.mark.parametrize("fn", ["gemv", "gemm"])
+@pytest.mark.parametrize("d,b,g", [(2, 8, 64), (4, 8, 64), (4, 12, 128), (8, 12, 128), (8, 8, 64)])
+def test_dense_exact_inputs_bit_identical(fn, d, b, g):
+    from vq_dequant_matmul_gemv_amd import binding
+    rows, cols = 260, _cols_for(d, g, 6)
+    spec, arrs, w = _case(d, b, g, rows, cols, ("exact", d, b, g), exact=True)
+    for T in (1, 2, 5, 33):
+        x = synth.activations((T, cols), "exact", d, b, g, T, exact=True)
+        announce(fn, "exact", d, b, g, T)
+        y = getattr(binding, fn)(w, to_dev(x)).cpu().numpy()
+        ref = O.gemv_ref(arrs["codes"][0], arrs["codebook"], arrs["scales"][0], x, cols, d, b, g)
+        assert np.array_equal(y.astype(np.float64), ref), (fn, T)
+
+
+@pytest.mark.parametrize("fn", ["gemv", "gemm"])
+def test_dense_shapes_and_tokens(fn):
+    """Ragged tokens around the tile sizes, tiny and tall shapes, a column
+    count with a half super-step (d=2, cols % 128 == 64) and a row count that
+    is not a multiple of 4."""
+    from vq_dequant_matmul_gemv_amd import binding
+    cases = [(1, 64, 2, 8, 64, [1, 2]), (3, 192, 2, 8, 64, [1, 7, 16, 17]),
+             (513, 320, 2, 8, 64, [1, 4, 129]), (257, 128, 4, 8, 64, [5, 64, 65]),
+             (64, 512, 8, 12, 128, [1, 63, 64, 65]), (1030, 256, 4, 8, 128, [1, 130])]
+    for rows, cols, d, b, g, Ts in cases:
+        spec, arrs, w = _case(d, b, g, rows, cols, ("shapes", rows, cols))
+        for T in Ts:
+            x = synth.activations((T, cols), "shapes", rows, cols, T)
+            announce(fn, "shape", rows, cols, d, b, g, T)
+            y = getattr(binding, fn)(w, to_dev(x)).cpu().numpy()
+            ref = O.gemv_ref(arrs["codes"][0], arrs["codebook"], arrs["scales"][0], x, cols, d, b, g)
+            assert row_rel_err(y, ref) <= TOL, (rows, cols, T)
+
+
+def test_gemv_wide_rows_split_into_column_slices():
+    """More than 1024 16-code chunks per row: the GEMV runs column slices
+    and accumulates them."""
+    from vq_dequant_matmul_gemv_amd import binding
+    d, b, g = 2, 8, 64
+    rows, cols = 40, 2 * 16 * 1030      # 1030 chunks per row
+    spec, arrs, w = _case(d, b, g, rows, cols, ("wide",))
+    for T in (1, 2):
+        x = synth.activations((T, cols), "wide", T)
+        announce("gemv-wide", T)
+        y = binding.gemv(w, to_dev(x)).cpu().numpy()
+        ref = O.gemv_ref(arrs["codes"][0], arrs["codebook"], arrs["scales"][0], x, cols, d, b, g)
+        assert row_rel_err(y, ref) <= TOL
+
+
+def test_zero_tokens_is_a_no_op():
+    import torch
+    from vq_dequant_matmul_gemv_amd import binding
+    spec, arrs, w = _case(2, 8, 64, 8, 64, ("empty",))
+    y = torch.full((0, 8), 7.0, device="cuda")
+    binding.gemv(w, torch.zeros((0, 64), dtype=torch.float16, device="cuda"), y)
+    binding.gemm(w, torch.zeros((0, 64), dtype=torch.float16, device="cuda"), y)
+
+
+# ---------------------------------------------------------------------------
+# routed experts
+# ---------------------------------------------------------------------------
+
+def _moe_ids(T, top_k, E, key):
+    ids = synth.zipf_routing(T, E, top_k, *key) if E >= top_k else \
+        synth.rng("ids", *key).integers(0, E, size=(T, top_k)).astype(np.int32)
+    return ids
+
+
+@pytest.mark.parametrize("fn", ["moe_gemv", "moe_gemm"])
+@pytest.mark.parametrize("x_per_slot", [False, True])
+@pytest.mark.parametrize("d,b,g", [(4, 8, 64), (8, 12, 128), (4, 12, 128), (2, 8, 64)])
+def test_moe_matches_oracle(fn, x_per_slot, d, b, g):
+    from vq_dequant_matmul_gemv_amd import binding
+    E, rows, cols, top_k = 16, 96, _cols_for(d, g, 4), 4
+    spec, arrs, w = _case(d, b, g, rows, cols, ("moe", d, b, g), experts=E)
+    for T in (1, 3, 70):
+        ids = _moe_ids(T, top_k, E, ("moe", T))
+        ids[0, 1] = -1                     # skipped slot
+        if T > 1:
+            ids[1, 2] = E + 5              # out of range: skipped
+            ids[2, 0] = ids[2, 3]          # duplicate within a token
+        shape = (T, top_k, cols) if x_per_slot else (T, cols)
+        x = synth.activations(shape, "moe", d, b, g, T)
+        announce(fn, d, b, g, "xps", x_per_slot, "T", T)
+        y = getattr(binding, fn)(w, to_dev(x), to_dev(ids), x_per_slot=x_per_slot).cpu().numpy()
+        ref = O.moe_ref(arrs["codes"], arrs["codebook"], arrs["scales"], x, ids, cols=cols, d=d,
+                        log2_k=b, group=g, x_per_slot=x_per_slot)
+        assert np.all(y[0, 1] == 0)
+        assert row_rel_err(y.reshape(-1, rows), ref.reshape(-1, rows)) <= TOL
+
+
+def test_moe_per_expert_codebooks():
+    from vq_dequant_matmul_gemv_amd import binding
+    E, rows, cols, top_k, T = 5, 64, 256, 2, 9
+    spec, arrs, w = _case(4, 8, 64, rows, cols, ("moe-cbpe",), experts=E, cbpe=True)
+    ids = synth.rng("ids-cbpe").integers(0, E, size=(T, top_k)).astype(np.int32)
+    x = synth.activations((T, cols), "moe-cbpe")
+    ref = O.moe_ref(arrs["codes"], arrs["codebook"], arrs["scales"], x, ids, cols=cols, d=4,
+                    log2_k=8, group=64, x_per_slot=False, codebook_per_expert=True)
+    for fn in ("moe_gemv", "moe_gemm"):
+        announce(fn, "cbpe")
+        y = getattr(binding, fn)(w, to_dev(x), to_dev(ids)).cpu().numpy()
+        assert row_rel_err(y.reshape(-1, rows), ref.reshape(-1, rows)) <= TOL
+
+
+def test_moe_grouped_equals_per_slot_bit_identical_on_exact_inputs():
+    """Grouping by expert does not change any row: on exact-arithmetic
+    inputs grouped GEMM, per-slot GEMV and the oracle agree bit for bit."""
+    from vq_dequant_matmul_gemv_amd import binding
+    E, rows, cols, top_k, T = 32, 128, 512, 8, 100
+    spec, arrs, w = _case(4, 8, 64, rows, cols, ("moe-exact",), exact=True, experts=E)
+    ids = synth.zipf_routing(T, E, top_k, "moe-exact")
+    x = synth.activations((T, cols), "moe-exact", exact=True)
+    announce("moe-exact")
+    a = binding.moe_gemm(w, to_dev(x), to_dev(ids)).cpu().numpy()
+    bgv = binding.moe_gemv(w, to_dev(x), to_dev(ids)).cpu().numpy()
+    ref = O.moe_ref(arrs["codes"], arrs["codebook"], arrs["scales"], x, ids, cols=cols, d=4,
+                    log2_k=8, group=64, x_per_slot=False)
+    assert np.array_equal(a, bgv)
+    assert np.array_equal(a.astype(np.float64), ref)
+
+
+def test_moe_all_slots_skipped_and_repeat_runs_identical():
+    import torch
+    from vq_dequant_matmul_gemv_amd import binding
+    E, rows, cols, top_k, T = 8, 64, 256, 2, 33
+    spec, arrs, w = _case(2, 8, 64, rows, cols, ("moe-skip",), experts=E)
+    x = to_dev(synth.activations((T, cols), "moe-skip"))
+    ids = torch.full((T, top_k), -1, dtype=torch.int32, device="cuda")
+    for fn in ("moe_gemv", "moe_gemm"):
+        announce(fn, "all-skipped")
+        y = torch.full((T, top_k, rows), 3.0, device="cuda")
+        getattr(binding, fn)(w, x, ids, y=y)
+        assert torch.count_nonzero(y).item() == 0
+    ids = to_dev(synth.zipf_routing(T, E, top_k, "moe-rep"))
+    outs = [binding.moe_gemm(w, x, ids).cpu().numpy() for _ in range(3)]
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])

@@ -1,0 +1,270 @@
+// vq_device.h -- device-side building blocks shared by every VQ kernel:
+// code extraction from packed words, codebook staging into LDS, and the
+// codebook gather.  gfx950 (CDNA4), wave64.
+//
+// Format (paper "Data-Free Vector Quantization Beats Affine Quantization at
+// Matched Bytes Below 5 Bits", §1 Notation and §2.3 Packing; model card
+// "Qwen3.5-397B-A17B-VQ-2.4bpw", Methodology): code j of a row is the B bits
+// starting at bit j*B of the row's little-endian code stream; rows hold whole
+// 32-code blocks of B uint32 words.  Kernels work on "chunks" of 16
+// consecutive codes of one row: 16*B bits = B/2 words (16 bytes for B = 8,
+// 24 bytes for B = 12), always starting on an 8-byte boundary.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vqmi {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kCodesPerChunk = 16;
+
+// ---------------------------------------------------------------------------
+// buffer loads: one wave-uniform resource (base, size in bytes) in SGPRs and
+// a 32-bit byte offset per lane.  Bytes at or past the size read as zero, so
+// rows past the end of a tensor need no clamping.  Every buffer a kernel
+// streams is below 2 GiB (the API checks).
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOutOfRange = 0x80000000u;  // an offset past every buffer
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes > 0x7fffffffull ? 0x7fffffffu : (uint32_t)bytes;
+  // dword 3 of a gfx9 buffer descriptor: 32-bit data format, raw addressing
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load_b128(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x2 buf_load_b64(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load_b32(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint16_t buf_load_b16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// codes
+// ---------------------------------------------------------------------------
+
+// Words of one 16-code chunk.
+template <int B>
+struct Chunk {
+  static constexpr int kWords = B / 2;  // 8-bit: 4 words, 12-bit: 6 words
+  uint32_t w[kWords];
+};
+
+template <int B>
+__device__ __forceinline__ void load_chunk(Chunk<B>& c, rsrc_t r, uint32_t off) {
+  if constexpr (B == 8) {
+    u32x4 v = buf_load_b128(r, off);  // 16-byte aligned
+    c.w[0] = v.x; c.w[1] = v.y; c.w[2] = v.z; c.w[3] = v.w;
+  } else {
+    u32x2 a = buf_load_b64(r, off);   // 24 bytes on an 8-byte boundary
+    u32x2 b = buf_load_b64(r, off + 8);
+    u32x2 d = buf_load_b64(r, off + 16);
+    c.w[0] = a.x; c.w[1] = a.y; c.w[2] = b.x; c.w[3] = b.y; c.w[4] = d.x; c.w[5] = d.y;
+  }
+}
+
+template <int B>
+__device__ __forceinline__ void load_chunk(Chunk<B>& c, const uint32_t* p) {
+  if constexpr (B == 8) {
+    u32x4 v = *reinterpret_cast<const u32x4*>(p);  // 16-byte aligned
+    c.w[0] = v.x; c.w[1] = v.y; c.w[2] = v.z; c.w[3] = v.w;
+  } else {
+    // 24 bytes on an 8-byte boundary
+    u32x2 a = *reinterpret_cast<const u32x2*>(p);
+    u32x2 b = *reinterpret_cast<const u32x2*>(p + 2);
+    u32x2 d = *reinterpret_cast<const u32x2*>(p + 4);
+    c.w[0] = a.x; c.w[1] = a.y; c.w[2] = b.x; c.w[3] = b.y; c.w[4] = d.x; c.w[5] = d.y;
+  }
+}
+
+// Code i (0..15, compile-time after unrolling) of a chunk.
+template <int B>
+__device__ __forceinline__ uint32_t chunk_code(const Chunk<B>& c, int i) {
+  constexpr uint32_t mask = (1u << B) - 1u;
+  const int bit = i * B;
+  const int wi = bit >> 5;
+  const int sh = bit & 31;
+  if (sh + B <= 32) return (c.w[wi] >> sh) & mask;
+  return __builtin_amdgcn_alignbit(c.w[wi + 1], c.w[wi], sh) & mask;  // straddles two words
+}
+
+// ---------------------------------------------------------------------------
+// codebook in LDS
+// ---------------------------------------------------------------------------
+//
+// Two layouts.
+//
+// Replicated (K = 256 only): each 256-byte LDS row holds 128/D copies of one
+// entry side by side, so the byte offset of copy c of entry e is
+//   e * 256 + c * (2*D).
+// A lane always reads copy (lane % copies): the LDS bank it touches depends
+// only on its lane id, never on the code, so a wave's random gather is free of
+// bank conflicts (64 lanes x 4 B, 32 lanes x 8 B or 16 lanes x 16 B hit
+// pairwise different banks within each LDS cycle).  The offset is one
+// v_perm_b32: byte 1 = the 8-bit code, byte 0 = the lane's copy offset.
+// 64 KiB for every D.
+//
+// Plain (any K): entry e at e * (2*D) bytes; random gathers may conflict.
+// Used for K = 4096 (32 KiB for d4, 64 KiB for d8, 16 KiB for d2).
+
+template <int D, int B>
+struct CodebookLayout {
+  static constexpr int kEntryBytes = 2 * D;
+  static constexpr bool kReplicated = (B == 8);
+  static constexpr int kCopies = kReplicated ? 256 / kEntryBytes : 1;
+  static constexpr int kBytes = kReplicated ? 256 * 256 : (1 << B) * kEntryBytes;
+};
+
+// Stage `cb` (global, [K][D] fp16, 16-byte aligned) into `lds`.
+// All threads of the block take part; the caller synchronises afterwards.
+// Every thread issues all of its global loads before its first LDS write, so
+// the staging costs one round trip to L2 rather than one per slot.
+template <int D, int B>
+__device__ __forceinline__ void stage_codebook(uint8_t* lds, const uint16_t* cb, int tid,
+                                               int nthreads) {
+  using L = CodebookLayout<D, B>;
+  if constexpr (L::kReplicated) {
+    // 4096 slots of 16 bytes; slot q holds copies of entry q / 16.  Lanes
+    // write consecutive slots (conflict-free); the 16 lanes sharing an entry
+    // read the same global address (one L1 line).
+    constexpr int V = 8;
+    for (int base = tid; base < 4096; base += V * nthreads) {
+      u32x4 v[V];
+#pragma unroll
+      for (int u = 0; u < V; ++u) {
+        const int q = base + u * nthreads;
+        const int e = (q < 4096 ? q : 0) >> 4;
+        if constexpr (D == 2) {
+          const uint32_t a = reinterpret_cast<const uint32_t*>(cb)[e];
+          v[u] = u32x4{a, a, a, a};
+        } else if constexpr (D == 4) {
+          const u32x2 a = reinterpret_cast<const u32x2*>(cb)[e];
+          v[u] = u32x4{a.x, a.y, a.x, a.y};
+        } else {
+          v[u] = reinterpret_cast<const u32x4*>(cb)[e];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < V; ++u) {
+        const int q = base + u * nthreads;
+        if (q < 4096) reinterpret_cast<u32x4*>(lds)[q] = v[u];
+      }
+    }
+  } else {
+    constexpr int n16 = L::kBytes / 16;
+    constexpr int V = 8;
+    for (int base = tid; base < n16; base += V * nthreads) {
+      u32x4 v[V];
+#pragma unroll
+      for (int u = 0; u < V; ++u) {
+        const int q = base + u * nthreads;
+        v[u] = reinterpret_cast<const u32x4*>(cb)[q < n16 ? q : 0];
+      }
+#pragma unroll
+      for (int u = 0; u < V; ++u) {
+        const int q = base + u * nthreads;
+        if (q < n16) reinterpret_cast<u32x4*>(lds)[q] = v[u];
+      }
+    }
+  }
+}
+
+// Per-lane constant part of the gather offset (replicated layout).
+template <int D, int B>
+__device__ __forceinline__ uint32_t lane_copy_offset(int lane) {
+  using L = CodebookLayout<D, B>;
+  if constexpr (L::kReplicated) return (uint32_t)((lane % L::kCopies) * L::kEntryBytes);
+  return 0u;
+}
+
+// Byte offset in LDS of entry `code` for this lane.  For the replicated
+// layout `word` is the packed word holding the 8-bit code as byte `byte`.
+template <int D, int B>
+__device__ __forceinline__ uint32_t entry_offset_byte(uint32_t word, int byte, uint32_t lane_off) {
+  // v_perm_b32: result byte0 = lane_off byte0, byte1 = word byte `byte`, bytes 2-3 = 0
+  const uint32_t sel = 0x0C0C0000u | ((uint32_t)(4 + byte) << 8);
+  return __builtin_amdgcn_perm(word, lane_off, sel);
+}
+
+template <int D>
+struct Entry;
+template <> struct Entry<2> { half2_t v[1]; };
+template <> struct Entry<4> { half2_t v[2]; };
+template <> struct Entry<8> { half2_t v[4]; };
+
+template <int D>
+__device__ __forceinline__ Entry<D> lds_entry(const uint8_t* lds, uint32_t off) {
+  Entry<D> e;
+  if constexpr (D == 2) {
+    e.v[0] = *reinterpret_cast<const half2_t*>(lds + off);
+  } else if constexpr (D == 4) {
+    half4_t h = *reinterpret_cast<const half4_t*>(lds + off);
+    e.v[0] = half2_t{h.x, h.y};
+    e.v[1] = half2_t{h.z, h.w};
+  } else {
+    half8_t h = *reinterpret_cast<const half8_t*>(lds + off);
+    e.v[0] = half2_t{h[0], h[1]};
+    e.v[1] = half2_t{h[2], h[3]};
+    e.v[2] = half2_t{h[4], h[5]};
+    e.v[3] = half2_t{h[6], h[7]};
+  }
+  return e;
+}
+
+// Entry of code i of a chunk for this lane.
+template <int D, int B>
+__device__ __forceinline__ Entry<D> gather(const uint8_t* lds, const Chunk<B>& c, int i,
+                                           uint32_t lane_off) {
+  using L = CodebookLayout<D, B>;
+  uint32_t off;
+  if constexpr (L::kReplicated) {
+    off = entry_offset_byte<D, B>(c.w[i >> 2], i & 3, lane_off);
+  } else {
+    off = chunk_code<B>(c, i) * (uint32_t)L::kEntryBytes;
+  }
+  return lds_entry<D>(lds, off);
+}
+
+__device__ __forceinline__ half2_t as_half2(uint32_t u) {
+  return __builtin_bit_cast(half2_t, u);
+}
+__device__ __forceinline__ uint32_t as_u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
+
+__device__ __forceinline__ float dot2(half2_t a, half2_t b, float c) {
+  return __builtin_amdgcn_fdot2(a, b, c, false);  // v_dot2_f32_f16
+}
+
+// Sum over each 16-lane DPP row; every lane of the row gets the total.
+// quad_perm [1,0,3,2] and [2,3,0,1] sum each quad, row_half_mirror pairs the
+// two quads of each half-row, row_mirror pairs the two half-rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141>(v);  // row_half_mirror
+  v += dpp_mov<0x140>(v);  // row_mirror
+  return v;
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+}  // namespace vqmi
