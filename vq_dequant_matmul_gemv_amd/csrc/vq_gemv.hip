@@ -9,24 +9,22 @@
 // with fp32 accumulation.  Each product of two fp16 values is exact in fp32.
 //
 // Design for gfx950 (batch-1 decode is bound by the bytes of codes + scales):
-//  * Each wave owns whole output rows and streams them on its own: no block
-//    barrier after set-up and no cross-wave reduction.  A row's code stream
-//    is walked in passes of 64 sixteen-code chunks, one chunk (16 or 24
-//    bytes) per lane per pass, so every load instruction of a wave covers a
-//    contiguous 1 KiB (or 1.5 KiB) run of the row.
-//  * A ring of PD chunks per lane is kept in flight: the load for unit u + PD
-//    (unit = one pass over one row) is issued as soon as unit u is consumed,
-//    so a CU holds ~100-150 KiB of outstanding reads with one or two waves per
-//    SIMD.  Loads are buffer loads (one SGPR descriptor, 32-bit lane offsets).
-//  * x is staged once per block into LDS, zero-padded to whole passes and
-//    swizzled so that the 16-byte x reads of eight consecutive chunks hit
-//    eight different bank groups.
+//  * A row's code stream is cut into passes of 64 sixteen-code chunks (one
+//    chunk, 16 or 24 bytes, per lane).  Each wave of a block owns one pass
+//    position and a contiguous range of the block's rows: its lanes keep the
+//    x columns of that pass in VGPRs for the whole kernel ("x-stationary"),
+//    and every load instruction covers a contiguous 1 KiB (1.5 KiB) run of a
+//    row.  Waves never wait on each other until the block's final combine.
+//  * Each lane keeps a ring of PD rows' chunks in flight: the load for row
+//    u + PD is issued as soon as row u is consumed.  Loads are buffer loads
+//    with the row offset in an SGPR, so a load costs no address VALU.
 //  * The codebook sits in LDS; for K = 256 it is replicated so that a lane's
 //    gather bank depends only on its lane id (conflict-free).
 //  * Inner loop per code: one v_perm_b32 (LDS offset), one LDS read, d/2
 //    v_dot2_f32_f16 per token; the group scale multiplies the group's sum
-//    once (an fma per group).  The row total is a DPP reduction across the
-//    wave; lane 63 stores it.
+//    once (an fma per group).  A row piece is summed across the wave by DPP;
+//    with one pass per row it is stored directly, otherwise the pieces go to
+//    a small LDS table and are added in pass order after one barrier.
 //  * Routed experts (top-k MoE): blockIdx.y is the (token, slot) pair; the
 //    block reads its expert id and points at that expert's codes and scales.
 //    An id outside [0, E) writes a zero row.
@@ -52,6 +50,7 @@ struct GemvArgs {
   int P;                  // 16-code chunks per row in this column slice
   int p0;                 // first chunk of the slice
   int passes;             // ceil(P / 64)
+  int waves_per_pass;     // waves of a block sharing one pass position
   int accumulate;         // add into y (column slices after the first)
   int T;                  // dense: tokens; routed: pairs
   int top_k;
@@ -59,12 +58,18 @@ struct GemvArgs {
   int x_per_slot;
 };
 
-// Prefetch depth (units in flight per lane) and largest token tile.
-template <int D, int B>
-struct GemvCfg {
-  static constexpr int kPD = B == 8 ? 12 : 8;
-};
 constexpr int gemv_max_tt(int D) { return D == 8 ? 1 : 2; }
+// Waves per block: 16 where x (8*d VGPRs per token) and the ring fit in 128
+// VGPRs, else 8.
+constexpr int gemv_max_waves(int D, int TT) { return (D == 2 || (D == 4 && TT == 1)) ? 16 : 8; }
+// Rows in flight per lane.  Measured on MI355X (17408x5120, d=2): a ring of
+// 3-4 rows with 15-16 waves per CU beats deeper rings (6: +8 %, 12: +30 %);
+// more outstanding requests per CU only queue up.
+template <int D, int B, int TT>
+struct GemvCfg {
+  static constexpr int kPD = gemv_max_waves(D, TT) == 16 ? 4 : 6;
+};
+constexpr int kGemvRowPieces = 4096;  // LDS table entries for split rows (floats)
 
 // Total of v over the 64 lanes of the wave, valid in lane 63.
 __device__ __forceinline__ float wave_sum_to_lane63(float v) {
@@ -74,108 +79,37 @@ __device__ __forceinline__ float wave_sum_to_lane63(float v) {
   return v;
 }
 
-// x for up to TT tokens -> LDS.  Chunk p's S = 2d segments of 16 bytes sit
-// at segment (p*(S+1) + q): one segment of padding per chunk, so the reads of
-// segment q by eight consecutive chunks fall in eight different bank groups
-// while q stays a compile-time offset.  Zero past the row end.  The codebook:
-// the plain layout is copied directly; the replicated layout's 256 entries
-// are copied raw to the area after x and expanded after a barrier.  Every
-// load of a round is issued before the first is waited on.
-template <int D, int B, int TT>
-__device__ __forceinline__ void stage_x_and_codebook_impl(u32x4* xl, uint8_t* cb_lds,
-                                                          const uint16_t* xb, const uint16_t* cb,
-                                                          int cols, int ntok, int P, int xchunks,
-                                                          int tid, int nt) {
-  using L = CodebookLayout<D, B>;
-  constexpr int S = 2 * D;
-  constexpr int XR = 12;  // x segments in flight per thread per round
-  const int xsegs = xchunks * (S + 1);       // per token, padded
-  u32x4* raw = xl + TT * xsegs;
-  u32x4 e = u32x4{0u, 0u, 0u, 0u};
-  if constexpr (L::kReplicated) {
-    if (tid < 256) {
-      if constexpr (D == 2) e.x = reinterpret_cast<const uint32_t*>(cb)[tid];
-      else if constexpr (D == 4) { const u32x2 t = reinterpret_cast<const u32x2*>(cb)[tid]; e.x = t.x; e.y = t.y; }
-      else e = reinterpret_cast<const u32x4*>(cb)[tid];
-    }
-  }
-  const int nseg = xchunks * S;               // segments per token (S is a power of two)
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(xb + (int64_t)tt * cols);
-    const bool tok_ok = tt < ntok;
-    for (int base = tid; base < nseg; base += XR * nt) {
-      u32x4 v[XR];
-#pragma unroll
-      for (int u = 0; u < XR; ++u) {
-        const int ls = base + u * nt;
-        v[u] = u32x4{0u, 0u, 0u, 0u};
-        if (ls < nseg && (ls / S) < P && tok_ok) v[u] = src[ls];
-      }
-#pragma unroll
-      for (int u = 0; u < XR; ++u) {
-        const int ls = base + u * nt;
-        if (ls < nseg) xl[tt * xsegs + (ls / S) * (S + 1) + (ls % S)] = v[u];
-      }
-    }
-  }
-  if constexpr (L::kReplicated) {
-    if (tid < 256) raw[tid] = e;
-  } else {
-    stage_codebook<D, B>(cb_lds, cb, tid, nt);
-  }
-}
-
-// Replicated layout: slot q (16 bytes) holds copies of entry q / 16, read
-// from the raw copy in LDS (16 lanes share one address: a broadcast).
-template <int D, int B>
-__device__ __forceinline__ void expand_codebook_impl(uint8_t* cb_lds, const u32x4* raw, int tid, int nt) {
-  using L = CodebookLayout<D, B>;
-  if constexpr (L::kReplicated) {
-    for (int q = tid; q < 4096; q += nt) {
-      const u32x4 e = raw[q >> 4];
-      u32x4 v;
-      if constexpr (D == 2) v = u32x4{e.x, e.x, e.x, e.x};
-      else if constexpr (D == 4) v = u32x4{e.x, e.y, e.x, e.y};
-      else v = e;
-      reinterpret_cast<u32x4*>(cb_lds)[q] = v;
-    }
-  }
-}
-
 template <int D, int B, int G, int TT, bool MOE>
-__global__ __launch_bounds__(1024) void vq_gemv_kernel(GemvArgs a) {
+__global__ __launch_bounds__(64 * gemv_max_waves(D, TT)) void vq_gemv_kernel(GemvArgs a) {
   using L = CodebookLayout<D, B>;
-  constexpr int PD = GemvCfg<D, B>::kPD;
+  constexpr int PD = GemvCfg<D, B, TT>::kPD;
   constexpr int NSC = (16 * D > G) ? (16 * D / G) : 1;  // scales per chunk
   constexpr int CPS = 16 / NSC;                          // codes per scale in a chunk
-  constexpr int S = 2 * D;                               // 16-byte x segments per chunk
+  constexpr int HX = 8 * D;                              // half2 of x per chunk per token
   constexpr int CB = Chunk<B>::kWords * 4;               // code bytes per chunk
-  constexpr int MAXW = 16;                               // waves per block (max)
   static_assert(TT <= gemv_max_tt(D), "token tile too large for this d");
 
   __shared__ __align__(16) uint8_t cb_lds[L::kBytes];
-  __shared__ float split_val[MAXW][2][TT];
-  __shared__ int split_row[MAXW][2];
-  extern __shared__ __align__(16) u32x4 xl[];           // [TT][chunks*(S+1)] segments + raw cb
+  __shared__ __align__(16) u32x4 raw[256];               // replicated layout: entries before expansion
+  __shared__ float pieces[kGemvRowPieces];               // [brows][passes][TT] when passes > 1
 
   const int tid = threadIdx.x;
   const int nt = blockDim.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
-  const int nw = nt >> 6;
-  const int P = a.P;
   const int passes = a.passes;
-  const int xchunks = passes * 64;
-  const int xsegs = xchunks * (S + 1);                   // per token
+  const int k = a.waves_per_pass;
+  const int c = wave % passes;                           // this wave's pass
+  const int jw = wave / passes;                          // its slot among the pass's waves
+  const bool wave_on = jw < k;
 
-  // ---- this block's rows, this wave's units (unit = one pass over a row) ----
+  // ---- this block's rows, this wave's rows ----
   const int nblk = gridDim.x;
   const int brow0 = (int)((int64_t)a.rows * blockIdx.x / nblk);
   const int brows = (int)((int64_t)a.rows * (blockIdx.x + 1) / nblk) - brow0;
-  const int units = brows * passes;
-  const int ub = units * wave / nw;
-  const int ue = units * (wave + 1) / nw;
+  const int wr0 = wave_on ? brows * jw / k : 0;
+  const int wr1 = wave_on ? brows * (jw + 1) / k : 0;
+  const int nrows = wr1 - wr0;
 
   const uint32_t* codes = a.codes;
   const uint16_t* scales = a.scales;
@@ -188,7 +122,8 @@ __global__ __launch_bounds__(1024) void vq_gemv_kernel(GemvArgs a) {
     const int e = a.ids[pair];
     yb = a.y + (int64_t)pair * a.rows;
     if (e < 0 || e >= a.num_experts) {  // skipped slot: zero rows (block-uniform exit)
-      for (int r = tid; r < brows; r += nt) yb[brow0 + r] = 0.f;
+      if (a.p0 == 0)
+        for (int r = tid; r < brows; r += nt) yb[brow0 + r] = 0.f;
       return;
     }
     codes += (int64_t)e * a.code_estride;
@@ -204,150 +139,152 @@ __global__ __launch_bounds__(1024) void vq_gemv_kernel(GemvArgs a) {
     ntok = min(TT, a.T - tok0);
   }
 
-  // ---- stage x and the codebook into LDS ----
-  // These loads come ahead of the first ring loads so that their wait does
-  // not include the HBM latency of the codes.
-  stage_x_and_codebook_impl<D, B, TT>(xl, cb_lds, xb + (int64_t)a.p0 * 16 * D, cb, a.cols, ntok, P,
-                                      xchunks, tid, nt);
+  const int p = c * 64 + lane;            // chunk within the slice
+  const int gp = a.p0 + p;                // chunk within the full row
+  const bool in_row = p < a.P;            // lanes past the row end add nothing
 
-  // ---- the prefetch ring ----
+  // ---- x of this lane's chunk into VGPRs; codebook entries ----
+  const rsrc_t rx = make_rsrc(xb, (uint64_t)ntok * a.cols * 2);
+  u32x4 xr[TT][HX / 4];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int q = 0; q < HX / 4; ++q)
+      xr[tt][q] = buf_load_b128(rx, in_row ? (uint32_t)(tt * a.cols + gp * 16 * D) * 2u + 16u * q : kOutOfRange);
+  u32x4 ce = u32x4{0u, 0u, 0u, 0u};
+  if constexpr (L::kReplicated) {
+    if (tid < 256) {
+      if constexpr (D == 2) ce.x = reinterpret_cast<const uint32_t*>(cb)[tid];
+      else if constexpr (D == 4) { const u32x2 t = reinterpret_cast<const u32x2*>(cb)[tid]; ce.x = t.x; ce.y = t.y; }
+      else ce = reinterpret_cast<const u32x4*>(cb)[tid];
+    }
+  }
+
+  // ---- the prefetch ring: row offsets in SGPRs, lane offsets constant ----
   const rsrc_t rc = make_rsrc(codes, (uint64_t)a.rows * a.wr * 4);
   const rsrc_t rs = make_rsrc(scales, (uint64_t)a.rows * a.spr * 2);
   const uint32_t row_cb = (uint32_t)a.wr * 4u;
   const uint32_t row_sb = (uint32_t)a.spr * 2u;
-  const uint32_t lane_cb = (uint32_t)lane * CB;
+  const uint32_t c_lane = in_row ? (uint32_t)gp * CB : kOutOfRange;
+  const uint32_t s_lane = in_row ? (uint32_t)((gp * 16 * D) / G) * 2u : kOutOfRange;
 
   Chunk<B> ring[PD];
   uint16_t rsc[PD][NSC];
-  int l_row = ub / passes, l_pass = ub - (ub / passes) * passes;  // next unit to load
-  int l_left = ue - ub;
-  // Loads are unconditional: a unit past the wave's last one gets an
-  // out-of-range offset and reads zeros, so every unit slot issues the same
-  // loads and the in-order vmcnt waits stay exact.
-  auto load_unit = [&](Chunk<B>& c, uint16_t (&sc)[NSC]) {
-    const bool live = l_left > 0;
-    const uint32_t r = (uint32_t)(brow0 + l_row);
-    const uint32_t cbase = r * row_cb + (uint32_t)((a.p0 + l_pass * 64) * CB);
-    // chunks past the row end read in-bounds neighbours; masked out at use
-    load_chunk<B>(c, rc, live ? cbase + lane_cb : kOutOfRange);
-    const int gp = a.p0 + l_pass * 64 + lane;  // chunk within the full row
+  int l_row = 0;  // next row (of this wave's range) to load
+  // Loads are unconditional: a row past the wave's range gets an
+  // out-of-range lane offset and reads zeros, so every ring slot issues the
+  // same loads and the in-order vmcnt waits stay exact.
+  auto load_row = [&](Chunk<B>& ch, uint16_t (&sc)[NSC]) {
+    const bool live = l_row < nrows;
+    const uint32_t so = live ? (uint32_t)(brow0 + wr0 + l_row) * row_cb : 0u;
+    const uint32_t ss = live ? (uint32_t)(brow0 + wr0 + l_row) * row_sb : 0u;
+    const uint32_t vc = live ? c_lane : kOutOfRange;
+    const uint32_t vs = live ? s_lane : kOutOfRange;
+    if constexpr (B == 8) {
+      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, vc, so, 0));
+      ch.w[0] = v.x; ch.w[1] = v.y; ch.w[2] = v.z; ch.w[3] = v.w;
+    } else {
 #pragma unroll
-    for (int s = 0; s < NSC; ++s)
-      sc[s] = buf_load_b16(rs, live ? r * row_sb + (uint32_t)(((gp * 16 * D) / G + s) * 2) : kOutOfRange);
-    if (++l_pass == passes) { l_pass = 0; ++l_row; }
-    --l_left;
+      for (int h = 0; h < 3; ++h) {
+        const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rc, vc + 8u * h, so, 0));
+        ch.w[2 * h] = v.x; ch.w[2 * h + 1] = v.y;
+      }
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < NSC; ++s2) sc[s2] = __builtin_amdgcn_raw_buffer_load_b16(rs, vs + 2u * s2, ss, 0);
+    ++l_row;
   };
 #pragma unroll
-  for (int j = 0; j < PD; ++j) load_unit(ring[j], rsc[j]);
-  __syncthreads();
-  expand_codebook_impl<D, B>(cb_lds, xl + TT * xsegs, tid, nt);
-  if (lane == 0) {
-    split_row[wave][0] = -1;
-    split_row[wave][1] = -1;
+  for (int j = 0; j < PD; ++j) load_row(ring[j], rsc[j]);
+
+  if constexpr (L::kReplicated) {
+    if (tid < 256) raw[tid] = ce;
+  } else {
+    stage_codebook<D, B>(cb_lds, cb, tid, nt);
   }
   __syncthreads();
+  if constexpr (L::kReplicated) {
+    for (int q = tid; q < 4096; q += nt) {  // slot q holds copies of entry q / 16
+      const u32x4 e = raw[q >> 4];
+      u32x4 v;
+      if constexpr (D == 2) v = u32x4{e.x, e.x, e.x, e.x};
+      else if constexpr (D == 4) v = u32x4{e.x, e.y, e.x, e.y};
+      else v = e;
+      reinterpret_cast<u32x4*>(cb_lds)[q] = v;
+    }
+    __syncthreads();
+  }
+
+  half2_t xv[TT][HX];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int q = 0; q < HX / 4; ++q) {
+      xv[tt][4 * q + 0] = as_half2(xr[tt][q].x);
+      xv[tt][4 * q + 1] = as_half2(xr[tt][q].y);
+      xv[tt][4 * q + 2] = as_half2(xr[tt][q].z);
+      xv[tt][4 * q + 3] = as_half2(xr[tt][q].w);
+    }
 
   const uint32_t lane_off = lane_copy_offset<D, B>(lane);
-  float part[TT];
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt) part[tt] = 0.f;
-  int c_row = ub / passes, c_pass = ub - (ub / passes) * passes;  // next unit to compute
-  const bool first_partial = c_pass != 0;  // the first row began in an earlier wave
-  const int first_row = c_row;
-
-  auto compute_unit = [&](const Chunk<B>& c, const uint16_t (&sc)[NSC]) {
-    const int p = c_pass * 64 + lane;
-    const u32x4* xs = xl + p * (S + 1);
-    float g[TT], acc[TT];
+  // one pass and no accumulation: a row's wave sum is final; otherwise the
+  // pieces meet in LDS and are stored (or added) after the loop
+  const bool direct = passes == 1 && !a.accumulate;
+  int c_row = 0;  // next row to compute
+  auto compute_row = [&](const Chunk<B>& ch, const uint16_t (&sc)[NSC]) {
+    float acc[TT];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) acc[tt] = 0.f;
 #pragma unroll
-    for (int s = 0; s < NSC; ++s) {
+    for (int s2 = 0; s2 < NSC; ++s2) {
+      float g[TT];
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) g[tt] = 0.f;
 #pragma unroll
-      for (int i = s * CPS; i < (s + 1) * CPS; ++i) {
-        const Entry<D> e = gather<D, B>(cb_lds, c, i, lane_off);
-        const int q = (i * D) / 8;  // x segment holding code i's D columns
+      for (int i = s2 * CPS; i < (s2 + 1) * CPS; ++i) {
+        const Entry<D> e = gather<D, B>(cb_lds, ch, i, lane_off);
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-          const u32x4 xv = xs[tt * xsegs + q];
+        for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-          for (int j = 0; j < D / 2; ++j) {
-            const int w = ((i * D) / 2 + j) & 3;  // dword within the segment
-            g[tt] = dot2(e.v[j], as_half2(w == 0 ? xv.x : w == 1 ? xv.y : w == 2 ? xv.z : xv.w), g[tt]);
-          }
-        }
+          for (int j = 0; j < D / 2; ++j) g[tt] = dot2(e.v[j], xv[tt][i * (D / 2) + j], g[tt]);
       }
-      const float scale = half_bits_to_float(sc[s]);
+      const float scale = half_bits_to_float(sc[s2]);
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) acc[tt] = __builtin_fmaf(g[tt], scale, acc[tt]);
     }
-    const bool in_row = p < P;  // lanes past the row end (last pass) add nothing
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) part[tt] += in_row ? acc[tt] : 0.f;
-    if (++c_pass == passes) {  // row complete: reduce across the wave
-      const bool split = first_partial && c_row == first_row;
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        const float v = wave_sum_to_lane63(part[tt]);
-        if (lane == 63) {
-          if (split) {
-            split_val[wave][0][tt] = v;
-          } else if (tt < ntok) {
-            float* dst = yb + (int64_t)tt * a.rows + brow0 + c_row;
-            *dst = a.accumulate ? *dst + v : v;
-          }
-        }
-        part[tt] = 0.f;
-      }
-      if (split && lane == 63) split_row[wave][0] = c_row;
-      c_pass = 0;
-      ++c_row;
-    }
-  };
-
-  const int u_total = ue - ub;
-  for (int u0 = 0; u0 < u_total; u0 += PD) {
-#pragma unroll
-    for (int j = 0; j < PD; ++j) {
-      if (u0 + j < u_total) compute_unit(ring[j], rsc[j]);  // wave-uniform branch
-      load_unit(ring[j], rsc[j]);
-    }
-  }
-  // an unfinished last row continues in the next wave(s)
-  if (c_pass != 0) {
-    const int slot = (first_partial && c_row == first_row) ? 0 : 1;
+    const int r = wr0 + c_row;  // block-relative row
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
-      const float v = wave_sum_to_lane63(part[tt]);
-      if (lane == 63) split_val[wave][slot][tt] = v;
-    }
-    if (lane == 63) split_row[wave][slot] = c_row;
-  }
-  __syncthreads();
-  // rows cut by a wave boundary: add the pieces in wave order (deterministic)
-  for (int r = tid; r < brows; r += nt) {
-    float v[TT];
-    bool any = false;
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) v[tt] = 0.f;
-    for (int w = 0; w < nw; ++w) {
-#pragma unroll
-      for (int sl = 0; sl < 2; ++sl) {
-        if (split_row[w][sl] == r) {
-          any = true;
-#pragma unroll
-          for (int tt = 0; tt < TT; ++tt) v[tt] += split_val[w][sl][tt];
+      const float v = wave_sum_to_lane63(in_row ? acc[tt] : 0.f);
+      if (lane == 63) {
+        if (direct) {
+          if (tt < ntok) yb[(int64_t)tt * a.rows + brow0 + r] = v;
+        } else {
+          pieces[(r * passes + c) * TT + tt] = v;
         }
       }
     }
-    if (any) {
+    ++c_row;
+  };
+
+  for (int u0 = 0; u0 < nrows; u0 += PD) {
+#pragma unroll
+    for (int j = 0; j < PD; ++j) {
+      if (u0 + j < nrows) compute_row(ring[j], rsc[j]);  // wave-uniform branch
+      load_row(ring[j], rsc[j]);
+    }
+  }
+
+  if (!direct) {  // add each row's pass pieces in pass order (deterministic)
+    __syncthreads();
+    for (int r = tid; r < brows; r += nt) {
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
+        float v = 0.f;
+        for (int cc = 0; cc < passes; ++cc) v += pieces[(r * passes + cc) * TT + tt];
         if (tt < ntok) {
           float* dst = yb + (int64_t)tt * a.rows + brow0 + r;
-          *dst = a.accumulate ? *dst + v[tt] : v[tt];
+          *dst = a.accumulate ? *dst + v : v;
         }
       }
     }
@@ -420,59 +357,33 @@ int num_cus() {
   return n;
 }
 
-// Raise the kernel's dynamic-LDS limit (set once per kernel and device;
-// gfx950 has 160 KiB of LDS per CU).
-template <typename K>
-hipError_t allow_lds(K kernel) {
-  static thread_local int done_dev = -1;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (done_dev == dev) return hipSuccess;
-  hipFuncAttributes fa;
-  e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kernel));
-  if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)(160 * 1024 - fa.sharedSizeBytes));
-  if (e == hipSuccess) done_dev = dev;
-  return e;
-}
-
-constexpr int kGemvWaves = 16;  // waves per block
-
 template <int D, int B, int G, int TT, bool MOE>
 hipError_t gemv_launch(const GemvArgs& a, dim3 grid, hipStream_t s) {
-  using L = CodebookLayout<D, B>;
-  const size_t lds = ((size_t)TT * a.passes * 64 * (2 * D + 1) + 256) * 16;  // dynamic: x + raw codebook
-  auto k = vq_gemv_kernel<D, B, G, TT, MOE>;
-  hipError_t e = allow_lds(k);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, grid, dim3(64 * kGemvWaves), lds, s, a);
+  hipLaunchKernelGGL((vq_gemv_kernel<D, B, G, TT, MOE>), grid, dim3(64 * a.passes * a.waves_per_pass),
+                     0, s, a);
   return hipGetLastError();
 }
 
-// Column-slice size (in 16-code chunks) whose x, padded, fits in the LDS the
-// codebook leaves free.
-template <int D, int B, int TT>
-int gemv_max_slice_chunks() {
-  using L = CodebookLayout<D, B>;
-  const int budget = 160 * 1024 - L::kBytes - 256 * 16 - 2048;  // minus raw codebook, split slots
-  const int per_pass = 64 * (2 * D + 1) * 16 * TT;
-  return std::max(1, budget / per_pass) * 64;
-}
-
+// Rows are split over blocks so that one block per CU covers the grid; each
+// pass of a slice gets `waves_per_pass` waves; slices of at most
+// `max_waves` passes run one after another, accumulating into y.
 template <int D, int B, int G, int TT, bool MOE>
-hipError_t gemv_slices(GemvArgs a, int P_total, dim3 grid, hipStream_t s) {
-  const int maxc = gemv_max_slice_chunks<D, B, TT>();
-  const int n_slices = (P_total + maxc - 1) / maxc;
-  const int per = (P_total + n_slices - 1) / n_slices;
+hipError_t gemv_slices(GemvArgs a, int P_total, int ycount, hipStream_t s) {
+  constexpr int maxw = gemv_max_waves(D, TT);
+  const int passes_total = (P_total + 63) / 64;
+  const int n_slices = (passes_total + maxw - 1) / maxw;
+  const int passes_per = (passes_total + n_slices - 1) / n_slices;
+  const int blocks_fill = std::max(1, num_cus() / std::max(1, ycount));
   for (int sl = 0; sl < n_slices; ++sl) {
-    a.p0 = sl * per;
-    a.P = std::min(per, P_total - a.p0);
+    a.p0 = sl * passes_per * 64;
+    a.P = std::min(passes_per * 64, P_total - a.p0);
     a.passes = (a.P + 63) / 64;
+    a.waves_per_pass = maxw / a.passes;
     a.accumulate = sl > 0;
-    hipError_t e = gemv_launch<D, B, G, TT, MOE>(a, grid, s);
+    // enough blocks that each block's row-piece table fits in LDS
+    const int64_t min_blocks = ((int64_t)a.rows * a.passes * TT + kGemvRowPieces - 1) / kGemvRowPieces;
+    const int blocks = (int)std::min<int64_t>(a.rows, std::max<int64_t>(blocks_fill, min_blocks));
+    hipError_t e = gemv_launch<D, B, G, TT, MOE>(a, dim3(blocks, ycount), s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -499,22 +410,17 @@ hipError_t gemv_geom(const TensorView& w, const uint16_t* x, int T, float* y, co
   a.top_k = top_k;
   a.num_experts = w.num_experts;
   a.x_per_slot = x_per_slot;
-  // one block of kGemvWaves waves per CU across the whole grid (all token
-  // tiles / pairs); rows are split evenly over blocks and units evenly over
-  // the waves of a block
   const int tt = std::min(T >= 2 ? 2 : 1, gemv_max_tt(D));
-  const int ycount = ids ? T * top_k : (T + tt - 1) / tt;
-  const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>(w.rows, num_cus() / std::max(1, ycount)));
-  dim3 grid(blocks, ycount);
   if (ids) {
     a.T = T * top_k;
-    return gemv_slices<D, B, G, 1, true>(a, P_total, grid, s);
+    return gemv_slices<D, B, G, 1, true>(a, P_total, T * top_k, s);
   }
   a.T = T;
+  const int ycount = (T + tt - 1) / tt;
   if constexpr (gemv_max_tt(D) >= 2) {
-    if (tt == 2) return gemv_slices<D, B, G, 2, false>(a, P_total, grid, s);
+    if (tt == 2) return gemv_slices<D, B, G, 2, false>(a, P_total, ycount, s);
   }
-  return gemv_slices<D, B, G, 1, false>(a, P_total, grid, s);
+  return gemv_slices<D, B, G, 1, false>(a, P_total, ycount, s);
 }
 
 template <int D, int B, int G>
