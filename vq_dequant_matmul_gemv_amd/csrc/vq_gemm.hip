@@ -8,22 +8,26 @@
 // Quantization at Matched Bytes Below 5 Bits", §2.2 and §3.4: prefill runs a
 // prefill-shaped path over the same codes; model card
 // "Qwen3.5-397B-A17B-VQ-2.4bpw", Methodology, for the format), fp32
-// accumulation in v_mfma_f32_16x16x32_f16.
+// accumulation in v_mfma_f32_32x32x16_f16.
 //
 // Design for gfx950:
-//  * A = dequantized W (16 rows x 32 k per MFMA), B = x (32 k x 16 tokens).
-//    A wave owns 64 rows (4 m-blocks) and all WN tokens of the block tile;
-//    the block's 4 waves cover 256 rows, so every weight is dequantized
-//    exactly once per token tile, straight into the A-operand registers
-//    (no LDS round trip for W).
-//  * The contraction order over k is free, so each lane group (lanes 16g ..
-//    16g+15) takes a contiguous run of CG columns per "super-step" (CG = 32,
+//  * A = dequantized W (32 rows x 16 k per MFMA), B = x (16 k x 32 tokens).
+//    A block's waves sit side by side along W rows; a wave owns MB m-blocks
+//    of 32 rows and all 32*NB tokens of the tile, so every weight is
+//    dequantized exactly once per token tile, straight into the A-operand
+//    registers (no LDS round trip for W).  Large token counts use 8 waves
+//    (two per SIMD) of 64 rows x 128 tokens; small ones 4 waves of 128 rows
+//    x 32 tokens.
+//  * The contraction order over k is free, so each lane half (lanes 32h ..
+//    32h+31) takes a contiguous run of CG columns per "super-step" (CG = 32,
 //    or 64 for d = 8): a lane's codes for one super-step are one small
-//    contiguous load (16, 8 or 12 bytes) and its x slices are contiguous.
-//  * x tiles (WN tokens x 4*CG columns) go through LDS, double-buffered, one
-//    barrier per super-step; rows are padded by 16 bytes so the 16-byte
-//    fragment reads of 16 tokens hit distinct banks.
-//  * Codebook in LDS (replicated for K = 256, as in the GEMV).
+//    contiguous load and its x slices are contiguous.
+//  * x tiles (32*NB tokens x 2*CG columns) go through LDS, double-buffered,
+//    one barrier per super-step; token rows are padded by 16 bytes so the
+//    16-byte fragment reads hit distinct banks.
+//  * Codebook in LDS (replicated for K = 256, as in the GEMV); the gathers of
+//    the next k-step are issued ahead of the current k-step's MFMAs.
+//  * Under-filled grids (few tiles) split K and add the slices atomically.
 //  * Routed experts: the routing kernel counts pairs per expert, scans,
 //    scatters pair ids by expert and emits a flat list of (expert, first,
 //    count) token tiles; the GEMM walks that list with gathered x rows and
@@ -107,22 +111,45 @@ struct GemmArgs {
   int top_k, x_per_slot;
   int x_rows;             // routed: rows of x (T or T*top_k)
   int n_row_tiles, n_tok_tiles;
+  int ksplit;             // dense: K slices (grid.y); results added atomically when > 1
 };
 
-template <int D, int B, int G, int NBT, bool MOE>
-__global__ __launch_bounds__(256) void vq_gemm_kernel(GemmArgs a) {
+// 32x32x16 fp16 MFMA, fp32 accumulation.  Operand lanes: lane l supplies row
+// (A) / column (B) l % 32 and the 8 k-values of half h = l / 32; result lane
+// l holds column l % 32, rows 8*(i/4) + 4*h + (i%4), i = 0..15.
+__device__ __forceinline__ float16_t mfma32(half8_t a, half8_t b, float16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Block shape: WAVES waves side by side along W rows, each owning MB m-blocks
+// of 32 rows and all 32*NB tokens of the tile.
+template <int WAVES, int MB, int NB>
+struct GemmShape {
+  static constexpr int kWaves = WAVES;
+  static constexpr int kMB = MB;
+  static constexpr int kNB = NB;
+  static constexpr int kThreads = 64 * WAVES;
+  static constexpr int kRows = 32 * MB * WAVES;   // W rows per block tile
+  static constexpr int kTokens = 32 * NB;         // tokens per block tile
+};
+
+template <int D, int B, int G, class SH, bool MOE, bool ATOMIC>
+__global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
   using L = CodebookLayout<D, B>;
-  constexpr int CG = (D == 8) ? 64 : 32;  // columns per lane group per super-step
-  constexpr int S = CG / 8;               // MFMA k-steps (32 columns each) per super-step
+  constexpr int CG = (D == 8) ? 64 : 32;  // columns per lane half per super-step
+  constexpr int S = CG / 8;               // k-steps of 16 (8 per half) per super-step
   constexpr int NCL = CG / D;             // codes per lane per super-step
-  constexpr int SS = 4 * CG;              // columns per super-step
-  constexpr int MB = 4;                   // 16-row m-blocks per wave
-  constexpr int WN = 16 * NBT;            // tokens per block tile
+  constexpr int SS = 2 * CG;              // columns per super-step
+  constexpr int MB = SH::kMB;
+  constexpr int NB = SH::kNB;
+  constexpr int WN = SH::kTokens;
   constexpr int XROW = SS * 2 + 16;       // LDS bytes per token row (padded)
   constexpr int SEGS = SS / 8;            // 16-byte segments per token row
-  constexpr int XLD = WN * SEGS / 256;    // x segments loaded per thread per super-step
-  static_assert(XLD >= 1 && (WN * SEGS) % 256 == 0, "x tile must split evenly");
-  constexpr int CPA = 8 / D;              // codes per A fragment (8 columns)
+  constexpr int NT = SH::kThreads;
+  constexpr int XLD = (WN * SEGS + NT - 1) / NT;  // x segments per thread per super-step
+  constexpr int CPA = 8 / D;              // codebook entries per A fragment (8 columns)
+  constexpr int NCLW = NCL * B / 32;      // code words per lane per super-step
+  constexpr int CW_SS = SS / D * B / 32;  // code words per row per super-step
 
   // Static LDS: codebook, then the two x tiles [2][WN][XROW].
   __shared__ __align__(16) uint8_t cb_lds[L::kBytes];
@@ -131,8 +158,8 @@ __global__ __launch_bounds__(256) void vq_gemm_kernel(GemmArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int l16 = lane & 15;
-  const int g = lane >> 4;
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
 
   // ---- which tile ----
   int rt, expert = 0, first = 0, count;
@@ -166,26 +193,33 @@ __global__ __launch_bounds__(256) void vq_gemm_kernel(GemmArgs a) {
   const uint16_t* scales = a.scales + (int64_t)expert * a.scale_estride;
   const uint16_t* cb = a.codebook + (int64_t)expert * a.cb_estride;
 
-  // All streaming loads are branch-free buffer loads with 32-bit offsets:
-  // tokens past the tile's count, rows past the end and columns past `cols`
-  // (the half super-step d = 2 can leave) get an out-of-range offset or fall
-  // outside the buffer and read zeros, so every load of a super-step is in
-  // flight at once and no lane needs a 64-bit address.
+  // K range (super-steps) of this block.
+  const int nks_all = (a.cols + SS - 1) / SS;
+  int ks_begin = 0, ks_end = nks_all;
+  if constexpr (!MOE) {
+    ks_begin = (int)((int64_t)nks_all * blockIdx.y / a.ksplit);
+    ks_end = (int)((int64_t)nks_all * (blockIdx.y + 1) / a.ksplit);
+  }
 
-  // ---- x loading assignment: XLD segments of 16 bytes per thread ----
-  const int seg = tid % SEGS;
+  // All streaming loads are branch-free buffer loads with 32-bit offsets:
+  // tokens past the tile's count, rows past the end and super-steps past
+  // ks_end get an out-of-range offset and read zeros.
+
+  // ---- x: XLD segments of 16 bytes per thread per super-step ----
   rsrc_t rx;
-  uint32_t xoff[XLD];
-  int xdst[XLD];
   if constexpr (MOE) {
     rx = make_rsrc(a.x, (uint64_t)a.x_rows * a.cols * 2);
   } else {
     rx = make_rsrc(a.x + (int64_t)tok_base * a.cols, (uint64_t)count * a.cols * 2);
   }
+  uint32_t xoff[XLD];
+  int xdst[XLD];
 #pragma unroll
   for (int i = 0; i < XLD; ++i) {
-    const int tok = tid / SEGS + i * (256 / SEGS);
-    xdst[i] = tok * XROW + seg * 16;
+    const int gs = tid + i * NT;
+    const int tok = gs / SEGS;
+    const int seg = gs % SEGS;
+    xdst[i] = gs < WN * SEGS ? tok * XROW + seg * 16 : -1;
     uint32_t row;
     if constexpr (MOE) {
       const int pair = tok < count ? a.pairs[first + tok] : 0;
@@ -193,123 +227,128 @@ __global__ __launch_bounds__(256) void vq_gemm_kernel(GemmArgs a) {
     } else {
       row = (uint32_t)tok;
     }
-    xoff[i] = tok < count ? row * (uint32_t)a.cols * 2u + (uint32_t)seg * 16u : kOutOfRange;
+    xoff[i] = (gs < WN * SEGS && tok < count) ? row * (uint32_t)a.cols * 2u + (uint32_t)seg * 16u : kOutOfRange;
   }
 
-  // ---- A assignment: wave owns rows rt*256 + wave*64 + [0, 64) ----
-  const int row_base = rt * 256 + wave * 64;
+  // ---- A: this wave's 32*MB rows, lane row l32 of each m-block ----
+  const int row_base = rt * SH::kRows + wave * 32 * MB;
   const rsrc_t rc = make_rsrc(codes, (uint64_t)a.rows * a.wr * 4);
   const rsrc_t rs = make_rsrc(scales, (uint64_t)a.rows * a.spr * 2);
   uint32_t coff[MB], soff[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    const uint32_t r = (uint32_t)(row_base + mb * 16 + l16);   // past the end: reads zeros
+    const uint32_t r = (uint32_t)(row_base + mb * 32 + l32);  // past the end: reads zeros
     coff[mb] = r * (uint32_t)a.wr * 4u;
     soff[mb] = r * (uint32_t)a.spr * 2u;
   }
 
-  const int nks = (a.cols + SS - 1) / SS;
-  constexpr int CW_SS = SS / D * B / 32;   // code words per row per super-step
-  constexpr int NCLW = NCL * B / 32;       // code words per lane per super-step
-
   auto load_x = [&](int ks, u32x4 (&xr)[XLD]) {
-    const bool ok = ks * SS + seg * 8 < a.cols;
-    const uint32_t colb = (uint32_t)ks * SS * 2u;
+    const bool live = ks < ks_end;
 #pragma unroll
-    for (int i = 0; i < XLD; ++i) xr[i] = buf_load_b128(rx, ok ? xoff[i] + colb : kOutOfRange);
+    for (int i = 0; i < XLD; ++i) xr[i] = buf_load_b128(rx, live ? xoff[i] + (uint32_t)ks * SS * 2u : kOutOfRange);
   };
   auto store_x = [&](int buf, const u32x4 (&xr)[XLD]) {
 #pragma unroll
     for (int i = 0; i < XLD; ++i)
-      *reinterpret_cast<u32x4*>(xbuf + buf * (WN * XROW) + xdst[i]) = xr[i];
+      if (xdst[i] >= 0) *reinterpret_cast<u32x4*>(xbuf + buf * (WN * XROW) + xdst[i]) = xr[i];
   };
   auto load_codes = [&](int ks, LaneCodes<NCL, B> (&cc)[MB], uint16_t (&sc)[MB]) {
-    const uint32_t wb = (uint32_t)(ks * CW_SS + g * NCLW) * 4u;
-    const uint32_t sb = (uint32_t)((ks * SS + g * CG) / G) * 2u;
+    const bool ok = ks < ks_end;
+    const uint32_t wb = (uint32_t)(ks * CW_SS + h * NCLW) * 4u;
+    const uint32_t sb = (uint32_t)((ks * SS + h * CG) / G) * 2u;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      load_lane_codes<NCL, B>(cc[mb], rc, coff[mb] + wb);
-      sc[mb] = buf_load_b16(rs, soff[mb] + sb);
+      load_lane_codes<NCL, B>(cc[mb], rc, ok ? coff[mb] + wb : kOutOfRange);
+      sc[mb] = buf_load_b16(rs, ok ? soff[mb] + sb : kOutOfRange);
     }
   };
 
   const uint32_t lane_off = lane_copy_offset<D, B>(lane);
-  float4_t acc[MB][NBT];
+  float16_t acc[MB][NB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < NBT; ++nb) acc[mb][nb] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
 
   // One super-step: dequantize the A fragments of each m-block straight into
-  // registers and run the MFMAs against the x tile in LDS buffer `buf`.
-  auto compute = [&](int ks, int buf, const LaneCodes<NCL, B> (&cc)[MB], const uint16_t (&sc)[MB]) {
-    const bool gcur = ks * SS + g * CG < a.cols;
+  // registers and run the MFMAs against the x tile in LDS buffer `buf`.  The
+  // codebook gathers of k-step s + 1 are issued before the arithmetic of
+  // k-step s, so their LDS latency overlaps the MFMAs.  Every super-step is
+  // whole: the API requires cols % (32 d) == 0 and SS divides 32 d.
+  auto compute = [&](int buf, const LaneCodes<NCL, B> (&cc)[MB], const uint16_t (&sc)[MB]) {
     const uint8_t* xb = xbuf + buf * (WN * XROW);
+    half2_t s2[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) s2[mb] = as_half2((uint32_t)sc[mb] * 0x10001u);
+    Entry<D> e[2][MB][CPA];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int c = 0; c < CPA; ++c) e[0][mb][c] = lane_gather<D, B, NCL>(cb_lds, cc[mb], c, lane_off);
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      half8_t bf[NBT];
+      if (s + 1 < S) {
 #pragma unroll
-      for (int nb = 0; nb < NBT; ++nb)
-        bf[nb] = *reinterpret_cast<const half8_t*>(xb + (nb * 16 + l16) * XROW + (g * CG + 8 * s) * 2);
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int c = 0; c < CPA; ++c)
+            e[(s + 1) & 1][mb][c] = lane_gather<D, B, NCL>(cb_lds, cc[mb], (s + 1) * CPA + c, lane_off);
+      }
+      half8_t bf[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        bf[nb] = *reinterpret_cast<const half8_t*>(xb + (nb * 32 + l32) * XROW + (h * CG + 8 * s) * 2);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const half2_t s2 = as_half2((uint32_t)sc[mb] | ((uint32_t)sc[mb] << 16));
         half2_t w[4];
 #pragma unroll
-        for (int c = 0; c < CPA; ++c) {
-          const Entry<D> e = lane_gather<D, B, NCL>(cb_lds, cc[mb], s * CPA + c, lane_off);
+        for (int c = 0; c < CPA; ++c)
 #pragma unroll
-          for (int j = 0; j < D / 2; ++j) w[c * (D / 2) + j] = e.v[j] * s2;
-        }
-        half8_t af = half8_t{w[0].x, w[0].y, w[1].x, w[1].y, w[2].x, w[2].y, w[3].x, w[3].y};
-        if (!gcur) af = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+          for (int j = 0; j < D / 2; ++j) w[c * (D / 2) + j] = e[s & 1][mb][c].v[j] * s2[mb];
+        const half8_t af = half8_t{w[0].x, w[0].y, w[1].x, w[1].y, w[2].x, w[2].y, w[3].x, w[3].y};
 #pragma unroll
-        for (int nb = 0; nb < NBT; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[nb], acc[mb][nb], 0, 0, 0);
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(af, bf[nb], acc[mb][nb]);
       }
     }
   };
 
   // Ping-pong over two register sets (A, B) and two LDS x buffers (0, 1):
   // the loads for super-step ks + 1 are issued before super-step ks is
-  // computed; no register copies, so the prefetch stays in flight.
+  // computed.  No register copies and no exit in the middle of the loop body
+  // (the second half is skipped by a uniform branch on an odd count), so the
+  // accumulators stay in place and the prefetch stays in flight.
   u32x4 xr[XLD];
   LaneCodes<NCL, B> ccA[MB], ccB[MB];
   uint16_t scA[MB], scB[MB];
 
-  load_x(0, xr);
-  load_codes(0, ccA, scA);
-  stage_codebook<D, B>(cb_lds, cb, tid, 256);
+  load_x(ks_begin, xr);
+  load_codes(ks_begin, ccA, scA);
+  stage_codebook<D, B>(cb_lds, cb, tid, NT);
   store_x(0, xr);
   __syncthreads();
 
-  for (int ks = 0; ks < nks; ks += 2) {
-    const bool has1 = ks + 1 < nks;
-    if (has1) {
-      load_x(ks + 1, xr);
-      load_codes(ks + 1, ccB, scB);
-    }
+  for (int ks = ks_begin; ks < ks_end; ks += 2) {
+    load_x(ks + 1, xr);
+    load_codes(ks + 1, ccB, scB);
     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
-    compute(ks, 0, ccA, scA);
-    if (has1) store_x(1, xr);
+    compute(0, ccA, scA);
+    store_x(1, xr);
     __syncthreads();
-    if (!has1) break;
-    const bool has2 = ks + 2 < nks;
-    if (has2) {
-      load_x(ks + 2, xr);
-      load_codes(ks + 2, ccA, scA);
-    }
+    load_x(ks + 2, xr);
+    load_codes(ks + 2, ccA, scA);
     __builtin_amdgcn_sched_barrier(0);
-    compute(ks + 1, 1, ccB, scB);
-    if (has2) store_x(0, xr);
+    if (ks + 1 < ks_end) compute(1, ccB, scB);
+    store_x(0, xr);
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds rows 4*g + i of each m-block for token l16 ----
+  // ---- epilogue: lane holds rows 8*(i/4) + 4*h + (i%4) of each m-block for token l32 ----
   const bool vec_ok = (a.rows & 3) == 0;
 #pragma unroll
-  for (int nb = 0; nb < NBT; ++nb) {
-    const int tok = nb * 16 + l16;
+  for (int nb = 0; nb < NB; ++nb) {
+    const int tok = nb * 32 + l32;
     if (tok >= count) continue;
     int yr;
     if constexpr (MOE) yr = a.pairs[first + tok];
@@ -317,18 +356,31 @@ __global__ __launch_bounds__(256) void vq_gemm_kernel(GemmArgs a) {
     float* yrow = a.y + (int64_t)yr * a.rows;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const int r = row_base + mb * 16 + 4 * g;
-      const float4_t v = acc[mb][nb];
-      if (vec_ok && r + 3 < a.rows) {
-        *reinterpret_cast<float4_t*>(yrow + r) = v;
-      } else {
-        if (r + 0 < a.rows) yrow[r + 0] = v.x;
-        if (r + 1 < a.rows) yrow[r + 1] = v.y;
-        if (r + 2 < a.rows) yrow[r + 2] = v.z;
-        if (r + 3 < a.rows) yrow[r + 3] = v.w;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int r = row_base + mb * 32 + 8 * i4 + 4 * h;
+        const float4_t v = float4_t{acc[mb][nb][4 * i4], acc[mb][nb][4 * i4 + 1],
+                                    acc[mb][nb][4 * i4 + 2], acc[mb][nb][4 * i4 + 3]};
+        if constexpr (ATOMIC) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (r + c < a.rows) atomicAdd(yrow + r + c, v[c]);
+        } else if (vec_ok && r + 3 < a.rows) {
+          *reinterpret_cast<float4_t*>(yrow + r) = v;
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (r + c < a.rows) yrow[r + c] = v[c];
+        }
       }
     }
   }
+}
+
+// Zero fill (a kernel rather than hipMemsetAsync, so it can sit in a graph).
+__global__ void vq_zero_kernel(float* y, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    y[i] = 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -424,15 +476,28 @@ __global__ __launch_bounds__(1024) void vq_route_kernel(RouteArgs a) {
 
 namespace {
 
-constexpr int kMoeTileTokens = 64;
+using GemmSmallT = GemmShape<4, 4, 1>;  // 512 rows x 32 tokens
+using GemmLargeT = GemmShape<8, 2, 4>;  // 512 rows x 128 tokens
+using GemmMoe = GemmShape<4, 4, 2>;     // 512 rows x 64 tokens
+constexpr int kMoeTileTokens = GemmMoe::kTokens;
 
 int max_tiles_for(int npairs, int E) { return (npairs + kMoeTileTokens - 1) / kMoeTileTokens + E; }
 
-template <int D, int B, int G, int NBT, bool MOE>
+template <int D, int B, int G, class SH, bool MOE, bool ATOMIC>
 hipError_t gemm_launch(const GemmArgs& a, dim3 grid, hipStream_t s) {
-  auto k = vq_gemm_kernel<D, B, G, NBT, MOE>;
-  hipLaunchKernelGGL(k, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((vq_gemm_kernel<D, B, G, SH, MOE, ATOMIC>), grid, dim3(SH::kThreads), 0, s, a);
   return hipGetLastError();
+}
+
+int num_cus() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+  }
+  return n;
 }
 
 GemmArgs base_args(const TensorView& w, const uint16_t* x, float* y, int G, int D, int B) {
@@ -449,26 +514,39 @@ GemmArgs base_args(const TensorView& w, const uint16_t* x, float* y, int G, int 
   a.cols = w.cols;
   a.wr = w.wr;
   a.spr = w.cols / G;
-  a.n_row_tiles = (w.rows + 255) / 256;
+  a.ksplit = 1;
   return a;
+}
+
+template <int D, int B, int G, class SH>
+hipError_t gemm_dense(GemmArgs a, hipStream_t s) {
+  a.n_row_tiles = (a.rows + SH::kRows - 1) / SH::kRows;
+  a.n_tok_tiles = (a.T + SH::kTokens - 1) / SH::kTokens;
+  const int tiles = a.n_row_tiles * a.n_tok_tiles;
+  const int nks = (a.cols + (D == 8 ? 128 : 64) - 1) / (D == 8 ? 128 : 64);
+  // Too few tiles to fill the chip: split K and add the slices atomically
+  // into a zeroed y (fp32 addition order then varies between runs).
+  int ksplit = 1;
+  if (tiles < num_cus()) ksplit = std::min(std::max(1, num_cus() / tiles), std::max(1, nks / 8));
+  a.ksplit = ksplit;
+  dim3 grid(tiles, ksplit);
+  if (ksplit > 1) {
+    const int64_t n = (int64_t)a.T * a.rows;
+    hipLaunchKernelGGL(vq_zero_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256), 0, s,
+                       a.y, n);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return gemm_launch<D, B, G, SH, false, true>(a, grid, s);
+  }
+  return gemm_launch<D, B, G, SH, false, false>(a, grid, s);
 }
 
 template <int D, int B, int G>
 hipError_t gemm_geom(const TensorView& w, const uint16_t* x, int T, float* y, hipStream_t s) {
   GemmArgs a = base_args(w, x, y, G, D, B);
   a.T = T;
-  // token tile: 128 for long prompts, smaller when there are few tokens
-  // (d = 8 is held to 64 by LDS: 64 KiB codebook + x tiles)
-  int nbt = std::min((T + 15) / 16, 4);
-  if (nbt > 2) nbt = 4;
-  a.n_tok_tiles = (T + 16 * nbt - 1) / (16 * nbt);
-  dim3 grid(a.n_row_tiles * a.n_tok_tiles);
-  switch (nbt) {
-    case 1: return gemm_launch<D, B, G, 1, false>(a, grid, s);
-    case 2: return gemm_launch<D, B, G, 2, false>(a, grid, s);
-    case 4: return gemm_launch<D, B, G, 4, false>(a, grid, s);
-    default: return gemm_launch<D, B, G, 4, false>(a, grid, s);
-  }
+  if (T <= 32) return gemm_dense<D, B, G, GemmSmallT>(a, s);
+  return gemm_dense<D, B, G, GemmLargeT>(a, s);
 }
 
 template <int D, int B, int G>
@@ -501,8 +579,9 @@ hipError_t moe_gemm_geom(const TensorView& w, const uint16_t* x, int x_per_slot,
   a.top_k = top_k;
   a.x_per_slot = x_per_slot;
   a.x_rows = x_per_slot ? npairs : T;
+  a.n_row_tiles = (a.rows + GemmMoe::kRows - 1) / GemmMoe::kRows;
   dim3 grid(mt, a.n_row_tiles);
-  return gemm_launch<D, B, G, kMoeTileTokens / 16, true>(a, grid, s);
+  return gemm_launch<D, B, G, GemmMoe, true, false>(a, grid, s);
 }
 
 }  // namespace
