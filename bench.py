@@ -44,7 +44,66 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=1024,
                     help="rows of the gate matrix the CPU oracle sample covers")
+    ap.add_argument("--profile-gate", action="store_true",
+                    help="run only a few gate GEMV and GEMM launches (for rocprofv3 --pmc passes)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only a plain device copy of known size (counter calibration)")
     return ap.parse_args()
+
+
+COPY_PROBE_ELEMS = 1 << 28          # fp16 -> fp32 copy: reads 512 MiB, writes 1 GiB
+COPY_READ_BYTES = 2 * COPY_PROBE_ELEMS
+COPY_WRITE_BYTES = 4 * COPY_PROBE_ELEMS
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def copy_probe():
+    """A plain converting copy of known size (fp16 -> fp32, 2^28 elements),
+    four times: what FETCH_SIZE and WRITE_SIZE read for it calibrates them
+    against known traffic."""
+    import torch
+    src = torch.ones(COPY_PROBE_ELEMS, dtype=torch.float16, device="cuda")
+    dst = torch.empty(COPY_PROBE_ELEMS, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_read_bytes": COPY_READ_BYTES, "copy_write_bytes": COPY_WRITE_BYTES,
+                      "launches": 4}), flush=True)
+
+
+def _pmc_value(fname, counter, kernel_prefix):
+    """Average per-dispatch value of `counter` for the first kernel whose
+    name starts with kernel_prefix, from a profsum pmc summary."""
+    path = os.path.join(PROFILES, fname)
+    if not os.path.exists(path):
+        return None, None
+    digest = None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("library source digest:"):
+                digest = line.split(":", 1)[1].strip()
+            if line.startswith(kernel_prefix):
+                for part in line.split():
+                    if part.startswith(counter + "="):
+                        return float(part.split("=", 1)[1]), digest
+    return None, digest
+
+
+def measured_traffic(kernel_prefix, tag):
+    """HBM bytes per launch of the named kernel from the committed FETCH_SIZE
+    and WRITE_SIZE passes, each scaled by the same counter's reading for the
+    1 GiB copy; None when a pass is missing or the kernels changed since."""
+    from vq_dequant_matmul_gemv_amd.profsum import source_digest
+    f, fd = _pmc_value(f"pmc_fetch_size_{tag}.txt", "FETCH_SIZE", kernel_prefix)
+    w, wd = _pmc_value(f"pmc_write_size_{tag}.txt", "WRITE_SIZE", kernel_prefix)
+    cf, _ = _pmc_value("pmc_fetch_size_copy.txt", "FETCH_SIZE", "torch copy")
+    cw, _ = _pmc_value("pmc_write_size_copy.txt", "WRITE_SIZE", "torch copy")
+    if None in (f, w, cf, cw) or fd != source_digest() or wd != source_digest():
+        return None
+    fetch_scale = (COPY_READ_BYTES / 1024) / cf     # true KiB per counted KiB
+    write_scale = (COPY_WRITE_BYTES / 1024) / cw
+    return round((f * fetch_scale + w * write_scale) * 1024)
 
 
 def tensor_bytes(spec, T):
@@ -88,7 +147,6 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     from vq_dequant_matmul_gemv_amd import binding, synth
 
@@ -97,6 +155,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        copy_probe()
+        return
 
     wl = synth.WORKLOADS[WORKLOAD]
     names = ["gate", "up", "down"]
@@ -119,6 +180,15 @@ def main():
     yd = {n: torch.empty((DECODE_T, specs[n].rows), dtype=torch.float32, device=dev) for n in names}
     yp = {n: torch.empty((PREFILL_T, specs[n].rows), dtype=torch.float32, device=dev) for n in names}
     torch.cuda.synchronize()
+
+    if args.profile_gate:
+        for i in range(4):
+            binding.gemv(reps[i % REPLICAS]["gate"], xd["gate"], yd["gate"])
+        for i in range(2):
+            binding.gemm(reps[i % REPLICAS]["gate"], xp["gate"], yp["gate"])
+        torch.cuda.synchronize()
+        print("profile-gate: 4 gate GEMVs (T=1), 2 gate GEMMs (T=2048)", flush=True)
+        return
 
     dec_bytes = {n: tensor_bytes(specs[n], DECODE_T) for n in names}
     pre_flops = {n: 2.0 * PREFILL_T * specs[n].rows * specs[n].cols for n in names}
@@ -221,11 +291,14 @@ def main():
         "kernel_us": {"gemv_gate_T1": round(gate_dec * 1e6, 2), "gemm_gate_T2048": round(gate_pre * 1e6, 2)},
         "roofline": {"bound": "hbm", "kernel": "vq_gemv (gate, T=1)",
                      "achieved": round(achieved_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic("vq_gemv_kernel<2, 8, 64", "gate"),
+                     "algorithmic_bytes": dec_bytes["gate"]},
         "roofline_prefill": {"bound": "mfma", "kernel": "vq_gemm (gate, T=2048)",
                              "achieved": round(achieved_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                              "unit": "TFLOP/s", "frac": round(achieved_tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                             "traffic": None},
+                             "traffic": measured_traffic("vq_gemm_kernel<2, 8, 64", "gate"),
+                             "algorithmic_bytes": tensor_bytes(specs["gate"], PREFILL_T)},
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(host["gate"], specs["gate"], args.cpu_rows)

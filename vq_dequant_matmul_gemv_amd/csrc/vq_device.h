@@ -263,6 +263,13 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// Block barrier that orders LDS only: waits for this wave's LDS operations,
+// not for its global loads in flight (a plain __syncthreads waits for those
+// too, which would stall a prefetch issued before the barrier).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }

@@ -9,22 +9,26 @@
 // with fp32 accumulation.  Each product of two fp16 values is exact in fp32.
 //
 // Design for gfx950 (batch-1 decode is bound by the bytes of codes + scales):
-//  * A row's code stream is cut into passes of 64 sixteen-code chunks (one
-//    chunk, 16 or 24 bytes, per lane).  Each wave of a block owns one pass
-//    position and a contiguous range of the block's rows: its lanes keep the
-//    x columns of that pass in VGPRs for the whole kernel ("x-stationary"),
-//    and every load instruction covers a contiguous 1 KiB (1.5 KiB) run of a
-//    row.  Waves never wait on each other until the block's final combine.
-//  * Each lane keeps a ring of PD rows' chunks in flight: the load for row
-//    u + PD is issued as soon as row u is consumed.  Loads are buffer loads
-//    with the row offset in an SGPR, so a load costs no address VALU.
-//  * The codebook sits in LDS; for K = 256 it is replicated so that a lane's
-//    gather bank depends only on its lane id (conflict-free).
-//  * Inner loop per code: one v_perm_b32 (LDS offset), one LDS read, d/2
-//    v_dot2_f32_f16 per token; the group scale multiplies the group's sum
-//    once (an fma per group).  A row piece is summed across the wave by DPP;
-//    with one pass per row it is stored directly, otherwise the pieces go to
-//    a small LDS table and are added in pass order after one barrier.
+//  * A block owns a contiguous range of rows.  Its waves walk the range in
+//    row groups: a group is 64 / L rows, each row served by L lanes, each lane
+//    holding C sixteen-code chunks of the row (chunks li, li + L, ... of the
+//    pass), so one load instruction reads a contiguous run of every row of the
+//    group and all 64 lanes are busy.  A row longer than L*C chunks is covered
+//    in several passes whose partial sums meet in LDS.
+//  * Everything small is staged once per block, before any compute: the x
+//    columns of the launch, the block's scales and the codebook (replicated
+//    for K = 256 so that a lane's gather bank depends only on its lane id).
+//    The per-row stream then carries only code loads, one 16-byte (or 24-byte)
+//    load per chunk and lane: the number of memory instructions in flight
+//    per CU, not their bytes, is what limits a streaming kernel here, so no
+//    instruction is spent on a 2-byte scale.
+//  * x sits in VGPRs for a whole pass (x-stationary); the inner loop per code
+//    is one v_perm_b32 (LDS offset), one LDS gather and d/2 v_dot2_f32_f16 per
+//    token; the group scale multiplies each group sum once.
+//  * Each wave has one row group's loads in flight at a time and issues the
+//    next group's loads right after computing the current one; deeper
+//    prefetch only holds the wave at the issue of loads that cannot enter the
+//    CU's full memory queue.
 //  * Routed experts (top-k MoE): blockIdx.y is the (token, slot) pair; the
 //    block reads its expert id and points at that expert's codes and scales.
 //    An id outside [0, E) writes a zero row.
@@ -47,69 +51,76 @@ struct GemvArgs {
   int64_t scale_estride;  // fp16 between experts
   int64_t cb_estride;     // fp16 between per-expert codebooks (0: shared)
   int rows, cols, wr, spr;
-  int P;                  // 16-code chunks per row in this column slice
-  int p0;                 // first chunk of the slice
-  int passes;             // ceil(P / 64)
-  int waves_per_pass;     // waves of a block sharing one pass position
+  int rows_base, rows_extra;  // block b owns rows_base (+1 if b < rows_extra) rows
+  int q0, nq;             // column slice of this launch, in 16-code chunks
+  int lanes_log2;         // L = 1 << lanes_log2 lanes per row (2..5)
+  int passes;             // ceil(nq / (L * C))
   int accumulate;         // add into y (column slices after the first)
   int T;                  // dense: tokens; routed: pairs
+  int tok0;               // dense: first token of this launch
   int top_k;
   int num_experts;
   int x_per_slot;
 };
 
-constexpr int gemv_max_tt(int D) { return D == 8 ? 1 : 2; }
-// Waves per block: 16 where x (8*d VGPRs per token) and the ring fit in 128
-// VGPRs, else 8.
-constexpr int gemv_max_waves(int D, int TT) { return (D == 2 || (D == 4 && TT == 1)) ? 16 : 8; }
-// Rows in flight per lane.  Measured on MI355X (17408x5120, d=2): a ring of
-// 3-4 rows with 15-16 waves per CU beats deeper rings (6: +8 %, 12: +30 %);
-// more outstanding requests per CU only queue up.
-template <int D, int B, int TT>
-struct GemvCfg {
-  static constexpr int kPD = gemv_max_waves(D, TT) == 16 ? 4 : 6;
-};
-constexpr int kGemvRowPieces = 4096;  // LDS table entries for split rows (floats)
+constexpr int kGemvWaves = 8;                  // two waves per SIMD
+constexpr int kGemvThreads = 64 * kGemvWaves;
+constexpr int kGemvXMaxBytes = 40 * 1024;      // largest x slice in LDS (all tokens of the tile)
+constexpr int kGemvScaleBytes = 16 * 1024;     // the block's scales
+constexpr int kGemvPieces = 4096;              // per-(row, pass, token) partial sums
 
-// Total of v over the 64 lanes of the wave, valid in lane 63.
-__device__ __forceinline__ float wave_sum_to_lane63(float v) {
-  v = row16_sum(v);
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false));
+constexpr int gemv_max_tt(int D) { return D == 8 ? 1 : 2; }
+
+// Chunks per lane a pass can hold in VGPRs: x costs 8*d VGPRs per chunk and token.
+__host__ __device__ constexpr int gemv_max_c(int D, int TT) {
+  return D == 2 ? (TT == 1 ? 5 : 2) : (D == 4 ? (TT == 1 ? 2 : 1) : 1);
+}
+
+// Sum of v over aligned groups of L = 1 << lg lanes; valid in the group's last lane.
+__device__ __forceinline__ float lane_group_sum(float v, int lg) {
+  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]: every lane holds its quad's sum
+  if (lg >= 3) v += dpp_mov<0x141>(v);  // row_half_mirror: 8-lane sums
+  if (lg >= 4) v += dpp_mov<0x140>(v);  // row_mirror: 16-lane sums
+  if (lg >= 5)                          // row_bcast15: rows 1 and 3 add rows 0 and 2
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
   return v;
 }
 
-template <int D, int B, int G, int TT, bool MOE>
-__global__ __launch_bounds__(64 * gemv_max_waves(D, TT)) void vq_gemv_kernel(GemvArgs a) {
-  using L = CodebookLayout<D, B>;
-  constexpr int PD = GemvCfg<D, B, TT>::kPD;
+// XS: the x slice takes XS * 8 KiB of LDS (2 or 5); fewer staging loads for
+// short rows.
+template <int D, int B, int G, int TT, int C, int XS, bool MOE>
+__global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
+  using LY = CodebookLayout<D, B>;
   constexpr int NSC = (16 * D > G) ? (16 * D / G) : 1;  // scales per chunk
   constexpr int CPS = 16 / NSC;                          // codes per scale in a chunk
   constexpr int HX = 8 * D;                              // half2 of x per chunk per token
   constexpr int CB = Chunk<B>::kWords * 4;               // code bytes per chunk
-  static_assert(TT <= gemv_max_tt(D), "token tile too large for this d");
+  constexpr int NW = kGemvWaves;
+  constexpr int NT = kGemvThreads;
+  static_assert(TT <= gemv_max_tt(D) && C <= gemv_max_c(D, TT), "tile does not fit the VGPR budget");
 
-  __shared__ __align__(16) uint8_t cb_lds[L::kBytes];
-  __shared__ __align__(16) u32x4 raw[256];               // replicated layout: entries before expansion
-  __shared__ float pieces[kGemvRowPieces];               // [brows][passes][TT] when passes > 1
+  __shared__ __align__(16) uint8_t cb_lds[LY::kBytes];
+  __shared__ __align__(16) u32x4 raw[LY::kReplicated ? 256 : 1];   // replicated layout: entries before expansion
+  constexpr int XBYTES = XS * 8192;
+  __shared__ __align__(16) uint8_t x_lds[XBYTES];                   // [TT][nq * 16 * D] fp16
+  __shared__ __align__(16) uint8_t s_lds[kGemvScaleBytes];          // the block's scale rows
+  __shared__ float pieces[kGemvPieces];                             // [rows][passes][TT]
 
   const int tid = threadIdx.x;
-  const int nt = blockDim.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
-  const int passes = a.passes;
-  const int k = a.waves_per_pass;
-  const int c = wave % passes;                           // this wave's pass
-  const int jw = wave / passes;                          // its slot among the pass's waves
-  const bool wave_on = jw < k;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lg = a.lanes_log2;
+  const int L = 1 << lg;
+  const int R = 64 >> lg;                 // rows per group
+  const int rsub = lane >> lg;            // this lane's row within the group
+  const int li = lane & (L - 1);          // this lane's position within the row
 
-  // ---- this block's rows, this wave's rows ----
-  const int nblk = gridDim.x;
-  const int brow0 = (int)((int64_t)a.rows * blockIdx.x / nblk);
-  const int brows = (int)((int64_t)a.rows * (blockIdx.x + 1) / nblk) - brow0;
-  const int wr0 = wave_on ? brows * jw / k : 0;
-  const int wr1 = wave_on ? brows * (jw + 1) / k : 0;
-  const int nrows = wr1 - wr0;
+  // ---- this block's rows ----
+  const int bid = blockIdx.x;
+  const int brow0 = bid * a.rows_base + min(bid, a.rows_extra);
+  const int brows = a.rows_base + (bid < a.rows_extra ? 1 : 0);
+  const int ngroups = (brows + R - 1) / R;
 
   const uint32_t* codes = a.codes;
   const uint16_t* scales = a.scales;
@@ -122,89 +133,138 @@ __global__ __launch_bounds__(64 * gemv_max_waves(D, TT)) void vq_gemv_kernel(Gem
     const int e = a.ids[pair];
     yb = a.y + (int64_t)pair * a.rows;
     if (e < 0 || e >= a.num_experts) {  // skipped slot: zero rows (block-uniform exit)
-      if (a.p0 == 0)
-        for (int r = tid; r < brows; r += nt) yb[brow0 + r] = 0.f;
+      if (!a.accumulate)
+        for (int r = tid; r < brows; r += NT) yb[brow0 + r] = 0.f;
       return;
     }
     codes += (int64_t)e * a.code_estride;
     scales += (int64_t)e * a.scale_estride;
     cb += (int64_t)e * a.cb_estride;
-    const int t = pair / a.top_k;
-    xb = a.x + (int64_t)(a.x_per_slot ? pair : t) * a.cols;
+    xb = a.x + (int64_t)(a.x_per_slot ? pair : pair / a.top_k) * a.cols;
     ntok = 1;
   } else {
-    const int tok0 = blockIdx.y * TT;
-    xb = a.x + (int64_t)tok0 * a.cols;
-    yb = a.y + (int64_t)tok0 * a.rows;
-    ntok = min(TT, a.T - tok0);
+    const int t0 = a.tok0 + blockIdx.y * TT;
+    xb = a.x + (int64_t)t0 * a.cols;
+    yb = a.y + (int64_t)t0 * a.rows;
+    ntok = min(TT, a.T - t0);
   }
 
-  const int p = c * 64 + lane;            // chunk within the slice
-  const int gp = a.p0 + p;                // chunk within the full row
-  const bool in_row = p < a.P;            // lanes past the row end add nothing
-
-  // ---- x of this lane's chunk into VGPRs; codebook entries ----
-  const rsrc_t rx = make_rsrc(xb, (uint64_t)ntok * a.cols * 2);
-  u32x4 xr[TT][HX / 4];
+  // ---- small loads first: x slice, codebook entries, the block's scales ----
+  const int xcols = a.nq * 16 * D;                      // columns of the slice
+  const uint32_t xbytes = (uint32_t)xcols * 2u;         // per token
+  constexpr int XL = (XBYTES + NT * 16 - 1) / (NT * 16);
+  u32x4 xg[XL];
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-    for (int q = 0; q < HX / 4; ++q)
-      xr[tt][q] = buf_load_b128(rx, in_row ? (uint32_t)(tt * a.cols + gp * 16 * D) * 2u + 16u * q : kOutOfRange);
+  for (int q = 0; q < XL; ++q) {
+    const uint32_t o = (uint32_t)(tid + q * NT) * 16u;  // byte in the [TT][xcols] tile
+    const uint32_t tt = o / xbytes, co = o - tt * xbytes;
+    const bool ok = o < (uint32_t)TT * xbytes && (int)tt < ntok;
+    const rsrc_t rx = make_rsrc(xb, (uint64_t)ntok * a.cols * 2);
+    xg[q] = buf_load_b128(rx, ok ? tt * (uint32_t)a.cols * 2u + (uint32_t)a.q0 * 32u * D + co : kOutOfRange);
+  }
   u32x4 ce = u32x4{0u, 0u, 0u, 0u};
-  if constexpr (L::kReplicated) {
+  if constexpr (LY::kReplicated) {
     if (tid < 256) {
       if constexpr (D == 2) ce.x = reinterpret_cast<const uint32_t*>(cb)[tid];
       else if constexpr (D == 4) { const u32x2 t = reinterpret_cast<const u32x2*>(cb)[tid]; ce.x = t.x; ce.y = t.y; }
       else ce = reinterpret_cast<const u32x4*>(cb)[tid];
     }
   }
-
-  // ---- the prefetch ring: row offsets in SGPRs, lane offsets constant ----
-  const rsrc_t rc = make_rsrc(codes, (uint64_t)a.rows * a.wr * 4);
-  const rsrc_t rs = make_rsrc(scales, (uint64_t)a.rows * a.spr * 2);
-  const uint32_t row_cb = (uint32_t)a.wr * 4u;
-  const uint32_t row_sb = (uint32_t)a.spr * 2u;
-  const uint32_t c_lane = in_row ? (uint32_t)gp * CB : kOutOfRange;
-  const uint32_t s_lane = in_row ? (uint32_t)((gp * 16 * D) / G) * 2u : kOutOfRange;
-
-  Chunk<B> ring[PD];
-  uint16_t rsc[PD][NSC];
-  int l_row = 0;  // next row (of this wave's range) to load
-  // Loads are unconditional: a row past the wave's range gets an
-  // out-of-range lane offset and reads zeros, so every ring slot issues the
-  // same loads and the in-order vmcnt waits stay exact.
-  auto load_row = [&](Chunk<B>& ch, uint16_t (&sc)[NSC]) {
-    const bool live = l_row < nrows;
-    const uint32_t so = live ? (uint32_t)(brow0 + wr0 + l_row) * row_cb : 0u;
-    const uint32_t ss = live ? (uint32_t)(brow0 + wr0 + l_row) * row_sb : 0u;
-    const uint32_t vc = live ? c_lane : kOutOfRange;
-    const uint32_t vs = live ? s_lane : kOutOfRange;
-    if constexpr (B == 8) {
-      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, vc, so, 0));
-      ch.w[0] = v.x; ch.w[1] = v.y; ch.w[2] = v.z; ch.w[3] = v.w;
-    } else {
+  // scale rows [brow0, brow0 + brows), read as 16-byte pieces from a 16-byte
+  // boundary at or below the first scale
+  const uint64_t s_first = (uint64_t)brow0 * a.spr * 2u;
+  const uint32_t s_skew = (uint32_t)(s_first & 15u);
+  const uint32_t s_span = (uint32_t)brows * (uint32_t)a.spr * 2u + s_skew;
+  const uint32_t s_avail = (uint32_t)((uint64_t)a.rows * a.spr * 2u - (s_first - s_skew));  // to the tensor's end
+  const rsrc_t rsb = make_rsrc(reinterpret_cast<const uint8_t*>(scales) + (s_first - s_skew), s_avail);
+  constexpr int SL = (kGemvScaleBytes + NT * 16 - 1) / (NT * 16);
+  u32x4 sg[SL];
 #pragma unroll
-      for (int h = 0; h < 3; ++h) {
-        const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rc, vc + 8u * h, so, 0));
-        ch.w[2 * h] = v.x; ch.w[2 * h + 1] = v.y;
+  for (int q = 0; q < SL; ++q) {
+    const uint32_t o = (uint32_t)(tid + q * NT) * 16u;
+    sg[q] = buf_load_b128(rsb, (o < s_span && o + 16u <= s_avail) ? o : kOutOfRange);
+    if (o < s_span && o + 16u > s_avail) {  // the tensor ends inside this piece: 2-byte loads
+      uint32_t h[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) h[k] = buf_load_b16(rsb, o + 2u * k < s_avail ? o + 2u * k : kOutOfRange);
+      sg[q] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    }
+  }
+
+  // Every wave's small loads enter the CU's in-order memory queue ahead of
+  // any wave's code loads (a plain s_barrier: it waits for no load).
+  __builtin_amdgcn_s_barrier();
+
+  // ---- the code stream: work item u = (pass, group) in pass-major order ----
+  const rsrc_t rc = make_rsrc(codes, (uint64_t)a.rows * a.wr * 4);
+  const uint32_t row_cb = (uint32_t)a.wr * 4u;
+  const int LC = L * C;                                 // chunks per pass
+  // items f = pass * ngroups + group, dealt round-robin over the waves
+  const int total_items = ngroups * a.passes;
+  const int n_items = total_items > wave ? (total_items - wave + NW - 1) / NW : 0;
+  Chunk<B> ring[C];                                     // codes of the item in flight
+  int l_item = 0;                                       // next item to load
+  int l_pass = 0, l_g = wave;                           // its pass and group
+  while (l_g >= ngroups && ngroups > 0) { l_g -= ngroups; ++l_pass; }
+  uint32_t lane_vo[C];                                  // per-lane code offsets of l_pass
+  auto set_pass_offsets = [&](int pass) {
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const int q = pass * LC + j * L + li;
+      lane_vo[j] = q < a.nq ? (uint32_t)rsub * row_cb + (uint32_t)(a.q0 + q) * CB : kOutOfRange;
+    }
+  };
+  set_pass_offsets(l_pass);
+  // Loads are unconditional: a chunk past the slice, a row past the block or
+  // an item past the wave's list gets an out-of-range offset and reads zeros,
+  // so every item issues the same loads and the in-order vmcnt waits stay exact.
+  auto load_item = [&]() {
+    const bool live = l_item < n_items;
+    const int g = l_g;
+    const int r = brow0 + g * R;                        // first row of the group
+    const bool rowok = live && g * R + rsub < brows;
+    const uint32_t so = live ? (uint32_t)r * row_cb : 0u;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const uint32_t vo = rowok ? lane_vo[j] : kOutOfRange;
+      if constexpr (B == 8) {
+        const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, vo, so, 0));
+        ring[j].w[0] = v.x; ring[j].w[1] = v.y; ring[j].w[2] = v.z; ring[j].w[3] = v.w;
+      } else {
+#pragma unroll
+        for (int h = 0; h < 3; ++h) {
+          const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rc, vo + 8u * h, so, 0));
+          ring[j].w[2 * h] = v.x; ring[j].w[2 * h + 1] = v.y;
+        }
       }
     }
-#pragma unroll
-    for (int s2 = 0; s2 < NSC; ++s2) sc[s2] = __builtin_amdgcn_raw_buffer_load_b16(rs, vs + 2u * s2, ss, 0);
-    ++l_row;
+    ++l_item;
+    l_g += NW;
+    if (l_g >= ngroups) {
+      while (l_g >= ngroups) { l_g -= ngroups; ++l_pass; }
+      set_pass_offsets(l_pass);
+    }
   };
-#pragma unroll
-  for (int j = 0; j < PD; ++j) load_row(ring[j], rsc[j]);
+  load_item();
 
-  if constexpr (L::kReplicated) {
+  // ---- stage the small data in LDS ----
+  if constexpr (LY::kReplicated) {
     if (tid < 256) raw[tid] = ce;
-  } else {
-    stage_codebook<D, B>(cb_lds, cb, tid, nt);
   }
-  __syncthreads();
-  if constexpr (L::kReplicated) {
-    for (int q = tid; q < 4096; q += nt) {  // slot q holds copies of entry q / 16
+#pragma unroll
+  for (int q = 0; q < XL; ++q) {
+    const uint32_t o = (uint32_t)(tid + q * NT) * 16u;
+    if (o < (uint32_t)XBYTES) *reinterpret_cast<u32x4*>(x_lds + o) = xg[q];
+  }
+#pragma unroll
+  for (int q = 0; q < SL; ++q) {
+    const uint32_t o = (uint32_t)(tid + q * NT) * 16u;
+    if (o < (uint32_t)kGemvScaleBytes) *reinterpret_cast<u32x4*>(s_lds + o) = sg[q];
+  }
+  if constexpr (!LY::kReplicated) stage_codebook<D, B>(cb_lds, cb, tid, NT);
+  lds_barrier();
+  if constexpr (LY::kReplicated) {
+    for (int q = tid; q < 4096; q += NT) {  // slot q holds copies of entry q / 16
       const u32x4 e = raw[q >> 4];
       u32x4 v;
       if constexpr (D == 2) v = u32x4{e.x, e.x, e.x, e.x};
@@ -212,76 +272,105 @@ __global__ __launch_bounds__(64 * gemv_max_waves(D, TT)) void vq_gemv_kernel(Gem
       else v = e;
       reinterpret_cast<u32x4*>(cb_lds)[q] = v;
     }
-    __syncthreads();
+    lds_barrier();
   }
 
-  half2_t xv[TT][HX];
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-    for (int q = 0; q < HX / 4; ++q) {
-      xv[tt][4 * q + 0] = as_half2(xr[tt][q].x);
-      xv[tt][4 * q + 1] = as_half2(xr[tt][q].y);
-      xv[tt][4 * q + 2] = as_half2(xr[tt][q].z);
-      xv[tt][4 * q + 3] = as_half2(xr[tt][q].w);
-    }
-
   const uint32_t lane_off = lane_copy_offset<D, B>(lane);
-  // one pass and no accumulation: a row's wave sum is final; otherwise the
-  // pieces meet in LDS and are stored (or added) after the loop
-  const bool direct = passes == 1 && !a.accumulate;
-  int c_row = 0;  // next row to compute
-  auto compute_row = [&](const Chunk<B>& ch, const uint16_t (&sc)[NSC]) {
-    float acc[TT];
+  const bool direct = a.passes == 1 && !a.accumulate;
+  half2_t xv[TT][C][HX];
+  int cur_pass = -1;
+  int pass = 0, g = wave;
+  while (g >= ngroups && ngroups > 0) { g -= ngroups; ++pass; }
+  for (int u = 0; u < n_items; ++u) {
+    if (pass != cur_pass) {  // x of this pass into VGPRs (zeros past the slice)
+      cur_pass = pass;
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) acc[tt] = 0.f;
-#pragma unroll
-    for (int s2 = 0; s2 < NSC; ++s2) {
-      float g[TT];
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) g[tt] = 0.f;
-#pragma unroll
-      for (int i = s2 * CPS; i < (s2 + 1) * CPS; ++i) {
-        const Entry<D> e = gather<D, B>(cb_lds, ch, i, lane_off);
+      for (int j = 0; j < C; ++j) {
+        const int q = pass * LC + j * L + li;
+        const bool ok = q < a.nq;
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-          for (int j = 0; j < D / 2; ++j) g[tt] = dot2(e.v[j], xv[tt][i * (D / 2) + j], g[tt]);
+          for (int k = 0; k < HX / 4; ++k) {
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (ok) v = *reinterpret_cast<const u32x4*>(x_lds + tt * xbytes + (uint32_t)q * 32u * D + 16u * k);
+            xv[tt][j][4 * k + 0] = as_half2(v.x);
+            xv[tt][j][4 * k + 1] = as_half2(v.y);
+            xv[tt][j][4 * k + 2] = as_half2(v.z);
+            xv[tt][j][4 * k + 3] = as_half2(v.w);
+          }
       }
-      const float scale = half_bits_to_float(sc[s2]);
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) acc[tt] = __builtin_fmaf(g[tt], scale, acc[tt]);
     }
-    const int r = wr0 + c_row;  // block-relative row
+
+    const int rb = g * R + rsub;                        // row within the block
+    float acc[TT];
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      const float v = wave_sum_to_lane63(in_row ? acc[tt] : 0.f);
-      if (lane == 63) {
-        if (direct) {
-          if (tt < ntok) yb[(int64_t)tt * a.rows + brow0 + r] = v;
-        } else {
-          pieces[(r * passes + c) * TT + tt] = v;
+    for (int tt = 0; tt < TT; ++tt) acc[tt] = 0.f;
+    // The gathers of chunk j + 1 are issued before the dot products of
+    // chunk j.  Everything is computed unconditionally; a chunk past the
+    // slice or a row past the block is dropped with a bit mask (a select
+    // would let the compiler branch around the gathers).
+    Entry<D> e[2][16];
+    auto issue = [&](int j, Entry<D> (&dst)[16]) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dst[i] = gather<D, B>(cb_lds, ring[j], i, lane_off);
+    };
+    issue(0, e[0]);
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      if (j + 1 < C) issue(j + 1, e[(j + 1) & 1]);
+      const int q = pass * LC + j * L + li;
+      const bool ok = q < a.nq && rb < brows;
+      const uint32_t keep = ok ? 0xffffffffu : 0u;
+      const uint32_t sbase = s_skew + ((uint32_t)rb * (uint32_t)a.spr + ((uint32_t)(a.q0 + q) * 16u * D) / G) * 2u;
+#pragma unroll
+      for (int s2 = 0; s2 < NSC; ++s2) {
+        float gs[TT][2];  // two chains per token for ILP
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) gs[tt][0] = gs[tt][1] = 0.f;
+#pragma unroll
+        for (int i = s2 * CPS; i < (s2 + 1) * CPS; ++i)
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+            for (int k = 0; k < D / 2; ++k)
+              gs[tt][(i * (D / 2) + k) & 1] =
+                  dot2(e[j & 1][i].v[k], xv[tt][j][i * (D / 2) + k], gs[tt][(i * (D / 2) + k) & 1]);
+        const uint16_t sbits = *reinterpret_cast<const uint16_t*>(s_lds + (ok ? sbase + 2u * s2 : 0u));
+        const float scale = half_bits_to_float(sbits);
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+          const float gsum = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, gs[tt][0] + gs[tt][1]) & keep);
+          acc[tt] = __builtin_fmaf(gsum, __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, scale) & keep), acc[tt]);
         }
       }
     }
-    ++c_row;
-  };
-
-  for (int u0 = 0; u0 < nrows; u0 += PD) {
 #pragma unroll
-    for (int j = 0; j < PD; ++j) {
-      if (u0 + j < nrows) compute_row(ring[j], rsc[j]);  // wave-uniform branch
-      load_row(ring[j], rsc[j]);
+    for (int tt = 0; tt < TT; ++tt) {
+      const float v = lane_group_sum(acc[tt], lg);
+      if (li == L - 1 && rb < brows) {
+        if (direct) {
+          if (tt < ntok) yb[(int64_t)tt * a.rows + brow0 + rb] = v;
+        } else {
+          pieces[(rb * a.passes + pass) * TT + tt] = v;
+        }
+      }
     }
+    // Only now the next item's loads: measured on MI355X, issuing them before
+    // the compute (a second buffer) is slower, as the loads then wait in the
+    // CU's memory queue behind other waves' while this wave could compute.
+    load_item();
+    g += NW;
+    while (g >= ngroups) { g -= ngroups; ++pass; }
   }
 
   if (!direct) {  // add each row's pass pieces in pass order (deterministic)
     __syncthreads();
-    for (int r = tid; r < brows; r += nt) {
+    for (int r = tid; r < brows; r += NT) {
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
         float v = 0.f;
-        for (int cc = 0; cc < passes; ++cc) v += pieces[(r * passes + cc) * TT + tt];
+        for (int c = 0; c < a.passes; ++c) v += pieces[(r * a.passes + c) * TT + tt];
         if (tt < ntok) {
           float* dst = yb + (int64_t)tt * a.rows + brow0 + r;
           *dst = a.accumulate ? *dst + v : v;
@@ -357,34 +446,98 @@ int num_cus() {
   return n;
 }
 
-template <int D, int B, int G, int TT, bool MOE>
-hipError_t gemv_launch(const GemvArgs& a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((vq_gemv_kernel<D, B, G, TT, MOE>), grid, dim3(64 * a.passes * a.waves_per_pass),
-                     0, s, a);
+// Lane tiling of a slice of nq chunks: L = 1 << lg lanes per row, C chunks
+// per lane, `passes` passes.  Each wave has one row group in flight at a
+// time, so the bytes per group (L * C chunks per row) set how much every
+// memory round trip delivers: take the widest pass (largest L * C) that
+// leaves at most a quarter of the lane-chunk slots idle, then the widest
+// rows.  Idle slots cost issue slots, not bytes.
+struct LaneTiling {
+  int lg, C, passes;
+};
+
+LaneTiling plan_tiling(int nq, int max_c) {
+  LaneTiling best{2, 1, (nq + 3) / 4};
+  int best_lc = 0;
+  long best_slots = -1;
+  for (int C = 1; C <= max_c; ++C)
+    for (int lg = 2; lg <= 5; ++lg) {
+      const int LC = C << lg;
+      const int passes = (nq + LC - 1) / LC;
+      const long slots = (long)passes * LC;
+      if (4 * (slots - nq) > slots) continue;  // over a quarter idle
+      if (LC > best_lc || (LC == best_lc && lg > best.lg)) {
+        best = LaneTiling{lg, C, passes};
+        best_lc = LC;
+      }
+    }
+  if (best_lc == 0) {  // tiny rows: fewest slots
+    for (int C = 1; C <= max_c; ++C)
+      for (int lg = 2; lg <= 5; ++lg) {
+        const int LC = C << lg;
+        const int passes = (nq + LC - 1) / LC;
+        const long slots = (long)passes * LC;
+        if (best_slots < 0 || slots < best_slots) {
+          best = LaneTiling{lg, C, passes};
+          best_slots = slots;
+        }
+      }
+  }
+  return best;
+}
+
+template <int D, int B, int G, int TT, int C, int XS, bool MOE>
+hipError_t gemv_launch_c(const GemvArgs& a, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((vq_gemv_kernel<D, B, G, TT, C, XS, MOE>), grid, dim3(kGemvThreads), 0, s, a);
   return hipGetLastError();
 }
 
-// Rows are split over blocks so that one block per CU covers the grid; each
-// pass of a slice gets `waves_per_pass` waves; slices of at most
-// `max_waves` passes run one after another, accumulating into y.
+template <int D, int B, int G, int TT, int XS, bool MOE>
+hipError_t gemv_launch(const GemvArgs& a, int C, dim3 grid, hipStream_t s) {
+  constexpr int MC = gemv_max_c(D, TT);
+  switch (C) {
+    case 1: return gemv_launch_c<D, B, G, TT, 1, XS, MOE>(a, grid, s);
+    case 2: if constexpr (MC >= 2) return gemv_launch_c<D, B, G, TT, 2, XS, MOE>(a, grid, s); break;
+    case 3: if constexpr (MC >= 3) return gemv_launch_c<D, B, G, TT, 3, XS, MOE>(a, grid, s); break;
+    case 4: if constexpr (MC >= 4) return gemv_launch_c<D, B, G, TT, 4, XS, MOE>(a, grid, s); break;
+    case 5: if constexpr (MC >= 5) return gemv_launch_c<D, B, G, TT, 5, XS, MOE>(a, grid, s); break;
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
+// Column slices that fit the x tile in LDS run one after another, adding into
+// y; rows are split over about one block per CU, or more where a block's
+// scales or row pieces would not fit in LDS.
 template <int D, int B, int G, int TT, bool MOE>
-hipError_t gemv_slices(GemvArgs a, int P_total, int ycount, hipStream_t s) {
-  constexpr int maxw = gemv_max_waves(D, TT);
-  const int passes_total = (P_total + 63) / 64;
-  const int n_slices = (passes_total + maxw - 1) / maxw;
-  const int passes_per = (passes_total + n_slices - 1) / n_slices;
+hipError_t gemv_run(GemvArgs a, int P, int ycount, hipStream_t s) {
+  const int slice_max = kGemvXMaxBytes / (TT * 32 * D);
+  const int n_slices = (P + slice_max - 1) / slice_max;
+  const int per_slice = (P + n_slices - 1) / n_slices;
   const int blocks_fill = std::max(1, num_cus() / std::max(1, ycount));
   for (int sl = 0; sl < n_slices; ++sl) {
-    a.p0 = sl * passes_per * 64;
-    a.P = std::min(passes_per * 64, P_total - a.p0);
-    a.passes = (a.P + 63) / 64;
-    a.waves_per_pass = maxw / a.passes;
+    a.q0 = sl * per_slice;
+    a.nq = std::min(per_slice, P - a.q0);
     a.accumulate = sl > 0;
-    // enough blocks that each block's row-piece table fits in LDS
-    const int64_t min_blocks = ((int64_t)a.rows * a.passes * TT + kGemvRowPieces - 1) / kGemvRowPieces;
-    const int blocks = (int)std::min<int64_t>(a.rows, std::max<int64_t>(blocks_fill, min_blocks));
-    hipError_t e = gemv_launch<D, B, G, TT, MOE>(a, dim3(blocks, ycount), s);
-    if (e != hipSuccess) return e;
+    const LaneTiling t = plan_tiling(a.nq, gemv_max_c(D, TT));
+    a.lanes_log2 = t.lg;
+    a.passes = t.passes;
+    const int64_t by_scales = std::max<int64_t>(1, (kGemvScaleBytes - 16) / (2 * (int64_t)a.spr));
+    const int64_t by_pieces = std::max<int64_t>(1, kGemvPieces / ((int64_t)t.passes * TT));
+    const int64_t rows_max = std::min(by_scales, by_pieces);
+    const int64_t blocks = std::min<int64_t>(a.rows, std::max<int64_t>(blocks_fill, (a.rows + rows_max - 1) / rows_max));
+    a.rows_base = (int)(a.rows / blocks);
+    a.rows_extra = (int)(a.rows - (int64_t)a.rows_base * blocks);
+    const int XS = (int64_t)TT * a.nq * 32 * D <= 2 * 8192 ? 2 : 5;
+    // dense: at most 65535 token tiles per launch
+    for (int y0 = 0; y0 < ycount; y0 += 65535) {
+      const int yc = std::min(65535, ycount - y0);
+      if (!MOE) a.tok0 = y0 * TT;
+      hipError_t e = XS == 2 ? gemv_launch<D, B, G, TT, 2, MOE>(a, t.C, dim3((unsigned)blocks, (unsigned)yc), s)
+                             : gemv_launch<D, B, G, TT, 5, MOE>(a, t.C, dim3((unsigned)blocks, (unsigned)yc), s);
+      if (e != hipSuccess) return e;
+      if (MOE) break;
+    }
   }
   return hipSuccess;
 }
@@ -406,21 +559,19 @@ hipError_t gemv_geom(const TensorView& w, const uint16_t* x, int T, float* y, co
   a.cols = w.cols;
   a.wr = w.wr;
   a.spr = w.cols / G;
-  const int P_total = w.cols / (16 * D);
+  const int P = w.cols / (16 * D);
   a.top_k = top_k;
   a.num_experts = w.num_experts;
   a.x_per_slot = x_per_slot;
-  const int tt = std::min(T >= 2 ? 2 : 1, gemv_max_tt(D));
   if (ids) {
     a.T = T * top_k;
-    return gemv_slices<D, B, G, 1, true>(a, P_total, T * top_k, s);
+    return gemv_run<D, B, G, 1, true>(a, P, T * top_k, s);
   }
   a.T = T;
-  const int ycount = (T + tt - 1) / tt;
   if constexpr (gemv_max_tt(D) >= 2) {
-    if (tt == 2) return gemv_slices<D, B, G, 2, false>(a, P_total, ycount, s);
+    if (T >= 2) return gemv_run<D, B, G, 2, false>(a, P, (T + 1) / 2, s);
   }
-  return gemv_slices<D, B, G, 1, false>(a, P_total, ycount, s);
+  return gemv_run<D, B, G, 1, false>(a, P, T, s);
 }
 
 template <int D, int B, int G>
