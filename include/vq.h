@@ -83,7 +83,8 @@ typedef enum {
  * "Qwen3.8-27B-VQ-4.5bpw", Multi-machine note: codebooks must be replicated,
  * never sliced, and a sliced one must fail loudly).
  * Alignment (else VQ_ERR_ALIGN): codes 16 bytes; codebook 16 bytes; scales 4
- * bytes.
+ * bytes.  Size limit (else VQ_ERR_SHAPE): one expert's codes and its scales
+ * each fit in 2 GiB - 1 bytes (the kernels address them with 32-bit offsets).
  */
 typedef struct vq_tensor {
   const uint32_t *codes;    /* device [E][rows][Wr] packed codes                 */
@@ -117,8 +118,8 @@ vq_status vq_dequant(const vq_tensor *w, int32_t expert, uint16_t *w_out, void *
  *   x: device [T][cols] fp16 bits, 16-byte aligned;
  *   y: device [T][rows] fp32, 16-byte aligned.
  * T >= 0 (T == 0 enqueues nothing).  Any T is accepted; the kernel streams
- * every code once per group of up to four tokens, which is the fast path for
- * T = 1 (the fused decode-and-matmul of paper §3.4).
+ * every code once per pair of tokens (once per token for d = 8), which is the
+ * fast path for T = 1 (the fused decode-and-matmul of paper §3.4).
  */
 vq_status vq_gemv(const vq_tensor *w, const uint16_t *x, int32_t T, float *y, void *stream);
 
@@ -141,7 +142,9 @@ vq_status vq_gemm(const vq_tensor *w, const uint16_t *x, int32_t T, float *y, vo
  * kernels for all expert tiers; Experimental MTP note: decode cost is the
  * routed experts' bytes.)
  *   expert_ids: device [T][top_k] int32, 4-byte aligned;
- *   y: device [T][top_k][rows] fp32, 16-byte aligned;  T >= 0, top_k >= 1.
+ *   y: device [T][top_k][rows] fp32, 16-byte aligned;  T >= 0, top_k >= 1,
+ *   T * top_k <= 65535 (larger batches belong to vq_moe_gemm), x at most
+ *   2 GiB - 1 bytes.
  */
 vq_status vq_moe_gemv(const vq_tensor *w, const uint16_t *x, int32_t x_per_slot,
                       const int32_t *expert_ids, int32_t T, int32_t top_k, float *y,

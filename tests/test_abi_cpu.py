@@ -139,3 +139,18 @@ def test_workspace_grows_with_pairs_and_experts(b):
     a = b.workspace_bytes(512, 8, 256)
     assert a < b.workspace_bytes(1024, 8, 256) and a < b.workspace_bytes(512, 8, 512)
     assert a % 4 == 0
+
+
+def test_buffer_size_limits(b):
+    """One expert's codes or scales above 2 GiB - 1 bytes, or an x of that
+    size for a routed call, is refused: the kernels address them with 32-bit
+    offsets."""
+    # 2^20 rows of 4096 columns at d=2, B=8: 2048 code bytes per row = 2 GiB
+    big = _t(b, rows=1 << 20, cols=4096)
+    assert b.STATUS_NAMES[_gemv(b, big)] == "VQ_ERR_SHAPE"
+    assert "exceed" in b.LIB.vq_last_error().decode()
+    ok = _t(b, rows=(1 << 20) - 1, cols=4096)
+    assert b.STATUS_NAMES[b.LIB.vq_gemv(ctypes.byref(ok), 0x40000, 0, 0x50000, None)] == "VQ_OK"
+    t = _t(b, num_experts=4, cols=4096)
+    st = b.LIB.vq_moe_gemv(ctypes.byref(t), 0x40000, 1, 0x70000, 1 << 16, 8, 0x50000, None)
+    assert b.STATUS_NAMES[st] == "VQ_ERR_SHAPE" and "x holds" in b.LIB.vq_last_error().decode()

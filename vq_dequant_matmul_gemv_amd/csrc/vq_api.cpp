@@ -29,6 +29,9 @@ vq_status fail(vq_status s, const char* fmt, ...) {
   return s;
 }
 
+// Largest buffer a kernel addresses with 32-bit offsets (2 GiB - 1).
+constexpr int64_t kMaxBufferBytes = 0x7fffffff;
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 int32_t words_per_row(int32_t cols, int32_t d, int32_t log2_k) {
@@ -72,6 +75,12 @@ vq_status check_tensor(const vq_tensor* w, vqmi::TensorView* v) {
   const int64_t elems = (int64_t)w->num_experts * w->rows * (int64_t)w->cols;
   if (elems > ((int64_t)1 << 40))
     return fail(VQ_ERR_SHAPE, "tensor too large (%lld weights)", (long long)elems);
+  // The kernels address one expert's codes and scales with 32-bit buffer offsets.
+  const int64_t code_bytes = (int64_t)w->rows * words_per_row(w->cols, w->d, w->log2_k) * 4;
+  const int64_t scale_bytes = (int64_t)w->rows * (w->cols / w->group) * 2;
+  if (code_bytes > kMaxBufferBytes || scale_bytes > kMaxBufferBytes)
+    return fail(VQ_ERR_SHAPE, "one expert's codes (%lld bytes) or scales (%lld bytes) exceed %lld bytes",
+                (long long)code_bytes, (long long)scale_bytes, (long long)kMaxBufferBytes);
   if (!aligned(w->codes, 16)) return fail(VQ_ERR_ALIGN, "codes pointer is not 16-byte aligned");
   if (!aligned(w->codebook, 16)) return fail(VQ_ERR_ALIGN, "codebook pointer is not 16-byte aligned");
   if (!aligned(w->scales, 4)) return fail(VQ_ERR_ALIGN, "scales pointer is not 4-byte aligned");
@@ -111,6 +120,10 @@ vq_status check_moe(const vq_tensor* w, const void* x, int32_t x_per_slot, const
   if (x_per_slot != 0 && x_per_slot != 1)
     return fail(VQ_ERR_SHAPE, "x_per_slot=%d must be 0 or 1", x_per_slot);
   if ((int64_t)T * top_k > (1 << 30)) return fail(VQ_ERR_SHAPE, "T*top_k too large");
+  const int64_t x_bytes = (int64_t)T * (x_per_slot ? top_k : 1) * w->cols * 2;
+  if (x_bytes > kMaxBufferBytes)
+    return fail(VQ_ERR_SHAPE, "x holds %lld bytes; at most %lld per call", (long long)x_bytes,
+                (long long)kMaxBufferBytes);
   if (T == 0) return VQ_OK;
   st = check_xy(x, y, "y");
   if (st != VQ_OK) return st;
