@@ -55,6 +55,8 @@ COPY_PROBE_ELEMS = 1 << 28          # fp16 -> fp32 copy: reads 512 MiB, writes 1
 COPY_READ_BYTES = 2 * COPY_PROBE_ELEMS
 COPY_WRITE_BYTES = 4 * COPY_PROBE_ELEMS
 PROFILES = os.path.join(ROOT, "profiles")
+GATE_TAG = "dense_mlp_gate_17408x5120"           # profiles/pmc_*_<tag>.txt of the gate kernels
+COPY_TAG = "torch_copy_2p28_fp16_to_fp32"        # profiles/pmc_*_<tag>.txt of the copy probe
 
 
 def copy_probe():
@@ -97,8 +99,8 @@ def measured_traffic(kernel_prefix, tag):
     from vq_dequant_matmul_gemv_amd.profsum import source_digest
     f, fd = _pmc_value(f"pmc_fetch_size_{tag}.txt", "FETCH_SIZE", kernel_prefix)
     w, wd = _pmc_value(f"pmc_write_size_{tag}.txt", "WRITE_SIZE", kernel_prefix)
-    cf, _ = _pmc_value("pmc_fetch_size_copy.txt", "FETCH_SIZE", "torch copy")
-    cw, _ = _pmc_value("pmc_write_size_copy.txt", "WRITE_SIZE", "torch copy")
+    cf, _ = _pmc_value(f"pmc_fetch_size_{COPY_TAG}.txt", "FETCH_SIZE", "torch copy")
+    cw, _ = _pmc_value(f"pmc_write_size_{COPY_TAG}.txt", "WRITE_SIZE", "torch copy")
     if None in (f, w, cf, cw) or fd != source_digest() or wd != source_digest():
         return None
     fetch_scale = (COPY_READ_BYTES / 1024) / cf     # true KiB per counted KiB
@@ -292,12 +294,12 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "vq_gemv (gate, T=1)",
                      "achieved": round(achieved_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic("vq_gemv_kernel<2, 8, 64", "gate"),
+                     "traffic": measured_traffic("vq_gemv_kernel<2, 8, 64", GATE_TAG),
                      "algorithmic_bytes": dec_bytes["gate"]},
         "roofline_prefill": {"bound": "mfma", "kernel": "vq_gemm (gate, T=2048)",
                              "achieved": round(achieved_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                              "unit": "TFLOP/s", "frac": round(achieved_tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                             "traffic": measured_traffic("vq_gemm_kernel<2, 8, 64", "gate"),
+                             "traffic": measured_traffic("vq_gemm_kernel<2, 8, 64", GATE_TAG),
                              "algorithmic_bytes": tensor_bytes(specs["gate"], PREFILL_T)},
     }
     if not args.no_cpu:

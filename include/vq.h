@@ -11,7 +11,7 @@
  *     card "Qwen3.5-397B-A17B-VQ-2.4bpw", Methodology (per-tensor fp16
  *     codebook); paper §2.2 (codebook fit on max-abs-scaled subvectors).
  *   - scales: one fp16 scale per (row, group of g weights), g = 64 or 128.
- *     Same card, Methodology ("fp16 scale per (row, 64 weights)"); model card
+ *     Same card, Methodology (an fp16 scale for each row and 64-weight group); model card
  *     "aquaman164/Qwen3.6-35B-A3B-MLX-VQ-2.4bpw", Recipe (+0.125 bpw: g = 128).
  * and dequantized on the fly:
  *   W[r][c] = fp16( codebook[code(r, c/d)][c % d] * scale[r][c/g] )  (one RNE
@@ -22,8 +22,9 @@
  * once per group), which differs from rounding W to fp16 first only by that
  * rounding; vq_dequant and the MFMA GEMM use the rounded W exactly.
  *
- * Code layout ("row-local, 32-code blocks", packed to the true bit width in
- * uint32 words: 397B card, Methodology; paper §2.3 Packing).  Row r of expert
+ * Code layout (codes packed to their true bit width into uint32 words, each
+ * row on its own in blocks of 32 codes: 397B card, Methodology; paper §2.3
+ * Packing).  Row r of expert
  * e starts at word (e*rows + r) * Wr, Wr = ceil(cols/d/32) * B.  Code j of a
  * row occupies bits [j*B, (j+1)*B) of the row's little-endian bit stream
  * (least significant bit first); 12-bit codes straddle words.  For B = 8 an
@@ -70,8 +71,8 @@ typedef enum {
 
 /*
  * One VQ tensor (dense: num_experts = 1; stacked MoE experts: num_experts = E,
- * one tensor per (layer, projection) holding all experts -- paper, Appendix A
- * "expert modules").
+ * one tensor per (layer, projection) holding all experts -- paper, Appendix A,
+ * on expert modules).
  *
  * Supported geometry: d in {2, 4, 8}, log2_k in {8, 12}, group in {64, 128}.
  * Shape rules (else VQ_ERR_SHAPE): rows >= 1; cols >= 1; cols % group == 0;

@@ -30,7 +30,8 @@ size K, B = log2 K bits per code; W is [rows = out][cols = in]):
 1. unpack: code j of row r is bits [j*B, (j+1)*B) of that row's code stream,
    read as a little-endian bit string (least significant bit first).  A row's
    stream is ceil(cols/d/32) blocks of 32 codes, each block exactly B uint32
-   words, so rows start on a word boundary ("row-local, 32-code blocks").
+   words, so rows start on a word boundary (each row packed on its own in
+   blocks of 32 codes).
 2. dequant: W[r][j*d + t] = f16( f32(codebook[code][t]) * f32(scale[r][c // g]) )
    with c = j*d + t.  The fp32 product of two fp16 values is exact, so this
    is one round-to-nearest-even to fp16, the same as an IEEE fp16 multiply.
