@@ -11,7 +11,8 @@
 // accumulation in v_mfma_f32_32x32x16_f16.
 //
 // Design for gfx950:
-//  * A = dequantized W (32 rows x 16 k per MFMA), B = x (16 k x 32 tokens).
+//  * Per MFMA: x (32 tokens x 16 k) times dequantized W^T (16 k x 32 rows),
+//    so each half-wave's results are 32 consecutive elements of a y row.
 //    A block's waves sit side by side along W rows; a wave owns MB m-blocks
 //    of 32 rows and all 32*NB tokens of the tile, so every weight is
 //    dequantized exactly once per token tile, straight into the A-operand
@@ -111,12 +112,28 @@ struct GemmArgs {
   int top_k, x_per_slot;
   int x_rows;             // routed: rows of x (T or T*top_k)
   int n_row_tiles, n_tok_tiles;
-  int ksplit;             // dense: K slices (grid.y); results added atomically when > 1
+  // dense grid: blocks [0, n_full) each own a whole tile; the blocks after them
+  // each own one of rem_split K slices of a remaining tile and add into y
+  // (zeroed beforehand) atomically.
+  int n_full, rem_split;
 };
+
+// Tile t -> (row tile, token tile): groups of 4 row tiles x all token tiles,
+// so neighbouring tile indices share x and W slices.
+__host__ __device__ __forceinline__ void gemm_tile_coords(int tile, int n_row_tiles, int n_tok_tiles, int& rt,
+                                                          int& tt) {
+  const int GR = 4;
+  const int grp = tile / (GR * n_tok_tiles);
+  const int in = tile - grp * GR * n_tok_tiles;
+  const int rows_in_grp = min(GR, n_row_tiles - grp * GR);
+  rt = grp * GR + in % rows_in_grp;
+  tt = in / rows_in_grp;
+}
 
 // 32x32x16 fp16 MFMA, fp32 accumulation.  Operand lanes: lane l supplies row
 // (A) / column (B) l % 32 and the 8 k-values of half h = l / 32; result lane
-// l holds column l % 32, rows 8*(i/4) + 4*h + (i%4), i = 0..15.
+// l holds column l % 32, rows 8*(i/4) + 4*h + (i%4), i = 0..15.  Here A is an
+// x fragment (32 tokens) and B a dequantized W fragment (32 rows).
 __device__ __forceinline__ float16_t mfma32(half8_t a, half8_t b, float16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
@@ -133,7 +150,7 @@ struct GemmShape {
   static constexpr int kTokens = 32 * NB;         // tokens per block tile
 };
 
-template <int D, int B, int G, class SH, bool MOE, bool ATOMIC>
+template <int D, int B, int G, class SH, bool MOE>
 __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
   using L = CodebookLayout<D, B>;
   constexpr int CG = (D == 8) ? 64 : 32;  // columns per lane half per super-step
@@ -164,6 +181,7 @@ __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
   // ---- which tile ----
   int rt, expert = 0, first = 0, count;
   int tok_base = 0;
+  int kslice = 0, nslices = 1;  // this block's share of the tile's K range
   if constexpr (MOE) {
     const int tix = blockIdx.x;
     if (tix >= *a.n_tiles) return;
@@ -172,19 +190,23 @@ __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
     count = a.tiles[3 * tix + 2];
     rt = blockIdx.y;
   } else {
-    // XCD-aware order: blocks land on XCD (bid % 8) round-robin; give each XCD
-    // a contiguous range of tiles, grouped 4 row tiles x all token tiles so
-    // concurrently running blocks share x and W slices in that XCD's L2.
-    const int N = a.n_row_tiles * a.n_tok_tiles;
     const int bid = blockIdx.x;
-    const int q = N / 8, r8 = N % 8, xcd = bid % 8, j = bid / 8;
-    const int tile = xcd * q + min(xcd, r8) + j;
-    const int GR = 4;
-    const int grp = tile / (GR * a.n_tok_tiles);
-    const int in = tile - grp * GR * a.n_tok_tiles;
-    const int rows_in_grp = min(GR, a.n_row_tiles - grp * GR);
-    rt = grp * GR + in % rows_in_grp;
-    const int tt = in / rows_in_grp;
+    int tile;
+    if (bid < a.n_full) {
+      // XCD-aware order: blocks land on XCD (bid % 8) round-robin; give each
+      // XCD a contiguous range of tiles so concurrently running blocks share
+      // x and W slices in that XCD's L2.
+      const int N = a.n_full;
+      const int q = N / 8, r8 = N % 8, xcd = bid % 8, j = bid / 8;
+      tile = xcd * q + min(xcd, r8) + j;
+    } else {
+      const int u = bid - a.n_full;
+      tile = a.n_full + u / a.rem_split;
+      kslice = u % a.rem_split;
+      nslices = a.rem_split;
+    }
+    int tt;
+    gemm_tile_coords(tile, a.n_row_tiles, a.n_tok_tiles, rt, tt);
     tok_base = tt * WN;
     count = min(WN, a.T - tok_base);
   }
@@ -197,8 +219,8 @@ __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
   const int nks_all = (a.cols + SS - 1) / SS;
   int ks_begin = 0, ks_end = nks_all;
   if constexpr (!MOE) {
-    ks_begin = (int)((int64_t)nks_all * blockIdx.y / a.ksplit);
-    ks_end = (int)((int64_t)nks_all * (blockIdx.y + 1) / a.ksplit);
+    ks_begin = (int)((int64_t)nks_all * kslice / nslices);
+    ks_end = (int)((int64_t)nks_all * (kslice + 1) / nslices);
   }
 
   // All streaming loads are branch-free buffer loads with 32-bit offsets:
@@ -309,7 +331,7 @@ __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
           for (int j = 0; j < D / 2; ++j) w[c * (D / 2) + j] = e[s & 1][mb][c].v[j] * s2[mb];
         const half8_t af = half8_t{w[0].x, w[0].y, w[1].x, w[1].y, w[2].x, w[2].y, w[3].x, w[3].y};
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(af, bf[nb], acc[mb][nb]);
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(bf[nb], af, acc[mb][nb]);
       }
     }
   };
@@ -344,43 +366,55 @@ __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds rows 8*(i/4) + 4*h + (i%4) of each m-block for token l32 ----
-  const bool vec_ok = (a.rows & 3) == 0;
+  // ---- epilogue: x is the MFMA's A operand and W its B operand, so lane
+  // (l32, h) holds W row row_base + 32*mb + l32 for tokens 32*nb + 8*(i/4) +
+  // 4*h + (i%4): for each i a half-wave covers 32 consecutive y elements of
+  // one token (128 contiguous bytes), for stores and atomics alike.
+  const int row = row_base + l32;  // + 32 * mb
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int tok = nb * 32 + l32;
-    if (tok >= count) continue;
-    int yr;
-    if constexpr (MOE) yr = a.pairs[first + tok];
-    else yr = tok_base + tok;
-    float* yrow = a.y + (int64_t)yr * a.rows;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
+    for (int i = 0; i < 16; ++i) {
+      const int tok = nb * 32 + 8 * (i / 4) + 4 * h + (i % 4);
+      if (tok >= count) continue;
+      int yr;
+      if constexpr (MOE) yr = a.pairs[first + tok];
+      else yr = tok_base + tok;
+      float* yrow = a.y + (int64_t)yr * a.rows;
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int r = row_base + mb * 32 + 8 * i4 + 4 * h;
-        const float4_t v = float4_t{acc[mb][nb][4 * i4], acc[mb][nb][4 * i4 + 1],
-                                    acc[mb][nb][4 * i4 + 2], acc[mb][nb][4 * i4 + 3]};
-        if constexpr (ATOMIC) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            if (r + c < a.rows) atomicAdd(yrow + r + c, v[c]);
-        } else if (vec_ok && r + 3 < a.rows) {
-          *reinterpret_cast<float4_t*>(yrow + r) = v;
-        } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            if (r + c < a.rows) yrow[r + c] = v[c];
+      for (int mb = 0; mb < MB; ++mb) {
+        const int r = row + 32 * mb;
+        if (r < a.rows) {
+          if (nslices > 1) atomicAdd(yrow + r, acc[mb][nb][i]);  // block-uniform branch
+          else yrow[r] = acc[mb][nb][i];
         }
       }
     }
   }
 }
 
-// Zero fill (a kernel rather than hipMemsetAsync, so it can sit in a graph).
-__global__ void vq_zero_kernel(float* y, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    y[i] = 0.f;
+// Zero the y region of tiles [first, first + gridDim.x), gridDim.y blocks per
+// tile, 16-byte stores where the rows allow (a kernel rather than
+// hipMemsetAsync, so it can sit in a graph).
+__global__ __launch_bounds__(256) void vq_zero_tiles_kernel(float* y, int rows, int T, int first, int n_row_tiles,
+                                                            int n_tok_tiles, int tile_rows, int tile_tokens) {
+  int rt, tt;
+  gemm_tile_coords(first + (int)blockIdx.x, n_row_tiles, n_tok_tiles, rt, tt);
+  const int r0 = rt * tile_rows, nr = min(tile_rows, rows - r0);
+  const int t0 = tt * tile_tokens, nt = min(tile_tokens, T - t0);
+  const bool vec = (rows & 3) == 0;  // r0 is a multiple of tile_rows (of 32)
+  const int per_row = vec ? (nr + 3) / 4 : nr;
+  for (int i = blockIdx.y * blockDim.x + threadIdx.x; i < nt * per_row; i += gridDim.y * blockDim.x) {
+    const int t = i / per_row, k = i - t * per_row;
+    float* yr = y + (int64_t)(t0 + t) * rows + r0;
+    if (vec && 4 * k + 3 < nr) {
+      *reinterpret_cast<float4_t*>(yr + 4 * k) = float4_t{0.f, 0.f, 0.f, 0.f};
+    } else if (vec) {
+      for (int c = 4 * k; c < nr; ++c) yr[c] = 0.f;
+    } else {
+      yr[k] = 0.f;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -483,9 +517,9 @@ constexpr int kMoeTileTokens = GemmMoe::kTokens;
 
 int max_tiles_for(int npairs, int E) { return (npairs + kMoeTileTokens - 1) / kMoeTileTokens + E; }
 
-template <int D, int B, int G, class SH, bool MOE, bool ATOMIC>
+template <int D, int B, int G, class SH, bool MOE>
 hipError_t gemm_launch(const GemmArgs& a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((vq_gemm_kernel<D, B, G, SH, MOE, ATOMIC>), grid, dim3(SH::kThreads), 0, s, a);
+  hipLaunchKernelGGL((vq_gemm_kernel<D, B, G, SH, MOE>), grid, dim3(SH::kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -514,7 +548,8 @@ GemmArgs base_args(const TensorView& w, const uint16_t* x, float* y, int G, int 
   a.cols = w.cols;
   a.wr = w.wr;
   a.spr = w.cols / G;
-  a.ksplit = 1;
+  a.n_full = 0;
+  a.rem_split = 1;
   return a;
 }
 
@@ -524,21 +559,37 @@ hipError_t gemm_dense(GemmArgs a, hipStream_t s) {
   a.n_tok_tiles = (a.T + SH::kTokens - 1) / SH::kTokens;
   const int tiles = a.n_row_tiles * a.n_tok_tiles;
   const int nks = (a.cols + (D == 8 ? 128 : 64) - 1) / (D == 8 ? 128 : 64);
-  // Too few tiles to fill the chip: split K and add the slices atomically
-  // into a zeroed y (fp32 addition order then varies between runs).
-  int ksplit = 1;
-  if (tiles < num_cus()) ksplit = std::min(std::max(1, num_cus() / tiles), std::max(1, nks / 8));
-  a.ksplit = ksplit;
-  dim3 grid(tiles, ksplit);
-  if (ksplit > 1) {
-    const int64_t n = (int64_t)a.T * a.rows;
-    hipLaunchKernelGGL(vq_zero_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256), 0, s,
-                       a.y, n);
+  const int cus = num_cus();
+  // Whole rounds of tiles run as whole tiles; the tiles of a last, partial
+  // round are split along K over the CUs and added atomically into a zeroed
+  // y (their fp32 addition order then varies between runs).
+  // The split minimises the partial round's time in tile rounds,
+  // ceil(rem * split / cus) / split, plus a small charge per extra slice for
+  // the atomic traffic; each slice keeps at least 8 super-steps.
+  int full = (tiles / cus) * cus, rem = tiles - full, split = 1;
+  if (rem > 0) {
+    double best = 1e30;
+    for (int sp = 1; sp <= std::min(16, std::max(1, nks / 8)); ++sp) {
+      const double c = (double)((rem * sp + cus - 1) / cus) / sp + 0.03 * (sp - 1);
+      if (c < best - 1e-9) {
+        best = c;
+        split = sp;
+      }
+    }
+  }
+  if (split == 1) {
+    full = tiles;
+    rem = 0;
+  }
+  a.n_full = full;
+  a.rem_split = split;
+  if (rem > 0) {
+    hipLaunchKernelGGL(vq_zero_tiles_kernel, dim3(rem, std::max(1, 2 * cus / rem)), dim3(256), 0, s, a.y, a.rows,
+                       a.T, full, a.n_row_tiles, a.n_tok_tiles, SH::kRows, SH::kTokens);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return gemm_launch<D, B, G, SH, false, true>(a, grid, s);
   }
-  return gemm_launch<D, B, G, SH, false, false>(a, grid, s);
+  return gemm_launch<D, B, G, SH, false>(a, dim3((unsigned)(full + rem * split)), s);
 }
 
 template <int D, int B, int G>
@@ -581,7 +632,7 @@ hipError_t moe_gemm_geom(const TensorView& w, const uint16_t* x, int x_per_slot,
   a.x_rows = x_per_slot ? npairs : T;
   a.n_row_tiles = (a.rows + GemmMoe::kRows - 1) / GemmMoe::kRows;
   dim3 grid(mt, a.n_row_tiles);
-  return gemm_launch<D, B, G, GemmMoe, true, false>(a, grid, s);
+  return gemm_launch<D, B, G, GemmMoe, true>(a, grid, s);
 }
 
 }  // namespace

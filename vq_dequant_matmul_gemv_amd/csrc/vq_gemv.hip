@@ -199,13 +199,15 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
   const rsrc_t rc = make_rsrc(codes, (uint64_t)a.rows * a.wr * 4);
   const uint32_t row_cb = (uint32_t)a.wr * 4u;
   const int LC = L * C;                                 // chunks per pass
-  // items f = pass * ngroups + group, dealt round-robin over the waves
+  // items f = group * passes + pass, dealt round-robin over the waves: when
+  // the wave count is a multiple of the pass count a wave keeps one pass (no
+  // x reloads), and the block's waves always read neighbouring row groups.
   const int total_items = ngroups * a.passes;
+  const int step_g = NW / a.passes, step_p = NW - step_g * a.passes;  // f += NW
   const int n_items = total_items > wave ? (total_items - wave + NW - 1) / NW : 0;
   Chunk<B> ring[C];                                     // codes of the item in flight
   int l_item = 0;                                       // next item to load
-  int l_pass = 0, l_g = wave;                           // its pass and group
-  while (l_g >= ngroups && ngroups > 0) { l_g -= ngroups; ++l_pass; }
+  int l_pass = wave % a.passes, l_g = wave / a.passes;  // its pass and group
   uint32_t lane_vo[C];                                  // per-lane code offsets of l_pass
   auto set_pass_offsets = [&](int pass) {
 #pragma unroll
@@ -239,11 +241,10 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
       }
     }
     ++l_item;
-    l_g += NW;
-    if (l_g >= ngroups) {
-      while (l_g >= ngroups) { l_g -= ngroups; ++l_pass; }
-      set_pass_offsets(l_pass);
-    }
+    l_g += step_g;
+    l_pass += step_p;
+    if (l_pass >= a.passes) { l_pass -= a.passes; ++l_g; }
+    if (step_p != 0) set_pass_offsets(l_pass);
   };
   load_item();
 
@@ -279,8 +280,7 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
   const bool direct = a.passes == 1 && !a.accumulate;
   half2_t xv[TT][C][HX];
   int cur_pass = -1;
-  int pass = 0, g = wave;
-  while (g >= ngroups && ngroups > 0) { g -= ngroups; ++pass; }
+  int pass = wave % a.passes, g = wave / a.passes;
   for (int u = 0; u < n_items; ++u) {
     if (pass != cur_pass) {  // x of this pass into VGPRs (zeros past the slice)
       cur_pass = pass;
@@ -360,8 +360,9 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
     // the compute (a second buffer) is slower, as the loads then wait in the
     // CU's memory queue behind other waves' while this wave could compute.
     load_item();
-    g += NW;
-    while (g >= ngroups) { g -= ngroups; ++pass; }
+    g += step_g;
+    pass += step_p;
+    if (pass >= a.passes) { pass -= a.passes; ++g; }
   }
 
   if (!direct) {  // add each row's pass pieces in pass order (deterministic)
