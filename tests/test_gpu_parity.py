@@ -103,12 +103,16 @@ def test_dense_exact_inputs_bit_identical(fn, d, b, g):
 @pytest.mark.parametrize("fn", ["gemv", "gemm"])
 def test_dense_shapes_and_tokens(fn):
     """Ragged tokens around the tile sizes, tiny and tall shapes, a column
-    count with a half super-step (d=2, cols % 128 == 64) and a row count that
-    is not a multiple of 4."""
+    count with a half super-step (d=2, cols % 128 == 64), a row count that
+    is not a multiple of 4, and K split over slices of a few tiles."""
     from vq_dequant_matmul_gemv_amd import binding
     cases = [(1, 64, 2, 8, 64, [1, 2]), (3, 192, 2, 8, 64, [1, 7, 16, 17]),
              (513, 320, 2, 8, 64, [1, 4, 129]), (257, 128, 4, 8, 64, [5, 64, 65]),
-             (64, 512, 8, 12, 128, [1, 63, 64, 65]), (1030, 256, 4, 8, 128, [1, 130])]
+             (64, 512, 8, 12, 128, [1, 63, 64, 65]), (1030, 256, 4, 8, 128, [1, 130]),
+             # several 8-group scale windows, K split into slices that start
+             # inside a window; 20 groups per row (windows not 16-byte aligned)
+             # and 40 (aligned)
+             (700, 1280, 2, 8, 64, [300]), (300, 2560, 4, 8, 64, [200])]
     for rows, cols, d, b, g, Ts in cases:
         spec, arrs, w = _case(d, b, g, rows, cols, ("shapes", rows, cols))
         for T in Ts:

@@ -15,10 +15,12 @@
 //    so each half-wave's results are 32 consecutive elements of a y row.
 //    A block's waves sit side by side along W rows; a wave owns MB m-blocks
 //    of 32 rows and all 32*NB tokens of the tile, so every weight is
-//    dequantized exactly once per token tile, straight into the A-operand
+//    dequantized exactly once per token tile, straight into the B-operand
 //    registers (no LDS round trip for W).  Large token counts use 8 waves
 //    (two per SIMD) of 64 rows x 128 tokens; small ones 4 waves of 128 rows
 //    x 32 tokens.
+//  * Scales are fetched in 16-byte windows of 8 groups per row, once per 8
+//    groups, not 2 bytes per row per super-step.
 //  * The contraction order over k is free, so each lane half (lanes 32h ..
 //    32h+31) takes a contiguous run of CG columns per "super-step" (CG = 32,
 //    or 64 for d = 8): a lane's codes for one super-step are one small
@@ -150,6 +152,14 @@ struct GemmShape {
   static constexpr int kTokens = 32 * NB;         // tokens per block tile
 };
 
+// 16-bit element `pos` (0..7) of a 16-byte window.
+__device__ __forceinline__ uint32_t pick16(u32x4 v, int pos) {
+  const uint32_t lo = (pos & 2) ? v.y : v.x;
+  const uint32_t hi = (pos & 2) ? v.w : v.z;
+  const uint32_t d = (pos & 4) ? hi : lo;
+  return (pos & 1) ? d >> 16 : d & 0xffffu;
+}
+
 template <int D, int B, int G, class SH, bool MOE>
 __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
   using L = CodebookLayout<D, B>;
@@ -274,15 +284,47 @@ __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
     for (int i = 0; i < XLD; ++i)
       if (xdst[i] >= 0) *reinterpret_cast<u32x4*>(xbuf + buf * (WN * XROW) + xdst[i]) = xr[i];
   };
+  // Scales come in 16-byte windows of 8 groups per row (one load per lane
+  // per 8 groups instead of one per super-step; a row's scales are used a
+  // few bytes per super-step, so per-step loads would fetch a cache line per
+  // row for 2 bytes).  The window of the next group range is fetched one
+  // super-step before it is needed.  Rows whose scale runs are not 16-byte
+  // aligned fill the window with 2-byte loads.  Every group of a super-step
+  // lies in one window for both lane halves (8 groups span >= 512 columns).
+  const bool sw_aligned = (a.spr & 7) == 0;
+  u32x4 swc[MB], swp[MB];
+  auto load_window = [&](int w, u32x4 (&dst)[MB]) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const uint32_t off = soff[mb] + (uint32_t)w * 16u;
+      if (sw_aligned) {
+        dst[mb] = buf_load_b128(rs, off);
+      } else {
+        uint32_t v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          v[q] = (uint32_t)buf_load_b16(rs, off + 4u * q) | ((uint32_t)buf_load_b16(rs, off + 4u * q + 2u) << 16);
+        dst[mb] = u32x4{v[0], v[1], v[2], v[3]};
+      }
+    }
+  };
+  auto window_of = [&](int ks) { return (ks * SS / G) >> 3; };
   auto load_codes = [&](int ks, LaneCodes<NCL, B> (&cc)[MB], uint16_t (&sc)[MB]) {
     const bool ok = ks < ks_end;
     const uint32_t wb = (uint32_t)(ks * CW_SS + h * NCLW) * 4u;
-    const uint32_t sb = (uint32_t)((ks * SS + h * CG) / G) * 2u;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      load_lane_codes<NCL, B>(cc[mb], rc, ok ? coff[mb] + wb : kOutOfRange);
-      sc[mb] = buf_load_b16(rs, ok ? soff[mb] + sb : kOutOfRange);
+    for (int mb = 0; mb < MB; ++mb) load_lane_codes<NCL, B>(cc[mb], rc, ok ? coff[mb] + wb : kOutOfRange);
+    const int w = window_of(ks);
+    if (ks == ks_begin) {
+      load_window(w, swc);
+    } else if (w != window_of(ks - 1)) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) swc[mb] = swp[mb];
     }
+    if (window_of(ks + 1) != w) load_window(w + 1, swp);
+    const int pos = ((ks * SS + h * CG) / G) & 7;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) sc[mb] = (uint16_t)pick16(swc[mb], pos);
   };
 
   const uint32_t lane_off = lane_copy_offset<D, B>(lane);
