@@ -25,10 +25,12 @@
 //  * x sits in VGPRs for a whole pass (x-stationary); the inner loop per code
 //    is one v_perm_b32 (LDS offset), one LDS gather and d/2 v_dot2_f32_f16 per
 //    token; the group scale multiplies each group sum once.
-//  * Each wave has one row group's loads in flight at a time and issues the
-//    next group's loads right after computing the current one; deeper
-//    prefetch only holds the wave at the issue of loads that cannot enter the
-//    CU's full memory queue.
+//  * Each wave keeps P row groups' loads in flight (P items of C chunks per
+//    lane, about six chunks in all) and issues a slot's next loads right after
+//    computing it: wide items (d = 2, five chunks per lane) keep one in
+//    flight, since deeper prefetch there only holds the wave at the issue of
+//    loads that cannot enter the CU's full memory queue; narrow ones (d = 4
+//    and 8) keep up to four.
 //  * Routed experts (top-k MoE): blockIdx.y is the (token, slot) pair; the
 //    block reads its expert id and points at that expert's codes and scales.
 //    An id outside [0, E) writes a zero row.
@@ -76,6 +78,11 @@ __host__ __device__ constexpr int gemv_max_c(int D, int TT) {
   return D == 2 ? (TT == 1 ? 5 : 2) : (D == 4 ? (TT == 1 ? 2 : 1) : 1);
 }
 
+// Items a wave keeps in flight: about six 16-code chunks per lane in all, so
+// narrow items (few chunks per lane) still put enough bytes on the wire per
+// memory round trip.
+__host__ __device__ constexpr int gemv_ring(int C) { return C >= 4 ? 1 : (C == 3 ? 2 : (C == 2 ? 3 : 4)); }
+
 // Sum of v over aligned groups of L = 1 << lg lanes; valid in the group's last lane.
 __device__ __forceinline__ float lane_group_sum(float v, int lg) {
   v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
@@ -101,7 +108,6 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
   static_assert(TT <= gemv_max_tt(D) && C <= gemv_max_c(D, TT), "tile does not fit the VGPR budget");
 
   __shared__ __align__(16) uint8_t cb_lds[LY::kBytes];
-  __shared__ __align__(16) u32x4 raw[LY::kReplicated ? 256 : 1];   // replicated layout: entries before expansion
   constexpr int XBYTES = XS * 8192;
   __shared__ __align__(16) uint8_t x_lds[XBYTES];                   // [TT][nq * 16 * D] fp16
   __shared__ __align__(16) uint8_t s_lds[kGemvScaleBytes];          // the block's scale rows
@@ -162,12 +168,15 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
     const rsrc_t rx = make_rsrc(xb, (uint64_t)ntok * a.cols * 2);
     xg[q] = buf_load_b128(rx, ok ? tt * (uint32_t)a.cols * 2u + (uint32_t)a.q0 * 32u * D + co : kOutOfRange);
   }
+  // codebook (replicated layout): lane l < 32 of wave w holds entry 32 w + l
   u32x4 ce = u32x4{0u, 0u, 0u, 0u};
   if constexpr (LY::kReplicated) {
-    if (tid < 256) {
-      if constexpr (D == 2) ce.x = reinterpret_cast<const uint32_t*>(cb)[tid];
-      else if constexpr (D == 4) { const u32x2 t = reinterpret_cast<const u32x2*>(cb)[tid]; ce.x = t.x; ce.y = t.y; }
-      else ce = reinterpret_cast<const u32x4*>(cb)[tid];
+    static_assert(NW * 32 == 256, "one codebook entry per lane of the first half-waves");
+    if (lane < 32) {
+      const int ent = wave * 32 + lane;
+      if constexpr (D == 2) ce.x = reinterpret_cast<const uint32_t*>(cb)[ent];
+      else if constexpr (D == 4) { const u32x2 t = reinterpret_cast<const u32x2*>(cb)[ent]; ce.x = t.x; ce.y = t.y; }
+      else ce = reinterpret_cast<const u32x4*>(cb)[ent];
     }
   }
   // scale rows [brow0, brow0 + brows), read as 16-byte pieces from a 16-byte
@@ -205,7 +214,8 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
   const int total_items = ngroups * a.passes;
   const int step_g = NW / a.passes, step_p = NW - step_g * a.passes;  // f += NW
   const int n_items = total_items > wave ? (total_items - wave + NW - 1) / NW : 0;
-  Chunk<B> ring[C];                                     // codes of the item in flight
+  constexpr int P = gemv_ring(C);
+  Chunk<B> ring[P][C];                                  // codes of the items in flight
   int l_item = 0;                                       // next item to load
   int l_pass = wave % a.passes, l_g = wave / a.passes;  // its pass and group
   uint32_t lane_vo[C];                                  // per-lane code offsets of l_pass
@@ -220,7 +230,7 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
   // Loads are unconditional: a chunk past the slice, a row past the block or
   // an item past the wave's list gets an out-of-range offset and reads zeros,
   // so every item issues the same loads and the in-order vmcnt waits stay exact.
-  auto load_item = [&]() {
+  auto load_item = [&](Chunk<B> (&dst)[C]) {
     const bool live = l_item < n_items;
     const int g = l_g;
     const int r = brow0 + g * R;                        // first row of the group
@@ -231,12 +241,12 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
       const uint32_t vo = rowok ? lane_vo[j] : kOutOfRange;
       if constexpr (B == 8) {
         const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, vo, so, 0));
-        ring[j].w[0] = v.x; ring[j].w[1] = v.y; ring[j].w[2] = v.z; ring[j].w[3] = v.w;
+        dst[j].w[0] = v.x; dst[j].w[1] = v.y; dst[j].w[2] = v.z; dst[j].w[3] = v.w;
       } else {
 #pragma unroll
         for (int h = 0; h < 3; ++h) {
           const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rc, vo + 8u * h, so, 0));
-          ring[j].w[2 * h] = v.x; ring[j].w[2 * h + 1] = v.y;
+          dst[j].w[2 * h] = v.x; dst[j].w[2 * h + 1] = v.y;
         }
       }
     }
@@ -246,11 +256,29 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
     if (l_pass >= a.passes) { l_pass -= a.passes; ++l_g; }
     if (step_p != 0) set_pass_offsets(l_pass);
   };
-  load_item();
+#pragma unroll
+  for (int k = 0; k < P; ++k) load_item(ring[k]);
 
   // ---- stage the small data in LDS ----
   if constexpr (LY::kReplicated) {
-    if (tid < 256) raw[tid] = ce;
+    // Wave w fills slots [512 w, 512 w + 512) of the 4096 16-byte slots (slot
+    // q holds copies of entry q / 16): lane l writes slots 512 w + 64 k + l,
+    // copies of entry 32 w + 4 k + l / 16, which lane 4 k + l / 16 of the same
+    // wave holds -- a cross-lane permute, no LDS round trip or extra barrier.
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int src = (4 * k + (lane >> 4)) * 4;
+      u32x4 e;
+      e.x = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)ce.x);
+      e.y = D >= 4 ? (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)ce.y) : 0u;
+      e.z = D == 8 ? (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)ce.z) : 0u;
+      e.w = D == 8 ? (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)ce.w) : 0u;
+      u32x4 v;
+      if constexpr (D == 2) v = u32x4{e.x, e.x, e.x, e.x};
+      else if constexpr (D == 4) v = u32x4{e.x, e.y, e.x, e.y};
+      else v = e;
+      reinterpret_cast<u32x4*>(cb_lds)[wave * 512 + 64 * k + lane] = v;
+    }
   }
 #pragma unroll
   for (int q = 0; q < XL; ++q) {
@@ -264,24 +292,12 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
   }
   if constexpr (!LY::kReplicated) stage_codebook<D, B>(cb_lds, cb, tid, NT);
   lds_barrier();
-  if constexpr (LY::kReplicated) {
-    for (int q = tid; q < 4096; q += NT) {  // slot q holds copies of entry q / 16
-      const u32x4 e = raw[q >> 4];
-      u32x4 v;
-      if constexpr (D == 2) v = u32x4{e.x, e.x, e.x, e.x};
-      else if constexpr (D == 4) v = u32x4{e.x, e.y, e.x, e.y};
-      else v = e;
-      reinterpret_cast<u32x4*>(cb_lds)[q] = v;
-    }
-    lds_barrier();
-  }
 
   const uint32_t lane_off = lane_copy_offset<D, B>(lane);
-  const bool direct = a.passes == 1 && !a.accumulate;
   half2_t xv[TT][C][HX];
   int cur_pass = -1;
   int pass = wave % a.passes, g = wave / a.passes;
-  for (int u = 0; u < n_items; ++u) {
+  auto item = [&](Chunk<B> (&rs)[C]) {
     if (pass != cur_pass) {  // x of this pass into VGPRs (zeros past the slice)
       cur_pass = pass;
 #pragma unroll
@@ -313,7 +329,7 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
     Entry<D> e[2][16];
     auto issue = [&](int j, Entry<D> (&dst)[16]) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dst[i] = gather<D, B>(cb_lds, ring[j], i, lane_off);
+      for (int i = 0; i < 16; ++i) dst[i] = gather<D, B>(cb_lds, rs[j], i, lane_off);
     };
     issue(0, e[0]);
 #pragma unroll
@@ -348,24 +364,28 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
       const float v = lane_group_sum(acc[tt], lg);
-      if (li == L - 1 && rb < brows) {
-        if (direct) {
-          if (tt < ntok) yb[(int64_t)tt * a.rows + brow0 + rb] = v;
-        } else {
-          pieces[(rb * a.passes + pass) * TT + tt] = v;
-        }
-      }
+      if (li == L - 1 && rb < brows) pieces[(rb * a.passes + pass) * TT + tt] = v;
     }
-    // Only now the next item's loads: measured on MI355X, issuing them before
-    // the compute (a second buffer) is slower, as the loads then wait in the
-    // CU's memory queue behind other waves' while this wave could compute.
-    load_item();
+    // Only now this slot's next loads (item u + P): measured on MI355X,
+    // issuing them before the compute is slower, as the loads then wait in
+    // the CU's memory queue behind other waves' while this wave could compute.
+    load_item(rs);
     g += step_g;
     pass += step_p;
     if (pass >= a.passes) { pass -= a.passes; ++g; }
+  };
+  // Slot k of the ring holds items k, k + P, k + 2P, ...: unrolled by P so
+  // every slot is a fixed set of registers.  The wave runs its item count
+  // rounded up to P; the extra items read zeros (their loads are out of
+  // range) and store nothing (their rows lie past the block).  With no
+  // branch and no global store in the loop, every wait for a slot's codes
+  // leaves the other slots' loads in flight.
+  for (int u0 = 0; u0 < n_items; u0 += P) {
+#pragma unroll
+    for (int k = 0; k < P; ++k) item(ring[k]);
   }
 
-  if (!direct) {  // add each row's pass pieces in pass order (deterministic)
+  {  // y: each row's pass pieces added in pass order (deterministic)
     __syncthreads();
     for (int r = tid; r < brows; r += NT) {
 #pragma unroll
@@ -448,31 +468,38 @@ int num_cus() {
 }
 
 // Lane tiling of a slice of nq chunks: L = 1 << lg lanes per row, C chunks
-// per lane, `passes` passes.  Each wave has one row group in flight at a
-// time, so the bytes per group (L * C chunks per row) set how much every
-// memory round trip delivers: take the widest pass (largest L * C) that
-// leaves at most a quarter of the lane-chunk slots idle, then the widest
-// rows.  Idle slots cost issue slots, not bytes.
+// per lane, `passes` passes.  The bytes per row group (L * C chunks per row)
+// set how much every memory round trip of a wave delivers, so the widest
+// pass wins, among tilings that leave at most a quarter of the lane-chunk
+// slots idle (idle slots cost issue slots, not bytes) -- with one exception:
+// when the pass count does not divide the wave count, a wave's items change
+// pass and reload x from LDS each time (8*d VGPRs per chunk), so a tiling
+// whose pass count divides the waves is taken at up to 3/8 idle slots.
 struct LaneTiling {
   int lg, C, passes;
 };
 
-LaneTiling plan_tiling(int nq, int max_c) {
+LaneTiling plan_tiling(int nq, int max_c, int waves) {
   LaneTiling best{2, 1, (nq + 3) / 4};
   int best_lc = 0;
-  long best_slots = -1;
-  for (int C = 1; C <= max_c; ++C)
-    for (int lg = 2; lg <= 5; ++lg) {
-      const int LC = C << lg;
-      const int passes = (nq + LC - 1) / LC;
-      const long slots = (long)passes * LC;
-      if (4 * (slots - nq) > slots) continue;  // over a quarter idle
-      if (LC > best_lc || (LC == best_lc && lg > best.lg)) {
-        best = LaneTiling{lg, C, passes};
-        best_lc = LC;
+  for (int pass_rule = 0; pass_rule < 2 && best_lc == 0; ++pass_rule)
+    for (int C = 1; C <= max_c; ++C)
+      for (int lg = 2; lg <= 5; ++lg) {
+        const int LC = C << lg;
+        const int passes = (nq + LC - 1) / LC;
+        const long slots = (long)passes * LC;
+        if (pass_rule == 0) {  // passes dividing the waves, up to 3/8 idle
+          if (waves % passes != 0 || 8 * (slots - nq) > 3 * slots) continue;
+        } else if (4 * (slots - nq) > slots) {
+          continue;
+        }
+        if (LC > best_lc || (LC == best_lc && lg > best.lg)) {
+          best = LaneTiling{lg, C, passes};
+          best_lc = LC;
+        }
       }
-    }
   if (best_lc == 0) {  // tiny rows: fewest slots
+    long best_slots = -1;
     for (int C = 1; C <= max_c; ++C)
       for (int lg = 2; lg <= 5; ++lg) {
         const int LC = C << lg;
@@ -520,7 +547,7 @@ hipError_t gemv_run(GemvArgs a, int P, int ycount, hipStream_t s) {
     a.q0 = sl * per_slice;
     a.nq = std::min(per_slice, P - a.q0);
     a.accumulate = sl > 0;
-    const LaneTiling t = plan_tiling(a.nq, gemv_max_c(D, TT));
+    const LaneTiling t = plan_tiling(a.nq, gemv_max_c(D, TT), kGemvWaves);
     a.lanes_log2 = t.lg;
     a.passes = t.passes;
     const int64_t by_scales = std::max<int64_t>(1, (kGemvScaleBytes - 16) / (2 * (int64_t)a.spr));
