@@ -83,7 +83,7 @@ def _pmc_value(fname, counter, kernel_prefix):
     digest = None
     with open(path) as fh:
         for line in fh:
-            if line.startswith("library source digest:"):
+            if line.startswith("kernel source digest:"):
                 digest = line.split(":", 1)[1].strip()
             if line.startswith(kernel_prefix):
                 for part in line.split():

@@ -128,7 +128,12 @@ vq_status vq_gemv(const vq_tensor *w, const uint16_t *x, int32_t T, float *y, vo
  * Prefill-shaped product, same arguments and result as vq_gemv: dequantized
  * weight tiles feed fp16 MFMA instructions with fp32 accumulation.  Any T is
  * accepted; it is the fast path for large T (paper §2.5: scoring runs a
- * prefill-shaped path; §3.4 prefill).
+ * prefill-shaped path; §3.4 prefill).  When the output tiles do not fill
+ * whole rounds of the GPU's compute units, the tiles of the last, partial
+ * round are split along the columns and their partial sums added atomically
+ * into y (zeroed first on the same stream): those outputs may differ in the
+ * last bits from run to run (fp32 addition order), within the stated
+ * tolerance; all others are deterministic.
  */
 vq_status vq_gemm(const vq_tensor *w, const uint16_t *x, int32_t T, float *y, void *stream);
 

@@ -11,8 +11,8 @@ profiles/.
       DIR/**/*counter_collection.csv (rocprofv3 --pmc ... --output-format csv).
 
 Only the library's kernels (and, for the copy calibration, the copy kernel)
-are listed.  The source digest printed with each summary lets a reader see
-whether the kernels have changed since the counters were taken.
+are listed.  The kernel source digest printed with each summary lets a reader
+see whether the kernels have changed since the counters were taken.
 """
 
 from __future__ import annotations
@@ -29,10 +29,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def source_digest() -> str:
-    """sha256 over the HIP sources and headers of the library (12 hex chars)."""
+    """sha256 over the kernel sources (csrc/*.hip and csrc/*.h), 12 hex chars.
+    The C-ABI wrapper and the public header are left out: they launch the
+    kernels but do not change what a launch does on the GPU."""
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(HERE, "csrc", "*")) +
-                   glob.glob(os.path.join(HERE, "..", "include", "*.h")))
+    files = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")) +
+                   glob.glob(os.path.join(HERE, "csrc", "*.h")))
     for f in files:
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode())
@@ -117,7 +119,7 @@ def main():
     ap.add_argument("--cmd", required=True, help="the full command that produced DIR")
     ap.add_argument("--copy", action="store_true", help="also list torch's copy kernel")
     a = ap.parse_args()
-    lines = [f"command: {a.cmd}", f"library source digest: {source_digest()}", ""]
+    lines = [f"command: {a.cmd}", f"kernel source digest: {source_digest()}", ""]
     lines += trace(a.dir, a.copy) if a.mode == "trace" else pmc(a.dir, a.copy)
     print("\n".join(lines))
 
