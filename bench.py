@@ -48,6 +48,9 @@ def parse():
                     help="run only a few gate GEMV and GEMM launches (for rocprofv3 --pmc passes)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain device copy of known size (counter calibration)")
+    ap.add_argument("--configs", action="store_true",
+                    help="print a per-workload report (every config, both kernels, median/p10/p90) "
+                         "as markdown instead of the JSON line")
     return ap.parse_args()
 
 
@@ -141,6 +144,148 @@ def cpu_baseline(arrs, spec, rows):
                       f"unpack + fp16 dequant + float64 matmul, {reps} reps, {dt * 1e3:.1f} ms each"}
 
 
+REPORT_CMD = "python3 bench.py --configs"
+
+
+def configs_report():
+    """Every workload of the benchmark set, both kernels, timed as back-to-back
+    calls in one HIP graph rotating over weight replicas (>= 1.1 GB touched
+    per replay where the tensors allow, so calls stream from HBM, not the
+    256 MB Infinity Cache); median, p10 and p90 over 30 replays of the per-call
+    average.  Algorithmic counting: bytes = codes + scales + codebook + x + y
+    (+ ids), routed calls counting only the distinct experts they hit;
+    flops = 2 T rows cols (x top_k when routed).  Context: a plain read and
+    torch's fp16 GEMM on uncompressed weights of the same shapes."""
+    import numpy as np
+    import torch
+    from vq_dequant_matmul_gemv_amd import binding, synth
+
+    dev = torch.device("cuda", 0)
+    from vq_dequant_matmul_gemv_amd.profsum import source_digest
+    out = [f"command: {REPORT_CMD}", f"kernel source digest: {source_digest()}", "",
+           "vq_gemv hands token counts above its measured crossover to the MFMA kernel (the rows with",
+           "larger T under vq_gemv time that kernel); vq_gemm always runs the MFMA kernel.", "",
+           "| workload | tensor | call | T | per call us (median, p10, p90) | GB/s | % of 8 TB/s | TFLOP/s | % of 2.5 PF |",
+           "|---|---|---|---|---|---|---|---|---|"]
+
+    def timed(calls, reps=30):
+        torch.cuda.synchronize()
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in calls:
+                c()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        per = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            per.append(a.elapsed_time(b) * 1e3 / len(calls))
+        del g
+        return np.percentile(per, [50, 10, 90])
+
+    def row(wl, name, call, T, us, nbytes, flops):
+        med = us[0]
+        gbs = nbytes / med / 1e3
+        tf = flops / med / 1e6
+        out.append(f"| {wl} | {name} | {call} | {T} | {us[0]:.2f} ({us[1]:.2f}, {us[2]:.2f}) | {gbs:.0f} | "
+                   f"{100 * gbs / HBM_PEAK_GBPS:.1f} | {tf:.1f} | {100 * tf / MFMA_F16_PEAK_TFLOPS:.1f} |")
+        print(out[-1], file=sys.stderr, flush=True)
+
+    def replicas(spec, host, nbytes, cap=2048):
+        base = binding.VQTensor.from_host(host, spec, device=dev)
+        n = int(min(cap, max(1, -(-1.1e9 // nbytes))))
+        reps = [base]
+        for _ in range(n - 1):
+            reps.append(binding.VQTensor(base.codes.clone(), base.codebook.clone(), base.scales.clone(),
+                                         spec.rows, spec.cols, spec.d, spec.log2_k, spec.group,
+                                         spec.experts))
+        return reps
+
+    def dense(wl, name, spec, gemv_T, gemm_T, key):
+        host = synth.tensor(spec, *key)
+        reps = replicas(spec, host, tensor_bytes(spec, 1))
+        for fn, Ts in (("gemv", gemv_T), ("gemm", gemm_T)):
+            for T in Ts:
+                x = torch.from_numpy(synth.activations((T, spec.cols), *key, "x", T)).to(dev)
+                y = torch.empty((T, spec.rows), dtype=torch.float32, device=dev)
+                n = max(16, len(reps)) if T * spec.rows * 4 < 64e6 else max(4, min(len(reps), 8))
+                calls = [(lambda w=reps[i % len(reps)]: getattr(binding, fn)(w, x, y)) for i in range(n)]
+                us = timed(calls)
+                row(wl, name, "vq_" + fn, T, us, tensor_bytes(spec, T), 2.0 * T * spec.rows * spec.cols)
+        del reps
+        torch.cuda.empty_cache()
+
+    def routed(wl, name, spec, top_k, Ts, x_per_slot, key):
+        host = synth.tensor(spec, *key)
+        per_expert = spec.rows * spec.words * 4 + spec.rows * (spec.cols // spec.group) * 2
+        reps = replicas(spec, host, per_expert * spec.experts, cap=8)
+        for fn, T in zip(("moe_gemv", "moe_gemm"), Ts):
+            draws = [synth.zipf_routing(T, spec.experts, top_k, *key, "ids", T, r) for r in range(16)]
+            ids = [torch.from_numpy(d.astype(np.int32)).to(dev) for d in draws]
+            shape = (T, top_k, spec.cols) if x_per_slot else (T, spec.cols)
+            x = torch.from_numpy(synth.activations(shape, *key, "x", T)).to(dev)
+            y = torch.empty((T, top_k, spec.rows), dtype=torch.float32, device=dev)
+            ws = torch.empty(max(16, binding.workspace_bytes(T, top_k, spec.experts)), dtype=torch.uint8, device=dev)
+            calls, nbytes = [], 0
+            for i in range(16):
+                w = reps[i % len(reps)]
+                if fn == "moe_gemv":
+                    calls.append(lambda w=w, d=ids[i]: binding.moe_gemv(w, x, d, x_per_slot=x_per_slot, y=y))
+                else:
+                    calls.append(lambda w=w, d=ids[i]: binding.moe_gemm(w, x, d, x_per_slot=x_per_slot, y=y,
+                                                                        workspace=ws))
+                hit = len(np.unique(draws[i]))
+                nbytes += (hit * per_expert + spec.k * spec.d * 2 + x.numel() * 2 + y.numel() * 4
+                           + T * top_k * 4)
+            us = timed(calls)
+            row(wl, name, "vq_" + fn, T, us, nbytes / 16, 2.0 * T * top_k * spec.rows * spec.cols)
+        del reps
+        torch.cuda.empty_cache()
+
+    W = synth.WORKLOADS
+    dense("gemv_1024", "w", W["gemv_1024"]["tensors"]["w"], [1], [], ("gemv_1024", "w"))
+    wl = "dense_mlp_5120x17408_d2k256"
+    for n in ("gate", "up", "down"):
+        dense(wl, n, W[wl]["tensors"][n], [1], [2048], (wl, n))
+    wl = "moe_e256_4096x1024_d4k256"
+    for n in ("gate", "down"):
+        routed(wl, n, W[wl]["tensors"][n], W[wl]["top_k"], (1, 1024), n == "down", (wl, n))
+    wl = "moe_mixed_tier_e256_2048x512"
+    for tier in ("T1", "T2", "T3"):
+        for idx, n in ((0, "gate"), (2, "down")):
+            routed(wl, f"{tier} {n}", synth.mixed_tier_spec(idx, tier), W[wl]["top_k"], (1, 512), idx == 2,
+                   (wl, tier, idx))
+    wl = "sweep_17408x5120_d4k256"
+    for n in ("A", "B"):
+        Ts = W[wl]["tokens"]
+        dense(wl, n, W[wl]["tensors"][n], Ts, Ts, (wl, n))
+
+    # context: a plain read and torch's fp16 GEMM on uncompressed weights
+    out += ["", "context (same GPU, same run):", ""]
+    src = torch.empty(1 << 29, dtype=torch.float16, device=dev).normal_()
+    dst = torch.empty_like(src)
+    us = timed([lambda: dst.copy_(src)] * 8)
+    out.append(f"- plain stream (torch copy of 1 GiB fp16: 1 GiB read + 1 GiB written): {us[0]:.1f} us median = "
+               f"{(2 << 30) / us[0] / 1e3:.0f} GB/s")
+    del src, dst
+    for (M, K, N) in ((17408, 5120, 2048), (17408, 5120, 4096), (5120, 17408, 4096)):
+        a = torch.randn(M, K, device=dev, dtype=torch.float16)
+        b = torch.randn(K, N, device=dev, dtype=torch.float16)
+        us = timed([lambda: a @ b] * 8)
+        out.append(f"- torch fp16 matmul (hipBLASLt), W {M}x{K} uncompressed, {N} tokens: {us[0]:.1f} us = "
+                   f"{2.0 * M * K * N / us[0] / 1e6:.1f} TFLOP/s")
+        del a, b
+    print("\n".join(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -159,6 +304,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.configs:
+        configs_report()
         return
 
     wl = synth.WORKLOADS[WORKLOAD]

@@ -118,9 +118,12 @@ vq_status vq_dequant(const vq_tensor *w, int32_t expert, uint16_t *w_out, void *
  * Decode-shaped product y = x W^T for a dense tensor (num_experts == 1):
  *   x: device [T][cols] fp16 bits, 16-byte aligned;
  *   y: device [T][rows] fp32, 16-byte aligned.
- * T >= 0 (T == 0 enqueues nothing).  Any T is accepted; the kernel streams
- * every code once per pair of tokens (once per token for d = 8), which is the
- * fast path for T = 1 (the fused decode-and-matmul of paper §3.4).
+ * T >= 0 (T == 0 enqueues nothing).  Any T is accepted.  The streaming
+ * kernel reads every code once per token, the fast path for T = 1 (the fused
+ * decode-and-matmul of paper §3.4); above a token count measured per shape
+ * (1 for tall d = 2/4 matrices, 2-4 for wide ones and d = 8, for matrices
+ * of at most 16M weights: 6) vq_gemv runs the MFMA kernel of vq_gemm instead,
+ * with the same result contract.
  */
 vq_status vq_gemv(const vq_tensor *w, const uint16_t *x, int32_t T, float *y, void *stream);
 

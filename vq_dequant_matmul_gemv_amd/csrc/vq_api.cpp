@@ -166,6 +166,19 @@ vq_status vq_dequant(const vq_tensor* w, int32_t expert, uint16_t* w_out, void* 
   return hip_status(vqmi::launch_dequant(v, expert, w_out, (hipStream_t)stream), "vq_dequant launch");
 }
 
+// Largest token count for which the streaming GEMV beats the MFMA GEMM,
+// measured on MI355X at the benchmark shapes: the GEMV re-reads every code
+// per token (one grid slice per token), the GEMM once per 128-token tile but
+// it needs enough tiles (or K slices) to fill the GPU.  Small matrices stay
+// in L2 between token slices; d = 8 codes are few per weight; matrices with
+// far more columns than rows give the GEMM few row tiles.
+static int gemv_token_limit(const vqmi::TensorView& v) {
+  if ((int64_t)v.rows * v.cols <= (int64_t)16 << 20) return 6;
+  if (v.d == 8) return 4;
+  if (v.cols >= 2 * v.rows) return v.d == 2 ? 4 : 2;
+  return 1;
+}
+
 vq_status vq_gemv(const vq_tensor* w, const uint16_t* x, int32_t T, float* y, void* stream) {
   vqmi::TensorView v;
   vq_status st = check_tensor(w, &v);
@@ -178,6 +191,8 @@ vq_status vq_gemv(const vq_tensor* w, const uint16_t* x, int32_t T, float* y, vo
   if (T == 0) return VQ_OK;
   st = check_xy(x, y, "y");
   if (st != VQ_OK) return st;
+  if (T > gemv_token_limit(v))  // above the crossover the MFMA kernel is faster
+    return hip_status(vqmi::launch_gemm(v, x, T, y, (hipStream_t)stream), "vq_gemv (MFMA path) launch");
   return hip_status(vqmi::launch_gemv(v, x, T, y, nullptr, 0, 0, (hipStream_t)stream),
                     "vq_gemv launch");
 }

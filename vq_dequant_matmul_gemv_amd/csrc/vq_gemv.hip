@@ -23,8 +23,11 @@
 //    per CU, not their bytes, is what limits a streaming kernel here, so no
 //    instruction is spent on a 2-byte scale.
 //  * x sits in VGPRs for a whole pass (x-stationary); the inner loop per code
-//    is one v_perm_b32 (LDS offset), one LDS gather and d/2 v_dot2_f32_f16 per
-//    token; the group scale multiplies each group sum once.
+//    is one v_perm_b32 (LDS offset), one LDS gather and d/2 v_dot2_f32_f16;
+//    the group scale multiplies each group sum once.
+//  * Several tokens run as one grid slice each (blockIdx.y), re-reading the
+//    codes per token: above a few tokens the MFMA GEMM is the faster kernel
+//    and the C ABI's vq_gemv hands such calls to it.
 //  * Each wave keeps P row groups' loads in flight (P items of C chunks per
 //    lane, about six chunks in all) and issues a slot's next loads right after
 //    computing it: wide items (d = 2, five chunks per lane) keep one in
@@ -67,16 +70,12 @@ struct GemvArgs {
 
 constexpr int kGemvWaves = 8;                  // two waves per SIMD
 constexpr int kGemvThreads = 64 * kGemvWaves;
-constexpr int kGemvXMaxBytes = 40 * 1024;      // largest x slice in LDS (all tokens of the tile)
+constexpr int kGemvXMaxBytes = 40 * 1024;      // largest x slice in LDS
 constexpr int kGemvScaleBytes = 16 * 1024;     // the block's scales
-constexpr int kGemvPieces = 4096;              // per-(row, pass, token) partial sums
+constexpr int kGemvPieces = 4096;              // per-(row, pass) partial sums
 
-constexpr int gemv_max_tt(int D) { return D == 8 ? 1 : 2; }
-
-// Chunks per lane a pass can hold in VGPRs: x costs 8*d VGPRs per chunk and token.
-__host__ __device__ constexpr int gemv_max_c(int D, int TT) {
-  return D == 2 ? (TT == 1 ? 5 : 2) : (D == 4 ? (TT == 1 ? 2 : 1) : 1);
-}
+// Chunks per lane a pass can hold in VGPRs: x costs 8*d VGPRs per chunk.
+__host__ __device__ constexpr int gemv_max_c(int D) { return D == 2 ? 5 : (D == 4 ? 2 : 1); }
 
 // Items a wave keeps in flight: about six 16-code chunks per lane in all, so
 // narrow items (few chunks per lane) still put enough bytes on the wire per
@@ -96,22 +95,22 @@ __device__ __forceinline__ float lane_group_sum(float v, int lg) {
 
 // XS: the x slice takes XS * 8 KiB of LDS (2 or 5); fewer staging loads for
 // short rows.
-template <int D, int B, int G, int TT, int C, int XS, bool MOE>
+template <int D, int B, int G, int C, int XS, bool MOE>
 __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
   using LY = CodebookLayout<D, B>;
   constexpr int NSC = (16 * D > G) ? (16 * D / G) : 1;  // scales per chunk
   constexpr int CPS = 16 / NSC;                          // codes per scale in a chunk
-  constexpr int HX = 8 * D;                              // half2 of x per chunk per token
+  constexpr int HX = 8 * D;                              // half2 of x per chunk
   constexpr int CB = Chunk<B>::kWords * 4;               // code bytes per chunk
   constexpr int NW = kGemvWaves;
   constexpr int NT = kGemvThreads;
-  static_assert(TT <= gemv_max_tt(D) && C <= gemv_max_c(D, TT), "tile does not fit the VGPR budget");
+  static_assert(C <= gemv_max_c(D), "tile does not fit the VGPR budget");
 
   __shared__ __align__(16) uint8_t cb_lds[LY::kBytes];
   constexpr int XBYTES = XS * 8192;
-  __shared__ __align__(16) uint8_t x_lds[XBYTES];                   // [TT][nq * 16 * D] fp16
+  __shared__ __align__(16) uint8_t x_lds[XBYTES];                   // [nq * 16 * D] fp16
   __shared__ __align__(16) uint8_t s_lds[kGemvScaleBytes];          // the block's scale rows
-  __shared__ float pieces[kGemvPieces];                             // [rows][passes][TT]
+  __shared__ float pieces[kGemvPieces];                             // [rows][passes]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -133,7 +132,6 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
   const uint16_t* cb = a.codebook;
   const uint16_t* xb;
   float* yb;
-  int ntok;
   if constexpr (MOE) {
     const int pair = blockIdx.y;
     const int e = a.ids[pair];
@@ -147,26 +145,22 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
     scales += (int64_t)e * a.scale_estride;
     cb += (int64_t)e * a.cb_estride;
     xb = a.x + (int64_t)(a.x_per_slot ? pair : pair / a.top_k) * a.cols;
-    ntok = 1;
   } else {
-    const int t0 = a.tok0 + blockIdx.y * TT;
-    xb = a.x + (int64_t)t0 * a.cols;
-    yb = a.y + (int64_t)t0 * a.rows;
-    ntok = min(TT, a.T - t0);
+    const int t = a.tok0 + blockIdx.y;  // one token per grid slice
+    xb = a.x + (int64_t)t * a.cols;
+    yb = a.y + (int64_t)t * a.rows;
   }
 
   // ---- small loads first: x slice, codebook entries, the block's scales ----
   const int xcols = a.nq * 16 * D;                      // columns of the slice
-  const uint32_t xbytes = (uint32_t)xcols * 2u;         // per token
+  const uint32_t xbytes = (uint32_t)xcols * 2u;
   constexpr int XL = (XBYTES + NT * 16 - 1) / (NT * 16);
   u32x4 xg[XL];
+  const rsrc_t rx = make_rsrc(xb, (uint64_t)a.cols * 2);
 #pragma unroll
   for (int q = 0; q < XL; ++q) {
-    const uint32_t o = (uint32_t)(tid + q * NT) * 16u;  // byte in the [TT][xcols] tile
-    const uint32_t tt = o / xbytes, co = o - tt * xbytes;
-    const bool ok = o < (uint32_t)TT * xbytes && (int)tt < ntok;
-    const rsrc_t rx = make_rsrc(xb, (uint64_t)ntok * a.cols * 2);
-    xg[q] = buf_load_b128(rx, ok ? tt * (uint32_t)a.cols * 2u + (uint32_t)a.q0 * 32u * D + co : kOutOfRange);
+    const uint32_t o = (uint32_t)(tid + q * NT) * 16u;  // byte in the x slice
+    xg[q] = buf_load_b128(rx, o < xbytes ? (uint32_t)a.q0 * 32u * D + o : kOutOfRange);
   }
   // codebook (replicated layout): lane l < 32 of wave w holds entry 32 w + l
   u32x4 ce = u32x4{0u, 0u, 0u, 0u};
@@ -294,7 +288,7 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
   lds_barrier();
 
   const uint32_t lane_off = lane_copy_offset<D, B>(lane);
-  half2_t xv[TT][C][HX];
+  half2_t xv[C][HX];
   int cur_pass = -1;
   int pass = wave % a.passes, g = wave / a.passes;
   auto item = [&](Chunk<B> (&rs)[C]) {
@@ -305,23 +299,19 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
         const int q = pass * LC + j * L + li;
         const bool ok = q < a.nq;
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-          for (int k = 0; k < HX / 4; ++k) {
-            u32x4 v = u32x4{0u, 0u, 0u, 0u};
-            if (ok) v = *reinterpret_cast<const u32x4*>(x_lds + tt * xbytes + (uint32_t)q * 32u * D + 16u * k);
-            xv[tt][j][4 * k + 0] = as_half2(v.x);
-            xv[tt][j][4 * k + 1] = as_half2(v.y);
-            xv[tt][j][4 * k + 2] = as_half2(v.z);
-            xv[tt][j][4 * k + 3] = as_half2(v.w);
-          }
+        for (int k = 0; k < HX / 4; ++k) {
+          u32x4 v = u32x4{0u, 0u, 0u, 0u};
+          if (ok) v = *reinterpret_cast<const u32x4*>(x_lds + (uint32_t)q * 32u * D + 16u * k);
+          xv[j][4 * k + 0] = as_half2(v.x);
+          xv[j][4 * k + 1] = as_half2(v.y);
+          xv[j][4 * k + 2] = as_half2(v.z);
+          xv[j][4 * k + 3] = as_half2(v.w);
+        }
       }
     }
 
     const int rb = g * R + rsub;                        // row within the block
-    float acc[TT];
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) acc[tt] = 0.f;
+    float acc = 0.f;
     // The gathers of chunk j + 1 are issued before the dot products of
     // chunk j.  Everything is computed unconditionally; a chunk past the
     // slice or a row past the block is dropped with a bit mask (a select
@@ -341,31 +331,20 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
       const uint32_t sbase = s_skew + ((uint32_t)rb * (uint32_t)a.spr + ((uint32_t)(a.q0 + q) * 16u * D) / G) * 2u;
 #pragma unroll
       for (int s2 = 0; s2 < NSC; ++s2) {
-        float gs[TT][2];  // two chains per token for ILP
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) gs[tt][0] = gs[tt][1] = 0.f;
+        float gs[2] = {0.f, 0.f};  // two chains for ILP
 #pragma unroll
         for (int i = s2 * CPS; i < (s2 + 1) * CPS; ++i)
 #pragma unroll
-          for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-            for (int k = 0; k < D / 2; ++k)
-              gs[tt][(i * (D / 2) + k) & 1] =
-                  dot2(e[j & 1][i].v[k], xv[tt][j][i * (D / 2) + k], gs[tt][(i * (D / 2) + k) & 1]);
+          for (int k = 0; k < D / 2; ++k)
+            gs[(i * (D / 2) + k) & 1] = dot2(e[j & 1][i].v[k], xv[j][i * (D / 2) + k], gs[(i * (D / 2) + k) & 1]);
         const uint16_t sbits = *reinterpret_cast<const uint16_t*>(s_lds + (ok ? sbase + 2u * s2 : 0u));
         const float scale = half_bits_to_float(sbits);
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-          const float gsum = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, gs[tt][0] + gs[tt][1]) & keep);
-          acc[tt] = __builtin_fmaf(gsum, __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, scale) & keep), acc[tt]);
-        }
+        const float gsum = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, gs[0] + gs[1]) & keep);
+        acc = __builtin_fmaf(gsum, __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, scale) & keep), acc);
       }
     }
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      const float v = lane_group_sum(acc[tt], lg);
-      if (li == L - 1 && rb < brows) pieces[(rb * a.passes + pass) * TT + tt] = v;
-    }
+    const float v = lane_group_sum(acc, lg);
+    if (li == L - 1 && rb < brows) pieces[rb * a.passes + pass] = v;
     // Only now this slot's next loads (item u + P): measured on MI355X,
     // issuing them before the compute is slower, as the loads then wait in
     // the CU's memory queue behind other waves' while this wave could compute.
@@ -388,15 +367,10 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
   {  // y: each row's pass pieces added in pass order (deterministic)
     __syncthreads();
     for (int r = tid; r < brows; r += NT) {
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        float v = 0.f;
-        for (int c = 0; c < a.passes; ++c) v += pieces[(r * a.passes + c) * TT + tt];
-        if (tt < ntok) {
-          float* dst = yb + (int64_t)tt * a.rows + brow0 + r;
-          *dst = a.accumulate ? *dst + v : v;
-        }
-      }
+      float v = 0.f;
+      for (int c = 0; c < a.passes; ++c) v += pieces[r * a.passes + c];
+      float* dst = yb + brow0 + r;
+      *dst = a.accumulate ? *dst + v : v;
     }
   }
 }
@@ -514,32 +488,34 @@ LaneTiling plan_tiling(int nq, int max_c, int waves) {
   return best;
 }
 
-template <int D, int B, int G, int TT, int C, int XS, bool MOE>
+template <int D, int B, int G, int C, int XS, bool MOE>
 hipError_t gemv_launch_c(const GemvArgs& a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((vq_gemv_kernel<D, B, G, TT, C, XS, MOE>), grid, dim3(kGemvThreads), 0, s, a);
+  hipLaunchKernelGGL((vq_gemv_kernel<D, B, G, C, XS, MOE>), grid, dim3(kGemvThreads), 0, s, a);
   return hipGetLastError();
 }
 
-template <int D, int B, int G, int TT, int XS, bool MOE>
+template <int D, int B, int G, int XS, bool MOE>
 hipError_t gemv_launch(const GemvArgs& a, int C, dim3 grid, hipStream_t s) {
-  constexpr int MC = gemv_max_c(D, TT);
+  constexpr int MC = gemv_max_c(D);
   switch (C) {
-    case 1: return gemv_launch_c<D, B, G, TT, 1, XS, MOE>(a, grid, s);
-    case 2: if constexpr (MC >= 2) return gemv_launch_c<D, B, G, TT, 2, XS, MOE>(a, grid, s); break;
-    case 3: if constexpr (MC >= 3) return gemv_launch_c<D, B, G, TT, 3, XS, MOE>(a, grid, s); break;
-    case 4: if constexpr (MC >= 4) return gemv_launch_c<D, B, G, TT, 4, XS, MOE>(a, grid, s); break;
-    case 5: if constexpr (MC >= 5) return gemv_launch_c<D, B, G, TT, 5, XS, MOE>(a, grid, s); break;
+    case 1: return gemv_launch_c<D, B, G, 1, XS, MOE>(a, grid, s);
+    case 2: if constexpr (MC >= 2) return gemv_launch_c<D, B, G, 2, XS, MOE>(a, grid, s); break;
+    case 3: if constexpr (MC >= 3) return gemv_launch_c<D, B, G, 3, XS, MOE>(a, grid, s); break;
+    case 4: if constexpr (MC >= 4) return gemv_launch_c<D, B, G, 4, XS, MOE>(a, grid, s); break;
+    case 5: if constexpr (MC >= 5) return gemv_launch_c<D, B, G, 5, XS, MOE>(a, grid, s); break;
     default: break;
   }
   return hipErrorInvalidValue;
 }
 
-// Column slices that fit the x tile in LDS run one after another, adding into
-// y; rows are split over about one block per CU, or more where a block's
-// scales or row pieces would not fit in LDS.
-template <int D, int B, int G, int TT, bool MOE>
+// Column slices that fit the x slice in LDS run one after another, adding
+// into y; rows are split over about one block per CU (per token slice), or
+// more where a block's scales or row pieces would not fit in LDS.  Dense
+// calls run one grid slice per token (blockIdx.y), routed calls one per
+// (token, slot) pair.
+template <int D, int B, int G, bool MOE>
 hipError_t gemv_run(GemvArgs a, int P, int ycount, hipStream_t s) {
-  const int slice_max = kGemvXMaxBytes / (TT * 32 * D);
+  const int slice_max = kGemvXMaxBytes / (32 * D);
   const int n_slices = (P + slice_max - 1) / slice_max;
   const int per_slice = (P + n_slices - 1) / n_slices;
   const int blocks_fill = std::max(1, num_cus() / std::max(1, ycount));
@@ -547,22 +523,22 @@ hipError_t gemv_run(GemvArgs a, int P, int ycount, hipStream_t s) {
     a.q0 = sl * per_slice;
     a.nq = std::min(per_slice, P - a.q0);
     a.accumulate = sl > 0;
-    const LaneTiling t = plan_tiling(a.nq, gemv_max_c(D, TT), kGemvWaves);
+    const LaneTiling t = plan_tiling(a.nq, gemv_max_c(D), kGemvWaves);
     a.lanes_log2 = t.lg;
     a.passes = t.passes;
     const int64_t by_scales = std::max<int64_t>(1, (kGemvScaleBytes - 16) / (2 * (int64_t)a.spr));
-    const int64_t by_pieces = std::max<int64_t>(1, kGemvPieces / ((int64_t)t.passes * TT));
+    const int64_t by_pieces = std::max<int64_t>(1, kGemvPieces / (int64_t)t.passes);
     const int64_t rows_max = std::min(by_scales, by_pieces);
     const int64_t blocks = std::min<int64_t>(a.rows, std::max<int64_t>(blocks_fill, (a.rows + rows_max - 1) / rows_max));
     a.rows_base = (int)(a.rows / blocks);
     a.rows_extra = (int)(a.rows - (int64_t)a.rows_base * blocks);
-    const int XS = (int64_t)TT * a.nq * 32 * D <= 2 * 8192 ? 2 : 5;
-    // dense: at most 65535 token tiles per launch
+    const int XS = (int64_t)a.nq * 32 * D <= 2 * 8192 ? 2 : 5;
+    // dense: at most 65535 token slices per launch
     for (int y0 = 0; y0 < ycount; y0 += 65535) {
       const int yc = std::min(65535, ycount - y0);
-      if (!MOE) a.tok0 = y0 * TT;
-      hipError_t e = XS == 2 ? gemv_launch<D, B, G, TT, 2, MOE>(a, t.C, dim3((unsigned)blocks, (unsigned)yc), s)
-                             : gemv_launch<D, B, G, TT, 5, MOE>(a, t.C, dim3((unsigned)blocks, (unsigned)yc), s);
+      if (!MOE) a.tok0 = y0;
+      hipError_t e = XS == 2 ? gemv_launch<D, B, G, 2, MOE>(a, t.C, dim3((unsigned)blocks, (unsigned)yc), s)
+                             : gemv_launch<D, B, G, 5, MOE>(a, t.C, dim3((unsigned)blocks, (unsigned)yc), s);
       if (e != hipSuccess) return e;
       if (MOE) break;
     }
@@ -593,13 +569,10 @@ hipError_t gemv_geom(const TensorView& w, const uint16_t* x, int T, float* y, co
   a.x_per_slot = x_per_slot;
   if (ids) {
     a.T = T * top_k;
-    return gemv_run<D, B, G, 1, true>(a, P, T * top_k, s);
+    return gemv_run<D, B, G, true>(a, P, T * top_k, s);
   }
   a.T = T;
-  if constexpr (gemv_max_tt(D) >= 2) {
-    if (T >= 2) return gemv_run<D, B, G, 2, false>(a, P, (T + 1) / 2, s);
-  }
-  return gemv_run<D, B, G, 1, false>(a, P, T, s);
+  return gemv_run<D, B, G, false>(a, P, T, s);
 }
 
 template <int D, int B, int G>
