@@ -48,9 +48,10 @@ def parse():
                     help="run only a few gate GEMV and GEMM launches (for rocprofv3 --pmc passes)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain device copy of known size (counter calibration)")
-    ap.add_argument("--configs", action="store_true",
+    ap.add_argument("--configs", nargs="?", const="", default=None, metavar="FILTER",
                     help="print a per-workload report (every config, both kernels, median/p10/p90) "
-                         "as markdown instead of the JSON line")
+                         "as markdown instead of the JSON line; FILTER keeps workloads whose name "
+                         "contains it")
     return ap.parse_args()
 
 
@@ -144,10 +145,10 @@ def cpu_baseline(arrs, spec, rows):
                       f"unpack + fp16 dequant + float64 matmul, {reps} reps, {dt * 1e3:.1f} ms each"}
 
 
-REPORT_CMD = "python3 bench.py --configs"
+REPORT_CMD = "python3 bench.py --configs"  # the full report (no filter)
 
 
-def configs_report():
+def configs_report(only=""):
     """Every workload of the benchmark set, both kernels, timed as back-to-back
     calls in one HIP graph rotating over weight replicas (>= 1.1 GB touched
     per replay where the tensors allow, so calls stream from HBM, not the
@@ -251,22 +252,27 @@ def configs_report():
         torch.cuda.empty_cache()
 
     W = synth.WORKLOADS
-    dense("gemv_1024", "w", W["gemv_1024"]["tensors"]["w"], [1], [], ("gemv_1024", "w"))
+    keep = lambda wl: only in wl
+    if keep("gemv_1024"):
+        dense("gemv_1024", "w", W["gemv_1024"]["tensors"]["w"], [1], [], ("gemv_1024", "w"))
     wl = "dense_mlp_5120x17408_d2k256"
-    for n in ("gate", "up", "down"):
+    for n in ("gate", "up", "down") if keep(wl) else ():
         dense(wl, n, W[wl]["tensors"][n], [1], [2048], (wl, n))
     wl = "moe_e256_4096x1024_d4k256"
-    for n in ("gate", "down"):
+    for n in ("gate", "down") if keep(wl) else ():
         routed(wl, n, W[wl]["tensors"][n], W[wl]["top_k"], (1, 1024), n == "down", (wl, n))
     wl = "moe_mixed_tier_e256_2048x512"
-    for tier in ("T1", "T2", "T3"):
+    for tier in ("T1", "T2", "T3") if keep(wl) else ():
         for idx, n in ((0, "gate"), (2, "down")):
             routed(wl, f"{tier} {n}", synth.mixed_tier_spec(idx, tier), W[wl]["top_k"], (1, 512), idx == 2,
                    (wl, tier, idx))
     wl = "sweep_17408x5120_d4k256"
-    for n in ("A", "B"):
+    for n in ("A", "B") if keep(wl) else ():
         Ts = W[wl]["tokens"]
         dense(wl, n, W[wl]["tensors"][n], Ts, Ts, (wl, n))
+    if only:
+        print("\n".join(out), flush=True)
+        return
 
     # context: a plain read and torch's fp16 GEMM on uncompressed weights
     out += ["", "context (same GPU, same run):", ""]
@@ -305,8 +311,8 @@ def main():
     if args.copy_probe:
         copy_probe()
         return
-    if args.configs:
-        configs_report()
+    if args.configs is not None:
+        configs_report(args.configs)
         return
 
     wl = synth.WORKLOADS[WORKLOAD]

@@ -554,7 +554,8 @@ namespace {
 
 using GemmSmallT = GemmShape<4, 4, 1>;  // 512 rows x 32 tokens
 using GemmLargeT = GemmShape<8, 2, 4>;  // 512 rows x 128 tokens
-using GemmMoe = GemmShape<4, 4, 2>;     // 512 rows x 64 tokens
+using GemmMoe = GemmShape<8, 2, 1>;     // 512 rows x 32 tokens: routed experts mostly get a
+                                        // few tokens, so thin tiles waste the least MFMA work
 constexpr int kMoeTileTokens = GemmMoe::kTokens;
 
 int max_tiles_for(int npairs, int E) { return (npairs + kMoeTileTokens - 1) / kMoeTileTokens + E; }
