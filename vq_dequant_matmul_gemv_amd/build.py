@@ -28,9 +28,13 @@ ARCH = "gfx950"
 # Packed-fp32 VALU forms are switched off: only scalar/packed-fp16 arithmetic
 # is used on purpose; hipcc's host pass warns that it does not know the
 # feature, which is harmless.
+# Kernel-argument preloading: the first 10 scalar arguments of a kernel (the
+# GEMV's pointers, row count and row split: 14 SGPRs) arrive in SGPRs at wave
+# launch.
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-kernarg-preload-count=10",
     "-fno-gpu-rdc", "-I", INCLUDE, "-I", CSRC,
 ]
 

@@ -96,7 +96,18 @@ __device__ __forceinline__ float lane_group_sum(float v, int lg) {
 // XS: the x slice takes XS * 8 KiB of LDS (2 or 5); fewer staging loads for
 // short rows.
 template <int D, int B, int G, int C, int XS, bool MOE>
-__global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
+//
+// The arguments a block needs before its first loads come first, as scalars:
+// with kernel-argument preloading (the build passes
+// -amdgpu-kernarg-preload-count) they arrive in SGPRs at wave launch instead
+// of after a scalar load from the argument buffer.  The rest (output,
+// routing, accumulation) is only needed later and stays in the struct.
+//   xs: x of token tok0 (dense) or x (routed); shape = nq | lanes_log2 << 16 |
+//   passes << 20; cols = spr * G.
+__global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
+    const uint32_t* __restrict__ codes_in, const uint16_t* __restrict__ cb_in,
+    const uint16_t* __restrict__ scales_in, const uint16_t* __restrict__ xs, int rows, int rows_base,
+    int rows_extra, int q0, int spr, uint32_t shape, GemvArgs a) {
   using LY = CodebookLayout<D, B>;
   constexpr int NSC = (16 * D > G) ? (16 * D / G) : 1;  // scales per chunk
   constexpr int CPS = 16 / NSC;                          // codes per scale in a chunk
@@ -115,7 +126,11 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lg = a.lanes_log2;
+  const int nq = (int)(shape & 0xffffu);
+  const int lg = (int)((shape >> 16) & 0xfu);
+  const int passes = (int)(shape >> 20);
+  const int cols = spr * G;
+  const int wr = cols / (32 * D) * B;     // code words per row
   const int L = 1 << lg;
   const int R = 64 >> lg;                 // rows per group
   const int rsub = lane >> lg;            // this lane's row within the group
@@ -123,19 +138,19 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
 
   // ---- this block's rows ----
   const int bid = blockIdx.x;
-  const int brow0 = bid * a.rows_base + min(bid, a.rows_extra);
-  const int brows = a.rows_base + (bid < a.rows_extra ? 1 : 0);
+  const int brow0 = bid * rows_base + min(bid, rows_extra);
+  const int brows = rows_base + (bid < rows_extra ? 1 : 0);
   const int ngroups = (brows + R - 1) / R;
 
-  const uint32_t* codes = a.codes;
-  const uint16_t* scales = a.scales;
-  const uint16_t* cb = a.codebook;
+  const uint32_t* codes = codes_in;
+  const uint16_t* scales = scales_in;
+  const uint16_t* cb = cb_in;
   const uint16_t* xb;
   float* yb;
   if constexpr (MOE) {
     const int pair = blockIdx.y;
     const int e = a.ids[pair];
-    yb = a.y + (int64_t)pair * a.rows;
+    yb = a.y + (int64_t)pair * rows;
     if (e < 0 || e >= a.num_experts) {  // skipped slot: zero rows (block-uniform exit)
       if (!a.accumulate)
         for (int r = tid; r < brows; r += NT) yb[brow0 + r] = 0.f;
@@ -144,23 +159,22 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
     codes += (int64_t)e * a.code_estride;
     scales += (int64_t)e * a.scale_estride;
     cb += (int64_t)e * a.cb_estride;
-    xb = a.x + (int64_t)(a.x_per_slot ? pair : pair / a.top_k) * a.cols;
+    xb = xs + (int64_t)(a.x_per_slot ? pair : pair / a.top_k) * cols;
   } else {
-    const int t = a.tok0 + blockIdx.y;  // one token per grid slice
-    xb = a.x + (int64_t)t * a.cols;
-    yb = a.y + (int64_t)t * a.rows;
+    xb = xs + (int64_t)blockIdx.y * cols;  // one token per grid slice
+    yb = a.y + (int64_t)(a.tok0 + blockIdx.y) * rows;
   }
 
   // ---- small loads first: x slice, codebook entries, the block's scales ----
-  const int xcols = a.nq * 16 * D;                      // columns of the slice
+  const int xcols = nq * 16 * D;                        // columns of the slice
   const uint32_t xbytes = (uint32_t)xcols * 2u;
   constexpr int XL = (XBYTES + NT * 16 - 1) / (NT * 16);
   u32x4 xg[XL];
-  const rsrc_t rx = make_rsrc(xb, (uint64_t)a.cols * 2);
+  const rsrc_t rx = make_rsrc(xb, (uint64_t)cols * 2);
 #pragma unroll
   for (int q = 0; q < XL; ++q) {
     const uint32_t o = (uint32_t)(tid + q * NT) * 16u;  // byte in the x slice
-    xg[q] = buf_load_b128(rx, o < xbytes ? (uint32_t)a.q0 * 32u * D + o : kOutOfRange);
+    xg[q] = buf_load_b128(rx, o < xbytes ? (uint32_t)q0 * 32u * D + o : kOutOfRange);
   }
   // codebook (replicated layout): lane l < 32 of wave w holds entry 32 w + l
   u32x4 ce = u32x4{0u, 0u, 0u, 0u};
@@ -175,10 +189,10 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
   }
   // scale rows [brow0, brow0 + brows), read as 16-byte pieces from a 16-byte
   // boundary at or below the first scale
-  const uint64_t s_first = (uint64_t)brow0 * a.spr * 2u;
+  const uint64_t s_first = (uint64_t)brow0 * spr * 2u;
   const uint32_t s_skew = (uint32_t)(s_first & 15u);
-  const uint32_t s_span = (uint32_t)brows * (uint32_t)a.spr * 2u + s_skew;
-  const uint32_t s_avail = (uint32_t)((uint64_t)a.rows * a.spr * 2u - (s_first - s_skew));  // to the tensor's end
+  const uint32_t s_span = (uint32_t)brows * (uint32_t)spr * 2u + s_skew;
+  const uint32_t s_avail = (uint32_t)((uint64_t)rows * spr * 2u - (s_first - s_skew));  // to the tensor's end
   const rsrc_t rsb = make_rsrc(reinterpret_cast<const uint8_t*>(scales) + (s_first - s_skew), s_avail);
   constexpr int SL = (kGemvScaleBytes + NT * 16 - 1) / (NT * 16);
   u32x4 sg[SL];
@@ -199,25 +213,25 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
   __builtin_amdgcn_s_barrier();
 
   // ---- the code stream: work item u = (pass, group) in pass-major order ----
-  const rsrc_t rc = make_rsrc(codes, (uint64_t)a.rows * a.wr * 4);
-  const uint32_t row_cb = (uint32_t)a.wr * 4u;
+  const rsrc_t rc = make_rsrc(codes, (uint64_t)rows * wr * 4);
+  const uint32_t row_cb = (uint32_t)wr * 4u;
   const int LC = L * C;                                 // chunks per pass
   // items f = group * passes + pass, dealt round-robin over the waves: when
   // the wave count is a multiple of the pass count a wave keeps one pass (no
   // x reloads), and the block's waves always read neighbouring row groups.
-  const int total_items = ngroups * a.passes;
-  const int step_g = NW / a.passes, step_p = NW - step_g * a.passes;  // f += NW
+  const int total_items = ngroups * passes;
+  const int step_g = NW / passes, step_p = NW - step_g * passes;  // f += NW
   const int n_items = total_items > wave ? (total_items - wave + NW - 1) / NW : 0;
   constexpr int P = gemv_ring(C);
   Chunk<B> ring[P][C];                                  // codes of the items in flight
   int l_item = 0;                                       // next item to load
-  int l_pass = wave % a.passes, l_g = wave / a.passes;  // its pass and group
+  int l_pass = wave % passes, l_g = wave / passes;  // its pass and group
   uint32_t lane_vo[C];                                  // per-lane code offsets of l_pass
   auto set_pass_offsets = [&](int pass) {
 #pragma unroll
     for (int j = 0; j < C; ++j) {
       const int q = pass * LC + j * L + li;
-      lane_vo[j] = q < a.nq ? (uint32_t)rsub * row_cb + (uint32_t)(a.q0 + q) * CB : kOutOfRange;
+      lane_vo[j] = q < nq ? (uint32_t)rsub * row_cb + (uint32_t)(q0 + q) * CB : kOutOfRange;
     }
   };
   set_pass_offsets(l_pass);
@@ -247,7 +261,7 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
     ++l_item;
     l_g += step_g;
     l_pass += step_p;
-    if (l_pass >= a.passes) { l_pass -= a.passes; ++l_g; }
+    if (l_pass >= passes) { l_pass -= passes; ++l_g; }
     if (step_p != 0) set_pass_offsets(l_pass);
   };
 #pragma unroll
@@ -290,14 +304,14 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
   const uint32_t lane_off = lane_copy_offset<D, B>(lane);
   half2_t xv[C][HX];
   int cur_pass = -1;
-  int pass = wave % a.passes, g = wave / a.passes;
+  int pass = wave % passes, g = wave / passes;
   auto item = [&](Chunk<B> (&rs)[C]) {
     if (pass != cur_pass) {  // x of this pass into VGPRs (zeros past the slice)
       cur_pass = pass;
 #pragma unroll
       for (int j = 0; j < C; ++j) {
         const int q = pass * LC + j * L + li;
-        const bool ok = q < a.nq;
+        const bool ok = q < nq;
 #pragma unroll
         for (int k = 0; k < HX / 4; ++k) {
           u32x4 v = u32x4{0u, 0u, 0u, 0u};
@@ -326,9 +340,9 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
     for (int j = 0; j < C; ++j) {
       if (j + 1 < C) issue(j + 1, e[(j + 1) & 1]);
       const int q = pass * LC + j * L + li;
-      const bool ok = q < a.nq && rb < brows;
+      const bool ok = q < nq && rb < brows;
       const uint32_t keep = ok ? 0xffffffffu : 0u;
-      const uint32_t sbase = s_skew + ((uint32_t)rb * (uint32_t)a.spr + ((uint32_t)(a.q0 + q) * 16u * D) / G) * 2u;
+      const uint32_t sbase = s_skew + ((uint32_t)rb * (uint32_t)spr + ((uint32_t)(q0 + q) * 16u * D) / G) * 2u;
 #pragma unroll
       for (int s2 = 0; s2 < NSC; ++s2) {
         float gs[2] = {0.f, 0.f};  // two chains for ILP
@@ -344,14 +358,14 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
       }
     }
     const float v = lane_group_sum(acc, lg);
-    if (li == L - 1 && rb < brows) pieces[rb * a.passes + pass] = v;
+    if (li == L - 1 && rb < brows) pieces[rb * passes + pass] = v;
     // Only now this slot's next loads (item u + P): measured on MI355X,
     // issuing them before the compute is slower, as the loads then wait in
     // the CU's memory queue behind other waves' while this wave could compute.
     load_item(rs);
     g += step_g;
     pass += step_p;
-    if (pass >= a.passes) { pass -= a.passes; ++g; }
+    if (pass >= passes) { pass -= passes; ++g; }
   };
   // Slot k of the ring holds items k, k + P, k + 2P, ...: unrolled by P so
   // every slot is a fixed set of registers.  The wave runs its item count
@@ -368,7 +382,7 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(GemvArgs a) {
     __syncthreads();
     for (int r = tid; r < brows; r += NT) {
       float v = 0.f;
-      for (int c = 0; c < a.passes; ++c) v += pieces[r * a.passes + c];
+      for (int c = 0; c < passes; ++c) v += pieces[r * passes + c];
       float* dst = yb + brow0 + r;
       *dst = a.accumulate ? *dst + v : v;
     }
@@ -490,7 +504,11 @@ LaneTiling plan_tiling(int nq, int max_c, int waves) {
 
 template <int D, int B, int G, int C, int XS, bool MOE>
 hipError_t gemv_launch_c(const GemvArgs& a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((vq_gemv_kernel<D, B, G, C, XS, MOE>), grid, dim3(kGemvThreads), 0, s, a);
+  const uint16_t* xs = MOE ? a.x : a.x + (int64_t)a.tok0 * a.cols;
+  if (a.nq > 0xffff || a.lanes_log2 > 15 || a.passes > 0xfff) return hipErrorInvalidValue;
+  const uint32_t shape = (uint32_t)a.nq | ((uint32_t)a.lanes_log2 << 16) | ((uint32_t)a.passes << 20);
+  hipLaunchKernelGGL((vq_gemv_kernel<D, B, G, C, XS, MOE>), grid, dim3(kGemvThreads), 0, s, a.codes, a.codebook,
+                     a.scales, xs, a.rows, a.rows_base, a.rows_extra, a.q0, a.spr, shape, a);
   return hipGetLastError();
 }
 
