@@ -75,7 +75,7 @@ constexpr int kGemvScaleBytes = 16 * 1024;     // the block's scales
 constexpr int kGemvPieces = 4096;              // per-(row, pass) partial sums
 
 // Chunks per lane a pass can hold in VGPRs: x costs 8*d VGPRs per chunk.
-__host__ __device__ constexpr int gemv_max_c(int D) { return D == 2 ? 5 : (D == 4 ? 2 : 1); }
+__host__ __device__ constexpr int gemv_max_c(int D) { return D == 2 ? 5 : (D == 4 ? 3 : 1); }
 
 // Items a wave keeps in flight: about six 16-code chunks per lane in all, so
 // narrow items (few chunks per lane) still put enough bytes on the wire per
@@ -326,35 +326,45 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
 
     const int rb = g * R + rsub;                        // row within the block
     float acc = 0.f;
-    // The gathers of chunk j + 1 are issued before the dot products of
-    // chunk j.  Everything is computed unconditionally; a chunk past the
-    // slice or a row past the block is dropped with a bit mask (a select
-    // would let the compiler branch around the gathers).
-    Entry<D> e[2][16];
-    auto issue = [&](int j, Entry<D> (&dst)[16]) {
+    // The gathers of step t + 1 are issued before the dot products of step
+    // t; a step is SB codes of one chunk (16 for d = 2, 8 for d = 4, 4 for
+    // d = 8), so the gathered entries in flight take 2 * SB * d / 2 = 32 VGPRs
+    // whatever d, and wide x-stationary tiles (5 chunks per lane) fit for d = 4
+    // too.  Everything is computed unconditionally; a chunk past the slice or
+    // a row past the block is dropped with a bit mask (a select would let the
+    // compiler branch around the gathers).
+    constexpr int S = (D == 2) ? 1 : (D == 4 ? 2 : 4);  // steps per chunk
+    constexpr int SB = 16 / S;                          // codes per step
+    static_assert(CPS % SB == 0, "a step lies inside one scale group");
+    Entry<D> e[2][SB];
+    auto issue = [&](int t, Entry<D> (&dst)[SB]) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dst[i] = gather<D, B>(cb_lds, rs[j], i, lane_off);
+      for (int i = 0; i < SB; ++i) dst[i] = gather<D, B>(cb_lds, rs[t / S], (t % S) * SB + i, lane_off);
     };
     issue(0, e[0]);
+    float gs[2] = {0.f, 0.f};  // two chains for ILP, restarted per scale group
 #pragma unroll
-    for (int j = 0; j < C; ++j) {
-      if (j + 1 < C) issue(j + 1, e[(j + 1) & 1]);
-      const int q = pass * LC + j * L + li;
-      const bool ok = q < nq && rb < brows;
-      const uint32_t keep = ok ? 0xffffffffu : 0u;
-      const uint32_t sbase = s_skew + ((uint32_t)rb * (uint32_t)spr + ((uint32_t)(q0 + q) * 16u * D) / G) * 2u;
+    for (int t = 0; t < C * S; ++t) {
+      if (t + 1 < C * S) issue(t + 1, e[(t + 1) & 1]);
+      const int j = t / S, b = t % S;
 #pragma unroll
-      for (int s2 = 0; s2 < NSC; ++s2) {
-        float gs[2] = {0.f, 0.f};  // two chains for ILP
+      for (int ii = 0; ii < SB; ++ii) {
+        const int i = b * SB + ii;
 #pragma unroll
-        for (int i = s2 * CPS; i < (s2 + 1) * CPS; ++i)
-#pragma unroll
-          for (int k = 0; k < D / 2; ++k)
-            gs[(i * (D / 2) + k) & 1] = dot2(e[j & 1][i].v[k], xv[j][i * (D / 2) + k], gs[(i * (D / 2) + k) & 1]);
+        for (int k = 0; k < D / 2; ++k)
+          gs[(i * (D / 2) + k) & 1] = dot2(e[t & 1][ii].v[k], xv[j][i * (D / 2) + k], gs[(i * (D / 2) + k) & 1]);
+      }
+      if (((b + 1) * SB) % CPS == 0) {  // the step ends scale group s2 of chunk j
+        const int s2 = (b + 1) * SB / CPS - 1;
+        const int q = pass * LC + j * L + li;
+        const bool ok = q < nq && rb < brows;
+        const uint32_t keep = ok ? 0xffffffffu : 0u;
+        const uint32_t sbase = s_skew + ((uint32_t)rb * (uint32_t)spr + ((uint32_t)(q0 + q) * 16u * D) / G) * 2u;
         const uint16_t sbits = *reinterpret_cast<const uint16_t*>(s_lds + (ok ? sbase + 2u * s2 : 0u));
         const float scale = half_bits_to_float(sbits);
         const float gsum = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, gs[0] + gs[1]) & keep);
         acc = __builtin_fmaf(gsum, __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, scale) & keep), acc);
+        gs[0] = gs[1] = 0.f;
       }
     }
     const float v = lane_group_sum(acc, lg);
