@@ -50,6 +50,8 @@ def short_name(name: str) -> str:
             return "torch fill"
         return "torch kernel"
     name = re.sub(r"^void ", "", name)
+    if ">(" in name:  # template kernel: drop the parameter list
+        name = name[:name.index(">(") + 1]
     name = re.sub(r"\(vqmi::\w+\)$", "", name)
     return name.replace("vqmi::", "")
 
