@@ -303,6 +303,7 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
 
   const uint32_t lane_off = lane_copy_offset<D, B>(lane);
   half2_t xv[C][HX];
+  uint32_t lane_sq[C], lane_ok[C];  // per pass: scale byte offset in the row, chunk-valid mask
   int cur_pass = -1;
   int pass = wave % passes, g = wave / passes;
   auto item = [&](Chunk<B> (&rs)[C]) {
@@ -312,6 +313,8 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
       for (int j = 0; j < C; ++j) {
         const int q = pass * LC + j * L + li;
         const bool ok = q < nq;
+        lane_sq[j] = ((uint32_t)(q0 + q) * 16u * D) / G * 2u;
+        lane_ok[j] = ok ? 0xffffffffu : 0u;
 #pragma unroll
         for (int k = 0; k < HX / 4; ++k) {
           u32x4 v = u32x4{0u, 0u, 0u, 0u};
@@ -325,6 +328,8 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
     }
 
     const int rb = g * R + rsub;                        // row within the block
+    const uint32_t srow = s_skew + (uint32_t)rb * (uint32_t)spr * 2u;  // the row's scales in s_lds
+    const uint32_t rowok = rb < brows ? 0xffffffffu : 0u;
     float acc = 0.f;
     // The gathers of step t + 1 are issued before the dot products of step
     // t; a step is SB codes of one chunk (16 for d = 2, 8 for d = 4, 4 for
@@ -356,11 +361,8 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
       }
       if (((b + 1) * SB) % CPS == 0) {  // the step ends scale group s2 of chunk j
         const int s2 = (b + 1) * SB / CPS - 1;
-        const int q = pass * LC + j * L + li;
-        const bool ok = q < nq && rb < brows;
-        const uint32_t keep = ok ? 0xffffffffu : 0u;
-        const uint32_t sbase = s_skew + ((uint32_t)rb * (uint32_t)spr + ((uint32_t)(q0 + q) * 16u * D) / G) * 2u;
-        const uint16_t sbits = *reinterpret_cast<const uint16_t*>(s_lds + (ok ? sbase + 2u * s2 : 0u));
+        const uint32_t keep = lane_ok[j] & rowok;
+        const uint16_t sbits = *reinterpret_cast<const uint16_t*>(s_lds + ((srow + lane_sq[j] + 2u * s2) & keep));
         const float scale = half_bits_to_float(sbits);
         const float gsum = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, gs[0] + gs[1]) & keep);
         acc = __builtin_fmaf(gsum, __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, scale) & keep), acc);
