@@ -121,9 +121,9 @@ vq_status vq_dequant(const vq_tensor *w, int32_t expert, uint16_t *w_out, void *
  * T >= 0 (T == 0 enqueues nothing).  Any T is accepted.  The streaming
  * kernel reads every code once per token, the fast path for T = 1 (the fused
  * decode-and-matmul of paper §3.4); above a token count measured per shape
- * (1 for tall d = 2/4 matrices, 2-4 for wide ones and d = 8, for matrices
- * of at most 16M weights: 6) vq_gemv runs the MFMA kernel of vq_gemm instead,
- * with the same result contract.
+ * (1 for d = 2/4 matrices, 4 for d = 8, 6 for matrices of at most 16M
+ * weights) vq_gemv runs the MFMA kernel of vq_gemm instead, with the same
+ * result contract.
  */
 vq_status vq_gemv(const vq_tensor *w, const uint16_t *x, int32_t T, float *y, void *stream);
 

@@ -168,14 +168,13 @@ vq_status vq_dequant(const vq_tensor* w, int32_t expert, uint16_t* w_out, void* 
 
 // Largest token count for which the streaming GEMV beats the MFMA GEMM,
 // measured on MI355X at the benchmark shapes: the GEMV re-reads every code
-// per token (one grid slice per token), the GEMM once per 128-token tile but
-// it needs enough tiles (or K slices) to fill the GPU.  Small matrices stay
-// in L2 between token slices; d = 8 codes are few per weight; matrices with
-// far more columns than rows give the GEMM few row tiles.
+// per token (one grid slice per token), the GEMM once per 32- or 128-token
+// tile, split along K to fill the GPU.  Small matrices stay in L2 between
+// token slices, and d = 8 codes are few per weight, so the GEMV keeps a few
+// tokens there; otherwise it wins at T = 1 only.
 static int gemv_token_limit(const vqmi::TensorView& v) {
   if ((int64_t)v.rows * v.cols <= (int64_t)16 << 20) return 6;
   if (v.d == 8) return 4;
-  if (v.cols >= 2 * v.rows) return v.d == 2 ? 4 : 2;
   return 1;
 }
 

@@ -552,7 +552,7 @@ __global__ __launch_bounds__(1024) void vq_route_kernel(RouteArgs a) {
 
 namespace {
 
-using GemmSmallT = GemmShape<4, 4, 1>;  // 512 rows x 32 tokens
+using GemmSmallT = GemmShape<8, 2, 1>;  // 512 rows x 32 tokens, two waves per SIMD
 using GemmLargeT = GemmShape<8, 2, 4>;  // 512 rows x 128 tokens
 using GemmMoe = GemmShape<8, 2, 1>;     // 512 rows x 32 tokens: routed experts mostly get a
                                         // few tokens, so thin tiles waste the least MFMA work
@@ -612,8 +612,11 @@ hipError_t gemm_dense(GemmArgs a, hipStream_t s) {
   int full = (tiles / cus) * cus, rem = tiles - full, split = 1;
   if (rem > 0) {
     double best = 1e30;
-    for (int sp = 1; sp <= std::min(16, std::max(1, nks / 8)); ++sp) {
-      const double c = (double)((rem * sp + cus - 1) / cus) / sp + 0.03 * (sp - 1);
+    // the charge per slice scales with the tokens of a tile: the atomic adds
+    // are T x rows per slice, negligible next to the weight stream at small T
+    const double charge = 0.03 * std::min(1.0, (double)a.T / SH::kTokens);
+    for (int sp = 1; sp <= std::min(32, std::max(1, nks / 8)); ++sp) {
+      const double c = (double)((rem * sp + cus - 1) / cus) / sp + charge * (sp - 1);
       if (c < best - 1e-9) {
         best = c;
         split = sp;
