@@ -16,9 +16,9 @@
 //    A block's waves sit side by side along W rows; a wave owns MB m-blocks
 //    of 32 rows and all 32*NB tokens of the tile, so every weight is
 //    dequantized exactly once per token tile, straight into the B-operand
-//    registers (no LDS round trip for W).  Large token counts use 8 waves
-//    (two per SIMD) of 64 rows x 128 tokens; small ones 4 waves of 128 rows
-//    x 32 tokens.
+//    registers (no LDS round trip for W).  Blocks are 8 waves (two per
+//    SIMD) of 64 rows each; a tile is 512 rows x 128 tokens for large token
+//    counts and 512 x 32 for small ones and routed experts.
 //  * Scales are fetched in 16-byte windows of 8 groups per row, once per 8
 //    groups, not 2 bytes per row per super-step.
 //  * The contraction order over k is free, so each lane half (lanes 32h ..
@@ -30,7 +30,10 @@
 //    16-byte fragment reads hit distinct banks.
 //  * Codebook in LDS (replicated for K = 256, as in the GEMV); the gathers of
 //    the next k-step are issued ahead of the current k-step's MFMAs.
-//  * Under-filled grids (few tiles) split K and add the slices atomically.
+//  * Tiles of a last, partial round of the grid (or of a grid with fewer
+//    tiles than CUs) are split along K over the CUs and their slices added
+//    atomically into a zeroed y; the number of slices weighs the rounds
+//    saved against the atomic traffic, which scales with the tokens per tile.
 //  * Routed experts: the routing kernel counts pairs per expert, scans,
 //    scatters pair ids by expert and emits a flat list of (expert, first,
 //    count) token tiles; the GEMM walks that list with gathered x rows and
