@@ -11,8 +11,15 @@ U[0.5, 1.5], x N(0, 1)) already resident in HBM.  The weights are replicated
 so the per-step rotation touches >= 1 GiB and every call streams from HBM, not
 from the 256 MB Infinity Cache.
 
+The K timed steps run as two back-to-back blocks, K decode passes then K
+prefill passes, each bracketed by HIP events on the launch stream.  Decode
+passes are captured as HIP graphs of one pass per weight replica (as a model's
+decode graph holds its layers), so graph-launch and event boundaries, which
+cost 5-15 us of idle GPU each, fall once per 8 passes rather than inside every
+pass.  Prefill passes are one graph each.
+
 Prints one JSON line.  `value` is the decode throughput (algorithmic bytes of
-codes + scales + codebook + x + y over the decode kernels' time); prefill
+codes + scales + codebook + x + y over the decode block's time); prefill
 TFLOP/s and both kernels' roofline fractions ride along.
 """
 
@@ -39,7 +46,7 @@ REPLICAS = 8
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=24)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=1024,
@@ -352,8 +359,8 @@ def main():
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
-    # Each phase of each replica is captured once as a HIP graph, so the three
-    # launches of a phase run back to back on the GPU without host gaps.  A
+    # Decode: one graph per replica (for a remainder of steps) and one graph
+    # of a pass over every replica in turn.  Prefill: one graph per replica.  A
     # burst graph of BURST gate GEMVs (and GEMMs), rotating over the replicas,
     # gives the per-launch kernel duration for the roofline.
     BURST = 2 * REPLICAS
@@ -371,6 +378,8 @@ def main():
             binding.gemm(reps[i][n], xp[n], yp[n])
     torch.cuda.synchronize()
     g_dec = [capture([(binding.gemv, reps[i][n], xd[n], yd[n]) for n in names]) for i in range(REPLICAS)]
+    g_dec_all = capture([(binding.gemv, reps[i][n], xd[n], yd[n])
+                         for i in range(REPLICAS) for n in names])
     g_pre = [capture([(binding.gemm, reps[i][n], xp[n], yp[n]) for n in names]) for i in range(REPLICAS)]
     g_burst_dec = capture([(binding.gemv, reps[i % REPLICAS]["gate"], xd["gate"], yd["gate"])
                            for i in range(BURST)])
@@ -378,27 +387,29 @@ def main():
                            for i in range(REPLICAS)])
     torch.cuda.synchronize()
 
-    def step(i, record):
-        marks = []
-        for phase, graphs in (("dec", g_dec), ("pre", g_pre)):
-            if record:
-                a, b = ev(), ev()
-                a.record()
-                graphs[i % REPLICAS].replay()
-                b.record()
-                marks.append((phase, a, b))
-            else:
-                graphs[i % REPLICAS].replay()
-        return marks
+    def decode_passes(n):
+        full, rest = divmod(n, REPLICAS)
+        for _ in range(full):
+            g_dec_all.replay()
+        for i in range(rest):
+            g_dec[i].replay()
 
-    for i in range(args.warmup):
-        step(i, False)
+    def prefill_passes(n):
+        for i in range(n):
+            g_pre[i % REPLICAS].replay()
+
+    decode_passes(args.warmup)
+    prefill_passes(args.warmup)
     torch.cuda.synchronize()
 
-    all_marks = []
+    marks = [ev() for _ in range(4)]
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        all_marks += step(args.warmup + i, True)
+    marks[0].record()
+    decode_passes(args.steps)
+    marks[1].record()
+    marks[2].record()
+    prefill_passes(args.steps)
+    marks[3].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -413,8 +424,8 @@ def main():
         torch.cuda.synchronize()
         bursts[key] = a.elapsed_time(b) * 1e-3 / count
 
-    dec_time = sum(a.elapsed_time(b) * 1e-3 for p, a, b in all_marks if p == "dec")
-    pre_time = sum(a.elapsed_time(b) * 1e-3 for p, a, b in all_marks if p == "pre")
+    dec_time = marks[0].elapsed_time(marks[1]) * 1e-3
+    pre_time = marks[2].elapsed_time(marks[3]) * 1e-3
     dec_gbps = sum(dec_bytes.values()) * args.steps / dec_time / 1e9
     pre_tflops = sum(pre_flops.values()) * args.steps / pre_time / 1e12
 

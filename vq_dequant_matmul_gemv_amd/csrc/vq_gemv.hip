@@ -29,11 +29,12 @@
 //    codes per token: above a few tokens the MFMA GEMM is the faster kernel
 //    and the C ABI's vq_gemv hands such calls to it.
 //  * Each wave keeps P row groups' loads in flight (P items of C chunks per
-//    lane, about six chunks in all) and issues a slot's next loads right after
-//    computing it: wide items (d = 2, five chunks per lane) keep one in
-//    flight, since deeper prefetch there only holds the wave at the issue of
-//    loads that cannot enter the CU's full memory queue; narrow ones (d = 4
-//    and 8) keep up to four.
+//    lane, about six chunks in all): wide items (d = 2, five chunks per lane)
+//    keep one, since a deeper ring only holds the wave at the issue of loads
+//    that cannot enter the CU's full memory queue; narrow ones (d = 4 and 8)
+//    keep up to four.  A slot's next item is loaded chunk by chunk, each
+//    chunk as soon as its codebook gathers are issued, so the loads leave
+//    during the compute without adding to the loads in flight.
 //  * Routed experts (top-k MoE): blockIdx.y is the (token, slot) pair; the
 //    block reads its expert id and points at that expert's codes and scales.
 //    An id outside [0, E) writes a zero row.
@@ -238,26 +239,34 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
   // Loads are unconditional: a chunk past the slice, a row past the block or
   // an item past the wave's list gets an out-of-range offset and reads zeros,
   // so every item issues the same loads and the in-order vmcnt waits stay exact.
-  auto load_item = [&](Chunk<B> (&dst)[C]) {
+  // An item's loads are issued chunk by chunk (load_chunk) between
+  // load_begin, which fixes the item's rows, and load_end, which moves on.
+  struct NextLoad {
+    uint32_t so;   // byte offset of the group's first row
+    bool rowok;    // this lane's row exists and the item is on the wave's list
+  };
+  auto load_begin = [&]() {
     const bool live = l_item < n_items;
-    const int g = l_g;
-    const int r = brow0 + g * R;                        // first row of the group
-    const bool rowok = live && g * R + rsub < brows;
-    const uint32_t so = live ? (uint32_t)r * row_cb : 0u;
+    const int r = brow0 + l_g * R;                      // first row of the group
+    // the row offset is wave-uniform; saying so keeps it in an SGPR (the
+    // buffer load's soffset) across the item loop
+    const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane((int)(live ? (uint32_t)r * row_cb : 0u));
+    return NextLoad{so, live && l_g * R + rsub < brows};
+  };
+  auto load_chunk = [&](Chunk<B>& dst, int j, const NextLoad& nl) {
+    const uint32_t vo = nl.rowok ? lane_vo[j] : kOutOfRange;
+    if constexpr (B == 8) {
+      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, vo, nl.so, 0));
+      dst.w[0] = v.x; dst.w[1] = v.y; dst.w[2] = v.z; dst.w[3] = v.w;
+    } else {
 #pragma unroll
-    for (int j = 0; j < C; ++j) {
-      const uint32_t vo = rowok ? lane_vo[j] : kOutOfRange;
-      if constexpr (B == 8) {
-        const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, vo, so, 0));
-        dst[j].w[0] = v.x; dst[j].w[1] = v.y; dst[j].w[2] = v.z; dst[j].w[3] = v.w;
-      } else {
-#pragma unroll
-        for (int h = 0; h < 3; ++h) {
-          const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rc, vo + 8u * h, so, 0));
-          dst[j].w[2 * h] = v.x; dst[j].w[2 * h + 1] = v.y;
-        }
+      for (int h = 0; h < 3; ++h) {
+        const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rc, vo + 8u * h, nl.so, 0));
+        dst.w[2 * h] = v.x; dst.w[2 * h + 1] = v.y;
       }
     }
+  };
+  auto load_end = [&]() {
     ++l_item;
     l_g += step_g;
     l_pass += step_p;
@@ -265,7 +274,12 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
     if (step_p != 0) set_pass_offsets(l_pass);
   };
 #pragma unroll
-  for (int k = 0; k < P; ++k) load_item(ring[k]);
+  for (int k = 0; k < P; ++k) {
+    const NextLoad nl = load_begin();
+#pragma unroll
+    for (int j = 0; j < C; ++j) load_chunk(ring[k][j], j, nl);
+    load_end();
+  }
 
   // ---- stage the small data in LDS ----
   if constexpr (LY::kReplicated) {
@@ -341,10 +355,22 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
     constexpr int S = (D == 2) ? 1 : (D == 4 ? 2 : 4);  // steps per chunk
     constexpr int SB = 16 / S;                          // codes per step
     static_assert(CPS % SB == 0, "a step lies inside one scale group");
+    //
+    // This slot's next item (u + P) is loaded chunk by chunk: once the last
+    // gather of chunk j is issued, the chunk's code registers are free and its
+    // load for the next item goes out at once.  The wave so keeps C chunk
+    // loads in flight, no more than loading whole items after the compute,
+    // but they leave during the compute rather than after it.
+    const NextLoad nl = load_begin();
     Entry<D> e[2][SB];
     auto issue = [&](int t, Entry<D> (&dst)[SB]) {
 #pragma unroll
       for (int i = 0; i < SB; ++i) dst[i] = gather<D, B>(cb_lds, rs[t / S], (t % S) * SB + i, lane_off);
+      if (t % S == S - 1) {  // kept in place: the scheduler would sink it below later waits
+        __builtin_amdgcn_sched_barrier(0);
+        load_chunk(rs[t / S], t / S, nl);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     };
     issue(0, e[0]);
     float gs[2] = {0.f, 0.f};  // two chains for ILP, restarted per scale group
@@ -371,10 +397,7 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
     }
     const float v = lane_group_sum(acc, lg);
     if (li == L - 1 && rb < brows) pieces[rb * passes + pass] = v;
-    // Only now this slot's next loads (item u + P): measured on MI355X,
-    // issuing them before the compute is slower, as the loads then wait in
-    // the CU's memory queue behind other waves' while this wave could compute.
-    load_item(rs);
+    load_end();
     g += step_g;
     pass += step_p;
     if (pass >= passes) { pass -= passes; ++g; }
