@@ -138,6 +138,27 @@ def test_gemv_wide_rows_split_into_column_slices():
         assert row_rel_err(y, ref) <= TOL
 
 
+def test_gemv_multi_pass_rows():
+    """Long rows covered in several column passes of equal width: narrower
+    than the lane tile (idle lane slots), pass counts that divide the eight
+    waves (each wave keeps one pass) and one that does not (x reloaded per
+    item)."""
+    from vq_dequant_matmul_gemv_amd import binding
+    cases = [(41, 6400, 4, 8, 64),       # 100 chunks: 2 passes of 50 on 32 lanes x 2
+             (37, 17408, 4, 8, 64),      # 272 chunks: 4 passes of 68 on 32 lanes x 3
+             (23, 17408, 2, 8, 64),      # 544 chunks: 4 passes of 136 on 32 lanes x 5
+             (29, 15360, 2, 8, 64),      # 480 chunks: 4 passes of 120 on 32 lanes x 5
+             (19, 17408, 8, 12, 128)]    # 136 chunks: 5 passes of 28 on 32 lanes x 1
+    for rows, cols, d, b, g in cases:
+        spec, arrs, w = _case(d, b, g, rows, cols, ("passes", rows, cols))
+        for T in (1, 2):
+            x = synth.activations((T, cols), "passes", rows, cols, T)
+            announce("gemv-passes", rows, cols, d, b, g, T)
+            y = binding.gemv(w, to_dev(x)).cpu().numpy()
+            ref = O.gemv_ref(arrs["codes"][0], arrs["codebook"], arrs["scales"][0], x, cols, d, b, g)
+            assert row_rel_err(y, ref) <= TOL, (rows, cols, d, T)
+
+
 def test_zero_tokens_is_a_no_op():
     import torch
     from vq_dequant_matmul_gemv_amd import binding

@@ -103,8 +103,9 @@ template <int D, int B, int G, int C, int XS, bool MOE>
 // -amdgpu-kernarg-preload-count) they arrive in SGPRs at wave launch instead
 // of after a scalar load from the argument buffer.  The rest (output,
 // routing, accumulation) is only needed later and stays in the struct.
-//   xs: x of token tok0 (dense) or x (routed); shape = nq | lanes_log2 << 16 |
-//   passes << 20; cols = spr * G.
+//   xs: x of token tok0 (dense) or x (routed); shape = nq | lanes_log2 << 12 |
+//   passes << 15 | pass width << 23 (chunks per pass, at most L * C); cols =
+//   spr * G.
 __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
     const uint32_t* __restrict__ codes_in, const uint16_t* __restrict__ cb_in,
     const uint16_t* __restrict__ scales_in, const uint16_t* __restrict__ xs, int rows, int rows_base,
@@ -127,9 +128,10 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nq = (int)(shape & 0xffffu);
-  const int lg = (int)((shape >> 16) & 0xfu);
-  const int passes = (int)(shape >> 20);
+  const int nq = (int)(shape & 0xfffu);
+  const int lg = (int)((shape >> 12) & 0x7u);
+  const int passes = (int)((shape >> 15) & 0xffu);
+  const int PW = (int)(shape >> 23);       // chunks per pass; the last pass may hold fewer
   const int cols = spr * G;
   const int wr = cols / (32 * D) * B;     // code words per row
   const int L = 1 << lg;
@@ -216,7 +218,6 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
   // ---- the code stream: work item u = (pass, group) in pass-major order ----
   const rsrc_t rc = make_rsrc(codes, (uint64_t)rows * wr * 4);
   const uint32_t row_cb = (uint32_t)wr * 4u;
-  const int LC = L * C;                                 // chunks per pass
   // items f = group * passes + pass, dealt round-robin over the waves: when
   // the wave count is a multiple of the pass count a wave keeps one pass (no
   // x reloads), and the block's waves always read neighbouring row groups.
@@ -229,10 +230,12 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
   int l_pass = wave % passes, l_g = wave / passes;  // its pass and group
   uint32_t lane_vo[C];                                  // per-lane code offsets of l_pass
   auto set_pass_offsets = [&](int pass) {
+    const int lim = min(PW, nq - pass * PW);            // chunks of this pass
 #pragma unroll
     for (int j = 0; j < C; ++j) {
-      const int q = pass * LC + j * L + li;
-      lane_vo[j] = q < nq ? (uint32_t)rsub * row_cb + (uint32_t)(q0 + q) * CB : kOutOfRange;
+      const int qp = j * L + li;                        // chunk within the pass
+      const uint32_t vo = (uint32_t)rsub * row_cb + (uint32_t)(q0 + pass * PW + qp) * CB;
+      lane_vo[j] = qp < lim ? vo : kOutOfRange;
     }
   };
   set_pass_offsets(l_pass);
@@ -323,10 +326,12 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
   auto item = [&](Chunk<B> (&rs)[C]) {
     if (pass != cur_pass) {  // x of this pass into VGPRs (zeros past the slice)
       cur_pass = pass;
+      const int lim = min(PW, nq - pass * PW);
 #pragma unroll
       for (int j = 0; j < C; ++j) {
-        const int q = pass * LC + j * L + li;
-        const bool ok = q < nq;
+        const int qp = j * L + li;
+        const int q = pass * PW + qp;
+        const bool ok = qp < lim;
         lane_sq[j] = ((uint32_t)(q0 + q) * 16u * D) / G * 2u;
         lane_ok[j] = ok ? 0xffffffffu : 0u;
 #pragma unroll
@@ -491,13 +496,16 @@ int num_cus() {
 }
 
 // Lane tiling of a slice of nq chunks: L = 1 << lg lanes per row, C chunks
-// per lane, `passes` passes.  The bytes per row group (L * C chunks per row)
-// set how much every memory round trip of a wave delivers, so the widest
-// pass wins, among tilings that leave at most a quarter of the lane-chunk
-// slots idle (idle slots cost issue slots, not bytes) -- with one exception:
-// when the pass count does not divide the wave count, a wave's items change
-// pass and reload x from LDS each time (8*d VGPRs per chunk), so a tiling
-// whose pass count divides the waves is taken at up to 3/8 idle slots.
+// per lane, `passes` passes of ceil(nq / passes) chunks each (the kernel
+// derives the same pass width).  The bytes per row group (L * C chunks per
+// row) set how much every memory round trip of a wave delivers, so the
+// widest pass wins, among tilings that leave at most a quarter of the
+// lane-chunk slots idle (idle slots cost issue slots, not bytes) -- with one
+// exception: when the pass count does not divide the wave count, a wave's
+// items change pass and reload x from LDS each time (8*d VGPRs per chunk,
+// as many LDS bytes as the item's gathers), so a tiling whose pass count
+// divides the waves -- the smallest such count the pass width allows -- is
+// taken at up to 3/8 idle slots.
 struct LaneTiling {
   int lg, C, passes;
 };
@@ -509,10 +517,14 @@ LaneTiling plan_tiling(int nq, int max_c, int waves) {
     for (int C = 1; C <= max_c; ++C)
       for (int lg = 2; lg <= 5; ++lg) {
         const int LC = C << lg;
-        const int passes = (nq + LC - 1) / LC;
-        const long slots = (long)passes * LC;
+        int passes = (nq + LC - 1) / LC;
         if (pass_rule == 0) {  // passes dividing the waves, up to 3/8 idle
-          if (waves % passes != 0 || 8 * (slots - nq) > 3 * slots) continue;
+          while (passes <= waves && waves % passes != 0) ++passes;
+          if (passes > waves) continue;
+        }
+        const long slots = (long)passes * LC;
+        if (pass_rule == 0) {
+          if (8 * (slots - nq) > 3 * slots) continue;
         } else if (4 * (slots - nq) > slots) {
           continue;
         }
@@ -540,8 +552,11 @@ LaneTiling plan_tiling(int nq, int max_c, int waves) {
 template <int D, int B, int G, int C, int XS, bool MOE>
 hipError_t gemv_launch_c(const GemvArgs& a, dim3 grid, hipStream_t s) {
   const uint16_t* xs = MOE ? a.x : a.x + (int64_t)a.tok0 * a.cols;
-  if (a.nq > 0xffff || a.lanes_log2 > 15 || a.passes > 0xfff) return hipErrorInvalidValue;
-  const uint32_t shape = (uint32_t)a.nq | ((uint32_t)a.lanes_log2 << 16) | ((uint32_t)a.passes << 20);
+  const int pw = (a.nq + a.passes - 1) / a.passes;
+  if (a.nq > 0xfff || a.lanes_log2 > 7 || a.passes > 0xff || pw > 0x1ff || pw > C << a.lanes_log2)
+    return hipErrorInvalidValue;
+  const uint32_t shape = (uint32_t)a.nq | ((uint32_t)a.lanes_log2 << 12) | ((uint32_t)a.passes << 15) |
+                         ((uint32_t)pw << 23);
   hipLaunchKernelGGL((vq_gemv_kernel<D, B, G, C, XS, MOE>), grid, dim3(kGemvThreads), 0, s, a.codes, a.codebook,
                      a.scales, xs, a.rows, a.rows_base, a.rows_extra, a.q0, a.spr, shape, a);
   return hipGetLastError();
