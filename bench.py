@@ -16,7 +16,8 @@ prefill passes, each bracketed by HIP events on the launch stream.  Decode
 passes are captured as HIP graphs of one pass per weight replica (as a model's
 decode graph holds its layers), so graph-launch and event boundaries, which
 cost 5-15 us of idle GPU each, fall once per 8 passes rather than inside every
-pass.  Prefill passes are one graph each.
+pass; a short device-side spin before the first event hides the host's
+submission of the first graph.  Prefill passes are one graph each.
 
 Prints one JSON line.  `value` is the decode throughput (algorithmic bytes of
 codes + scales + codebook + x + y over the decode block's time); prefill
@@ -404,6 +405,10 @@ def main():
 
     marks = [ev() for _ in range(4)]
     t0 = time.perf_counter()
+    # A device-side spin (~0.4 ms) ahead of the first event keeps the GPU busy
+    # while the host submits the first decode graph, so the decode block's
+    # events time the kernels, not that submission (it is in the wall time).
+    torch.cuda._sleep(1_000_000)
     marks[0].record()
     decode_passes(args.steps)
     marks[1].record()
@@ -418,6 +423,7 @@ def main():
     bursts = {}
     for key, g, count in (("dec", g_burst_dec, BURST), ("pre", g_burst_pre, REPLICAS)):
         a, b = ev(), ev()
+        torch.cuda._sleep(1_000_000)   # the GPU is busy while the graph is submitted
         a.record()
         g.replay()
         b.record()
