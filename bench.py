@@ -4,7 +4,9 @@
 One step = the whole hot path over one batch of the dense MLP trio workload
 (gate/up [17408][5120], down [5120][17408], d=2, K=256, fp16 scale per 64
 weights = 4.25 bits per weight):
-  decode : vq_gemv on gate, up, down at T = 1 token
+  decode : gate and up (which share their input) as one vq_moe_gemv launch
+           over the two-expert stack of them, ids {0, 1}; vq_gemv on down;
+           T = 1 token
   prefill: vq_gemm on gate, up, down at T = 2048 tokens
 Inputs are seeded synthetic tensors (codes uniform, codebook N(0, 0.02), scales
 U[0.5, 1.5], x N(0, 1)) already resident in HBM.  The weights are replicated
@@ -327,31 +329,71 @@ def main():
     names = ["gate", "up", "down"]
     specs = {n: wl["tensors"][n] for n in names}
     host = {n: synth.tensor(specs[n], WORKLOAD, n) for n in names}
-    base = {n: binding.VQTensor.from_host(host[n], specs[n]) for n in names}
+    sg, sd = specs["gate"], specs["down"]
+
+    # Gate and up share their input, so they are stored as one two-expert
+    # stack (per-expert codebooks) and decoded by one routed launch with ids
+    # {0, 1}; the prefill GEMMs take per-expert views of the same stack.
+    def stack_gate_up(src_gate, src_up):
+        t = [binding.VQTensor.from_host(h, sg) for h in (src_gate, src_up)]
+        return binding.VQTensor(torch.stack([t[0].codes, t[1].codes]), torch.stack([t[0].codebook, t[1].codebook]),
+                                torch.stack([t[0].scales, t[1].scales]), sg.rows, sg.cols, sg.d, sg.log2_k,
+                                sg.group, 2, True)
+
+    def expert_view(st, e):
+        return binding.VQTensor(st.codes[e], st.codebook[e], st.scales[e], st.rows, st.cols, st.d, st.log2_k,
+                                st.group)
+
+    base_gu = stack_gate_up(host["gate"], host["up"])
+    base_down = binding.VQTensor.from_host(host["down"], sd)
     reps = []
     for r in range(REPLICAS):
-        if r == 0:
-            reps.append(base)
-        else:
-            reps.append({n: binding.VQTensor(base[n].codes.clone(), base[n].codebook.clone(),
-                                             base[n].scales.clone(), specs[n].rows, specs[n].cols,
-                                             specs[n].d, specs[n].log2_k, specs[n].group)
-                         for n in names})
-    xd = {n: torch.from_numpy(synth.activations((DECODE_T, specs[n].cols), WORKLOAD, "xd", n)).to(dev)
-          for n in names}
-    xp = {n: torch.from_numpy(synth.activations((PREFILL_T, specs[n].cols), WORKLOAD, "xp", n)).to(dev)
-          for n in names}
-    yd = {n: torch.empty((DECODE_T, specs[n].rows), dtype=torch.float32, device=dev) for n in names}
+        gu = base_gu if r == 0 else binding.VQTensor(base_gu.codes.clone(), base_gu.codebook.clone(),
+                                                     base_gu.scales.clone(), sg.rows, sg.cols, sg.d, sg.log2_k,
+                                                     sg.group, 2, True)
+        down = base_down if r == 0 else binding.VQTensor(base_down.codes.clone(), base_down.codebook.clone(),
+                                                         base_down.scales.clone(), sd.rows, sd.cols, sd.d,
+                                                         sd.log2_k, sd.group)
+        reps.append({"gate_up": gu, "gate": expert_view(gu, 0), "up": expert_view(gu, 1), "down": down})
+    xd_gu = torch.from_numpy(synth.activations((DECODE_T, sg.cols), WORKLOAD, "xd", "gate_up")).to(dev)
+    xd_dn = torch.from_numpy(synth.activations((DECODE_T, sd.cols), WORKLOAD, "xd", "down")).to(dev)
+    xp_gu = torch.from_numpy(synth.activations((PREFILL_T, sg.cols), WORKLOAD, "xp", "gate_up")).to(dev)
+    xp_dn = torch.from_numpy(synth.activations((PREFILL_T, sd.cols), WORKLOAD, "xp", "down")).to(dev)
+    ids_gu = torch.tensor([[0, 1]] * DECODE_T, dtype=torch.int32, device=dev)
+    yd_gu = torch.empty((DECODE_T, 2, sg.rows), dtype=torch.float32, device=dev)
+    yd_g = torch.empty((DECODE_T, sg.rows), dtype=torch.float32, device=dev)
+    yd_dn = torch.empty((DECODE_T, sd.rows), dtype=torch.float32, device=dev)
     yp = {n: torch.empty((PREFILL_T, specs[n].rows), dtype=torch.float32, device=dev) for n in names}
     torch.cuda.synchronize()
 
+    def dec_gate_up(i):
+        binding.moe_gemv(reps[i]["gate_up"], xd_gu, ids_gu, y=yd_gu)
+
+    def dec_pass(i):
+        dec_gate_up(i)
+        binding.gemv(reps[i]["down"], xd_dn, yd_dn)
+
+    def dec_gate(i):
+        binding.gemv(reps[i]["gate"], xd_gu, yd_g)
+
+    def pre_gate(i):
+        binding.gemm(reps[i]["gate"], xp_gu, yp["gate"])
+
+    def pre_pass(i):
+        pre_gate(i)
+        binding.gemm(reps[i]["up"], xp_gu, yp["up"])
+        binding.gemm(reps[i]["down"], xp_dn, yp["down"])
+
     if args.profile_gate:
         for i in range(4):
-            binding.gemv(reps[i % REPLICAS]["gate"], xd["gate"], yd["gate"])
+            dec_gate_up(i % REPLICAS)
+        for i in range(4):
+            dec_gate(i % REPLICAS)
         for i in range(2):
-            binding.gemm(reps[i % REPLICAS]["gate"], xp["gate"], yp["gate"])
+            pre_gate(i % REPLICAS)
         torch.cuda.synchronize()
-        print("profile-gate: 4 gate GEMVs (T=1), 2 gate GEMMs (T=2048)", flush=True)
+        print("profile-gate: 4 gate+up routed GEMVs (T=1), 4 gate GEMVs (T=1), 2 gate GEMMs (T=2048)",
+              flush=True)
         return
 
     dec_bytes = {n: tensor_bytes(specs[n], DECODE_T) for n in names}
@@ -361,31 +403,29 @@ def main():
         return torch.cuda.Event(enable_timing=True)
 
     # Decode: one graph per replica (for a remainder of steps) and one graph
-    # of a pass over every replica in turn.  Prefill: one graph per replica.  A
-    # burst graph of BURST gate GEMVs (and GEMMs), rotating over the replicas,
-    # gives the per-launch kernel duration for the roofline.
+    # of a pass over every replica in turn.  Prefill: one graph per replica.
+    # Burst graphs of back-to-back launches rotating over the replicas give
+    # the per-launch kernel durations for the rooflines.
     BURST = 2 * REPLICAS
 
-    def capture(fn_calls):
+    def capture(calls):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for fn, w, x, y in fn_calls:
-                fn(w, x, y)
+            for fn, i in calls:
+                fn(i)
         return g
 
     for i in range(REPLICAS):              # warm every code path eagerly first
-        for n in names:
-            binding.gemv(reps[i][n], xd[n], yd[n])
-            binding.gemm(reps[i][n], xp[n], yp[n])
+        dec_pass(i)
+        dec_gate(i)
+        pre_pass(i)
     torch.cuda.synchronize()
-    g_dec = [capture([(binding.gemv, reps[i][n], xd[n], yd[n]) for n in names]) for i in range(REPLICAS)]
-    g_dec_all = capture([(binding.gemv, reps[i][n], xd[n], yd[n])
-                         for i in range(REPLICAS) for n in names])
-    g_pre = [capture([(binding.gemm, reps[i][n], xp[n], yp[n]) for n in names]) for i in range(REPLICAS)]
-    g_burst_dec = capture([(binding.gemv, reps[i % REPLICAS]["gate"], xd["gate"], yd["gate"])
-                           for i in range(BURST)])
-    g_burst_pre = capture([(binding.gemm, reps[i % REPLICAS]["gate"], xp["gate"], yp["gate"])
-                           for i in range(REPLICAS)])
+    g_dec = [capture([(dec_pass, i)]) for i in range(REPLICAS)]
+    g_dec_all = capture([(dec_pass, i) for i in range(REPLICAS)])
+    g_pre = [capture([(pre_pass, i)]) for i in range(REPLICAS)]
+    g_burst = {"gate_up": (capture([(dec_gate_up, i % REPLICAS) for i in range(BURST)]), BURST),
+               "gate": (capture([(dec_gate, i % REPLICAS) for i in range(BURST)]), BURST),
+               "gemm": (capture([(pre_gate, i) for i in range(REPLICAS)]), REPLICAS)}
     torch.cuda.synchronize()
 
     def decode_passes(n):
@@ -419,26 +459,30 @@ def main():
     wall = time.perf_counter() - t0
 
     # per-launch durations of the dominant kernels (inside the timed process,
-    # same stream, back-to-back launches as in the steps)
+    # same stream, back-to-back launches as in the steps): median of 5 burst
+    # replays
     bursts = {}
-    for key, g, count in (("dec", g_burst_dec, BURST), ("pre", g_burst_pre, REPLICAS)):
-        a, b = ev(), ev()
-        torch.cuda._sleep(1_000_000)   # the GPU is busy while the graph is submitted
-        a.record()
-        g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        bursts[key] = a.elapsed_time(b) * 1e-3 / count
+    for key, (g, count) in g_burst.items():
+        times = []
+        for _ in range(5):
+            a, b = ev(), ev()
+            torch.cuda._sleep(1_000_000)   # the GPU is busy while the graph is submitted
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e-3 / count)
+        bursts[key] = sorted(times)[2]
 
     dec_time = marks[0].elapsed_time(marks[1]) * 1e-3
     pre_time = marks[2].elapsed_time(marks[3]) * 1e-3
     dec_gbps = sum(dec_bytes.values()) * args.steps / dec_time / 1e9
     pre_tflops = sum(pre_flops.values()) * args.steps / pre_time / 1e12
 
-    gate_dec = bursts["dec"]
-    gate_pre = bursts["pre"]
-    achieved_gbps = dec_bytes["gate"] / gate_dec / 1e9
-    achieved_tflops = pre_flops["gate"] / gate_pre / 1e12
+    gu_bytes = dec_bytes["gate"] + dec_bytes["up"]
+    gu_gbps = gu_bytes / bursts["gate_up"] / 1e9
+    gate_gbps = dec_bytes["gate"] / bursts["gate"] / 1e9
+    gate_tflops = pre_flops["gate"] / bursts["gemm"] / 1e12
 
     out = {
         "metric": "VQ-GEMV effective HBM GB/s (% of peak) at batch 1; prefill VQ-GEMM TFLOP/s",
@@ -455,21 +499,30 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "decode_tokens": DECODE_T, "prefill_tokens": PREFILL_T,
                    "tensors": "gate,up [17408x5120]; down [5120x17408]; d=2 K=256 group=64 (4.25 bpw)",
+                   "decode_calls": "gate+up: one routed GEMV over the two-expert stack, ids {0,1}; down: GEMV",
+                   "prefill_calls": "gate, up, down: one GEMM each",
                    "weight_replicas": REPLICAS, "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * dec_gbps / HBM_PEAK_GBPS, 2),
         "decode_ms_per_step": round(dec_time / args.steps * 1e3, 4),
         "prefill": {"value": round(pre_tflops, 2), "unit": "TFLOP/s",
                     "pct_of_fp16_mfma_peak": round(100 * pre_tflops / MFMA_F16_PEAK_TFLOPS, 2),
                     "ms_per_step": round(pre_time / args.steps * 1e3, 4)},
-        "kernel_us": {"gemv_gate_T1": round(gate_dec * 1e6, 2), "gemm_gate_T2048": round(gate_pre * 1e6, 2)},
-        "roofline": {"bound": "hbm", "kernel": "vq_gemv (gate, T=1)",
-                     "achieved": round(achieved_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic("vq_gemv_kernel<2, 8, 64", GATE_TAG),
-                     "algorithmic_bytes": dec_bytes["gate"]},
+        "kernel_us": {"gemv_gate_up_T1": round(bursts["gate_up"] * 1e6, 2),
+                      "gemv_gate_T1": round(bursts["gate"] * 1e6, 2),
+                      "gemm_gate_T2048": round(bursts["gemm"] * 1e6, 2)},
+        "roofline": {"bound": "hbm", "kernel": "vq_moe_gemv over the gate+up stack (T=1, ids {0,1})",
+                     "achieved": round(gu_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic("vq_gemv_kernel<2, 8, 64, 5, 2, true>", GATE_TAG),
+                     "algorithmic_bytes": gu_bytes},
+        "roofline_single_tensor": {"bound": "hbm", "kernel": "vq_gemv (gate, T=1)",
+                                   "achieved": round(gate_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                   "frac": round(gate_gbps / HBM_PEAK_GBPS, 4),
+                                   "traffic": measured_traffic("vq_gemv_kernel<2, 8, 64, 5, 2, false>", GATE_TAG),
+                                   "algorithmic_bytes": dec_bytes["gate"]},
         "roofline_prefill": {"bound": "mfma", "kernel": "vq_gemm (gate, T=2048)",
-                             "achieved": round(achieved_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
-                             "unit": "TFLOP/s", "frac": round(achieved_tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                             "achieved": round(gate_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(gate_tflops / MFMA_F16_PEAK_TFLOPS, 4),
                              "traffic": measured_traffic("vq_gemm_kernel<2, 8, 64", GATE_TAG),
                              "algorithmic_bytes": tensor_bytes(specs["gate"], PREFILL_T)},
     }

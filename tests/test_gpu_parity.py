@@ -215,6 +215,28 @@ def test_moe_per_expert_codebooks():
         assert row_rel_err(y.reshape(-1, rows), ref.reshape(-1, rows)) <= TOL
 
 
+def test_gate_up_stack_in_one_routed_call():
+    """Two projections that share x (an MLP's gate and up), stored as a
+    two-expert stack with per-expert codebooks, run as one routed GEMV with
+    ids {0, 1}: 17408 rows each, so a block holds 136 rows (two pairs over
+    the CUs).  The outputs match the oracle and, bit for bit, two dense GEMV
+    calls on the experts (same lane tiling per row)."""
+    from vq_dequant_matmul_gemv_amd import binding
+    rows, cols = 17408, 512
+    spec, arrs, w = _case(2, 8, 64, rows, cols, ("gate-up",), experts=2, cbpe=True)
+    x = synth.activations((1, cols), "gate-up")
+    ids = np.array([[0, 1]], dtype=np.int32)
+    announce("gate-up stack", rows, cols)
+    y = binding.moe_gemv(w, to_dev(x), to_dev(ids)).cpu().numpy()
+    ref = O.moe_ref(arrs["codes"], arrs["codebook"], arrs["scales"], x, ids, cols=cols, d=2,
+                    log2_k=8, group=64, x_per_slot=False, codebook_per_expert=True)
+    assert row_rel_err(y.reshape(-1, rows), ref.reshape(-1, rows)) <= TOL
+    for e in range(2):
+        we = binding.VQTensor(w.codes[e], w.codebook[e], w.scales[e], rows, cols, 2, 8, 64)
+        ye = binding.gemv(we, to_dev(x)).cpu().numpy()
+        assert np.array_equal(ye[0], y[0, e]), e
+
+
 def test_moe_grouped_equals_per_slot_bit_identical_on_exact_inputs():
     """Grouping by expert does not change any row: on exact-arithmetic
     inputs grouped GEMM, per-slot GEMV and the oracle agree bit for bit."""

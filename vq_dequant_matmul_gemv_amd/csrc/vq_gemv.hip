@@ -72,7 +72,7 @@ struct GemvArgs {
 constexpr int kGemvWaves = 8;                  // two waves per SIMD
 constexpr int kGemvThreads = 64 * kGemvWaves;
 constexpr int kGemvXMaxBytes = 40 * 1024;      // largest x slice in LDS
-constexpr int kGemvScaleBytes = 16 * 1024;     // the block's scales
+constexpr int kGemvScaleBytes = 24 * 1024;     // the block's scale rows (136 rows of 80 groups fit)
 constexpr int kGemvPieces = 4096;              // per-(row, pass) partial sums
 
 // Chunks per lane a pass can hold in VGPRs: x costs 8*d VGPRs per chunk.
