@@ -154,6 +154,11 @@ vq_status vq_gemm(const vq_tensor *w, const uint16_t *x, int32_t T, float *y, vo
  *   y: device [T][top_k][rows] fp32, 16-byte aligned;  T >= 0, top_k >= 1,
  *   T * top_k <= 65535 (larger batches belong to vq_moe_gemm), x at most
  *   2 GiB - 1 bytes.
+ * Dense projections that share their input (an MLP's gate and up) can be
+ * stored as an expert stack (codebook_per_expert = 1 keeps each tensor's own
+ * codebook) and run by this call in one launch, with expert_ids {0, 1, ...}
+ * in every token: the same results as one vq_gemv per tensor, bit for bit,
+ * at one launch's fixed cost.
  */
 vq_status vq_moe_gemv(const vq_tensor *w, const uint16_t *x, int32_t x_per_slot,
                       const int32_t *expert_ids, int32_t T, int32_t top_k, float *y,
