@@ -159,6 +159,25 @@ def test_gemv_multi_pass_rows():
             assert row_rel_err(y, ref) <= TOL, (rows, cols, d, T)
 
 
+def test_gemv_partial_last_rounds():
+    """Blocks whose row groups leave a partial last round over the 8 waves
+    (32 lanes x 5 chunks per row, 2-row groups): 2 and 7 groups left over
+    (the latter with a 1-row last group), no whole round, an exact round."""
+    from vq_dequant_matmul_gemv_amd import binding
+    cases = [(5000, 5120),     # 19-20 rows per block: 10 groups, 2 left
+             (7500, 5120),     # 29-30 rows: 15 groups, 7 left
+             (2600, 5120),     # 10-11 rows: 5-6 groups, no whole round
+             (4096, 5120)]     # 16 rows: 8 groups, none left
+    for rows, cols in cases:
+        spec, arrs, w = _case(2, 8, 64, rows, cols, ("rounds", rows, cols))
+        for T in (1, 2):
+            x = synth.activations((T, cols), "rounds", rows, cols, T)
+            announce("gemv-rounds", rows, cols, T)
+            y = binding.gemv(w, to_dev(x)).cpu().numpy()
+            ref = O.gemv_ref(arrs["codes"][0], arrs["codebook"], arrs["scales"][0], x, cols, 2, 8, 64)
+            assert row_rel_err(y, ref) <= TOL, (rows, cols, T)
+
+
 def test_zero_tokens_is_a_no_op():
     import torch
     from vq_dequant_matmul_gemv_amd import binding
@@ -215,15 +234,16 @@ def test_moe_per_expert_codebooks():
         assert row_rel_err(y.reshape(-1, rows), ref.reshape(-1, rows)) <= TOL
 
 
-def test_gate_up_stack_in_one_routed_call():
+@pytest.mark.parametrize("rows,cols", [(17408, 512), (4352, 5120)])
+def test_gate_up_stack_in_one_routed_call(rows, cols):
     """Two projections that share x (an MLP's gate and up), stored as a
     two-expert stack with per-expert codebooks, run as one routed GEMV with
-    ids {0, 1}: 17408 rows each, so a block holds 136 rows (two pairs over
-    the CUs).  The outputs match the oracle and, bit for bit, two dense GEMV
-    calls on the experts (same lane tiling per row)."""
+    ids {0, 1}: at 17408 rows a block holds 136 rows (two pairs over the
+    CUs); at 4352 x 5120 the blocks' row groups leave a partial last round.
+    The outputs match the oracle and, bit for bit, two dense GEMV calls on
+    the experts (same lane tiling per row)."""
     from vq_dequant_matmul_gemv_amd import binding
-    rows, cols = 17408, 512
-    spec, arrs, w = _case(2, 8, 64, rows, cols, ("gate-up",), experts=2, cbpe=True)
+    spec, arrs, w = _case(2, 8, 64, rows, cols, ("gate-up", rows, cols), experts=2, cbpe=True)
     x = synth.activations((1, cols), "gate-up")
     ids = np.array([[0, 1]], dtype=np.int32)
     announce("gate-up stack", rows, cols)
