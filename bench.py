@@ -194,6 +194,7 @@ def configs_report(only=""):
         per = []
         for _ in range(reps):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(1_000_000)   # the GPU is busy while the graph is submitted
             a.record()
             g.replay()
             b.record()
@@ -234,6 +235,27 @@ def configs_report(only=""):
         del reps
         torch.cuda.empty_cache()
 
+    def stacked_pair(wl, name, spec, keys):
+        """Two tensors sharing x (gate and up), stacked as two experts with
+        per-expert codebooks, in one vq_moe_gemv launch with ids {0, 1}."""
+        t = [binding.VQTensor.from_host(synth.tensor(spec, *k), spec, device=dev) for k in keys]
+        base = binding.VQTensor(torch.stack([t[0].codes, t[1].codes]), torch.stack([t[0].codebook, t[1].codebook]),
+                                torch.stack([t[0].scales, t[1].scales]), spec.rows, spec.cols, spec.d,
+                                spec.log2_k, spec.group, 2, True)
+        del t
+        nbytes = 2 * tensor_bytes(spec, 1)
+        reps = [base] + [binding.VQTensor(base.codes.clone(), base.codebook.clone(), base.scales.clone(),
+                                          spec.rows, spec.cols, spec.d, spec.log2_k, spec.group, 2, True)
+                         for _ in range(int(max(0, -(-1.1e9 // nbytes) - 1)))]
+        x = torch.from_numpy(synth.activations((1, spec.cols), *keys[0], "x", 1)).to(dev)
+        ids = torch.tensor([[0, 1]], dtype=torch.int32, device=dev)
+        y = torch.empty((1, 2, spec.rows), dtype=torch.float32, device=dev)
+        calls = [(lambda w=reps[i % len(reps)]: binding.moe_gemv(w, x, ids, y=y)) for i in range(16)]
+        us = timed(calls)
+        row(wl, name, "vq_moe_gemv", 1, us, nbytes, 2.0 * 2 * spec.rows * spec.cols)
+        del reps
+        torch.cuda.empty_cache()
+
     def routed(wl, name, spec, top_k, Ts, x_per_slot, key):
         host = synth.tensor(spec, *key)
         per_expert = spec.rows * spec.words * 4 + spec.rows * (spec.cols // spec.group) * 2
@@ -268,6 +290,9 @@ def configs_report(only=""):
     wl = "dense_mlp_5120x17408_d2k256"
     for n in ("gate", "up", "down") if keep(wl) else ():
         dense(wl, n, W[wl]["tensors"][n], [1], [2048], (wl, n))
+    if keep(wl):
+        stacked_pair(wl, "gate+up (two-expert stack, ids {0,1})", W[wl]["tensors"]["gate"],
+                     ((wl, "gate"), (wl, "up")))
     wl = "moe_e256_4096x1024_d4k256"
     for n in ("gate", "down") if keep(wl) else ():
         routed(wl, n, W[wl]["tensors"][n], W[wl]["top_k"], (1, 1024), n == "down", (wl, n))
