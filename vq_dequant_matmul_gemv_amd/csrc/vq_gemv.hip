@@ -506,13 +506,20 @@ int num_cus() {
 // as many LDS bytes as the item's gathers), so a tiling whose pass count
 // divides the waves -- the smallest such count the pass width allows -- is
 // taken at up to 3/8 idle slots.
+// For d >= 4 the kernel is bound by its gathers and dot products, not by HBM,
+// and idle slots still gather and multiply: among the tilings whose pass
+// count divides the waves it takes the most useful chunks per item (C times
+// the pass width over L*C), then the fewest idle slots, then the fewest
+// passes -- e.g. 64 chunks run on 32 lanes x 2 rather than 32 x 3 (a third
+// of the slots idle), the same bytes per item.
 struct LaneTiling {
   int lg, C, passes;
 };
 
-LaneTiling plan_tiling(int nq, int max_c, int waves) {
+LaneTiling plan_tiling(int nq, int max_c, int waves, bool cu_bound) {
   LaneTiling best{2, 1, (nq + 3) / 4};
   int best_lc = 0;
+  double best_useful = -1.0, best_idle = 2.0;
   for (int pass_rule = 0; pass_rule < 2 && best_lc == 0; ++pass_rule)
     for (int C = 1; C <= max_c; ++C)
       for (int lg = 2; lg <= 5; ++lg) {
@@ -528,7 +535,22 @@ LaneTiling plan_tiling(int nq, int max_c, int waves) {
         } else if (4 * (slots - nq) > slots) {
           continue;
         }
-        if (LC > best_lc || (LC == best_lc && lg > best.lg)) {
+        if (pass_rule == 0 && cu_bound) {
+          const int pw = (nq + passes - 1) / passes;
+          const double useful = (double)C * pw / LC;     // useful chunks per lane per item
+          const double idle = (double)(slots - nq) / slots;
+          const bool better = useful > best_useful + 1e-9 ||
+                              (useful > best_useful - 1e-9 &&
+                               (idle < best_idle - 1e-9 ||
+                                (idle < best_idle + 1e-9 &&
+                                 (passes < best.passes || (passes == best.passes && lg > best.lg)))));
+          if (best_lc == 0 || better) {
+            best = LaneTiling{lg, C, passes};
+            best_lc = LC;
+            best_useful = useful;
+            best_idle = idle;
+          }
+        } else if (LC > best_lc || (LC == best_lc && lg > best.lg)) {
           best = LaneTiling{lg, C, passes};
           best_lc = LC;
         }
@@ -591,7 +613,7 @@ hipError_t gemv_run(GemvArgs a, int P, int ycount, hipStream_t s) {
     a.q0 = sl * per_slice;
     a.nq = std::min(per_slice, P - a.q0);
     a.accumulate = sl > 0;
-    const LaneTiling t = plan_tiling(a.nq, gemv_max_c(D), kGemvWaves);
+    const LaneTiling t = plan_tiling(a.nq, gemv_max_c(D), kGemvWaves, D >= 4);
     a.lanes_log2 = t.lg;
     a.passes = t.passes;
     const int64_t by_scales = std::max<int64_t>(1, (kGemvScaleBytes - 16) / (2 * (int64_t)a.spr));
