@@ -14,7 +14,8 @@
 //    holding C sixteen-code chunks of the row (chunks li, li + L, ... of the
 //    pass), so one load instruction reads a contiguous run of every row of the
 //    group and all 64 lanes are busy.  A row longer than L*C chunks is covered
-//    in several passes whose partial sums meet in LDS.
+//    in several passes of equal width whose partial sums meet in LDS; a pass
+//    count dividing the waves lets every wave keep one pass (and its x).
 //  * Everything small is staged once per block, before any compute: the x
 //    columns of the launch, the block's scales and the codebook (replicated
 //    for K = 256 so that a lane's gather bank depends only on its lane id).
@@ -37,7 +38,8 @@
 //    during the compute without adding to the loads in flight.
 //  * Routed experts (top-k MoE): blockIdx.y is the (token, slot) pair; the
 //    block reads its expert id and points at that expert's codes and scales.
-//    An id outside [0, E) writes a zero row.
+//    An id outside [0, E) writes a zero row.  Dense projections sharing x
+//    (gate and up) run the same way as a two-expert stack in one launch.
 
 #include "vq_device.h"
 #include "vq_kernels.h"
