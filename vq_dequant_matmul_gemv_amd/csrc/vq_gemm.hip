@@ -22,9 +22,11 @@
 //  * Scales are fetched in 16-byte windows of 8 groups per row, once per 8
 //    groups, not 2 bytes per row per super-step.
 //  * The contraction order over k is free, so each lane half (lanes 32h ..
-//    32h+31) takes a contiguous run of CG columns per "super-step" (CG = 32,
-//    or 64 for d = 8): a lane's codes for one super-step are one small
-//    contiguous load and its x slices are contiguous.
+//    32h+31) takes a contiguous run of CG columns per "super-step" (CG = 32
+//    for d = 2, 64 for d = 4 and 8: half as many barriers and x stages per
+//    column where the format's column alignment allows it): a lane's codes
+//    for one super-step are one small contiguous load and its x slices are
+//    contiguous.
 //  * x tiles (32*NB tokens x 2*CG columns) go through LDS, double-buffered,
 //    one barrier per super-step; token rows are padded by 16 bytes so the
 //    16-byte fragment reads hit distinct banks.
@@ -166,7 +168,7 @@ __device__ __forceinline__ uint32_t pick16(u32x4 v, int pos) {
 template <int D, int B, int G, class SH, bool MOE>
 __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
   using L = CodebookLayout<D, B>;
-  constexpr int CG = (D == 8) ? 64 : 32;  // columns per lane half per super-step
+  constexpr int CG = (D >= 4) ? 64 : 32;  // columns per lane half per super-step
   constexpr int S = CG / 8;               // k-steps of 16 (8 per half) per super-step
   constexpr int NCL = CG / D;             // codes per lane per super-step
   constexpr int SS = 2 * CG;              // columns per super-step
