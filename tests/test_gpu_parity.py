@@ -257,6 +257,24 @@ def test_gate_up_stack_in_one_routed_call(rows, cols):
         assert np.array_equal(ye[0], y[0, e]), e
 
 
+def test_moe_gemm_more_experts_than_lds_counters():
+    """8200 experts: the routing kernel keeps its per-expert counters in the
+    workspace rather than in LDS (which holds 8192)."""
+    from vq_dequant_matmul_gemv_amd import binding
+    E, rows, cols, top_k, T = 8200, 32, 64, 4, 40
+    spec, arrs, w = _case(2, 8, 64, rows, cols, ("moe-many",), experts=E)
+    ids = synth.rng("ids-many").integers(0, E, size=(T, top_k)).astype(np.int32)
+    ids[0, :] = 17                      # a hot expert with several slots
+    ids[1, 2] = -1                      # skipped slot
+    x = synth.activations((T, cols), "moe-many")
+    announce("moe-many-experts", E)
+    y = binding.moe_gemm(w, to_dev(x), to_dev(ids)).cpu().numpy()
+    ref = O.moe_ref(arrs["codes"], arrs["codebook"], arrs["scales"], x, ids, cols=cols, d=2,
+                    log2_k=8, group=64, x_per_slot=False)
+    assert np.all(y[1, 2] == 0)
+    assert row_rel_err(y.reshape(-1, rows), ref.reshape(-1, rows)) <= TOL
+
+
 def test_moe_grouped_equals_per_slot_bit_identical_on_exact_inputs():
     """Grouping by expert does not change any row: on exact-arithmetic
     inputs grouped GEMM, per-slot GEMV and the oracle agree bit for bit."""

@@ -478,17 +478,21 @@ struct RouteArgs {
   int npairs, num_experts, rows, tile_tokens, max_tiles;
 };
 
-__global__ __launch_bounds__(1024) void vq_route_kernel(RouteArgs a) {
+// Experts whose counters fit in LDS (two int32 per expert); more experts use
+// the workspace copies.  Counters in LDS matter: with skewed routing hundreds
+// of pairs add to one hot expert's counter, and global atomics on one address
+// serialize at L2 (tens of microseconds per call), LDS atomics do not.
+constexpr int kRouteLdsExperts = 8192;
+
+template <bool kLds>
+__device__ __forceinline__ void route_pairs(const RouteArgs& a, int32_t* counts, int32_t* fill, int32_t* part) {
   const int E = a.num_experts;
-  int32_t* counts = a.ws;
-  int32_t* offsets = counts + E;
-  int32_t* fill = offsets + E;
-  int32_t* tbase = fill + E;
+  int32_t* offsets = a.ws + E;
+  int32_t* tbase = a.ws + 3 * E;
   int32_t* n_tiles = tbase + E;
   int32_t* pairs = a.ws + ((4 * E + 1 + 3) & ~3);
   int32_t* tiles = pairs + ((a.npairs + 3) & ~3);
   const int tid = threadIdx.x, nt = blockDim.x;
-  __shared__ int32_t part[1024];
 
   for (int e = tid; e < E; e += nt) { counts[e] = 0; fill[e] = 0; }
   __syncthreads();
@@ -503,7 +507,6 @@ __global__ __launch_bounds__(1024) void vq_route_kernel(RouteArgs a) {
   const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
   int sc = 0, st = 0;
   for (int e = e0; e < e1; ++e) { sc += counts[e]; st += (counts[e] + a.tile_tokens - 1) / a.tile_tokens; }
-  // block scan over threads (two values packed: counts < 2^20 per block? use two passes)
   part[tid] = sc;
   __syncthreads();
   for (int off = 1; off < nt; off <<= 1) {
@@ -548,6 +551,16 @@ __global__ __launch_bounds__(1024) void vq_route_kernel(RouteArgs a) {
       float* yr = a.y + (int64_t)p * a.rows;  // skipped slot: zero row
       for (int r = 0; r < a.rows; ++r) yr[r] = 0.f;
     }
+  }
+}
+
+__global__ __launch_bounds__(1024) void vq_route_kernel(RouteArgs a) {
+  __shared__ int32_t part[1024];
+  __shared__ int32_t lds_counts[kRouteLdsExperts], lds_fill[kRouteLdsExperts];
+  if (a.num_experts <= kRouteLdsExperts) {
+    route_pairs<true>(a, lds_counts, lds_fill, part);
+  } else {
+    route_pairs<false>(a, a.ws, a.ws + 2 * a.num_experts, part);
   }
 }
 
