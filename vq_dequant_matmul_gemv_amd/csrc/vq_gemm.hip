@@ -507,26 +507,29 @@ __device__ __forceinline__ void route_pairs(const RouteArgs& a, int32_t* counts,
   const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
   int sc = 0, st = 0;
   for (int e = e0; e < e1; ++e) { sc += counts[e]; st += (counts[e] + a.tile_tokens - 1) / a.tile_tokens; }
-  part[tid] = sc;
-  __syncthreads();
-  for (int off = 1; off < nt; off <<= 1) {
-    const int v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  // Both scans at once: inclusive within each wave by shuffles, then over
+  // the (at most 16) wave totals by the first wave; two barriers in all.
+  const int lane = tid & 63, wid = tid >> 6, nw = nt >> 6;
+  int ic = sc, it = st;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int c = __shfl_up(ic, off, 64), t = __shfl_up(it, off, 64);
+    if (lane >= off) { ic += c; it += t; }
   }
-  int run_c = part[tid] - sc;
+  if (lane == 63) { part[wid] = ic; part[32 + wid] = it; }
   __syncthreads();
-  part[tid] = st;
-  __syncthreads();
-  for (int off = 1; off < nt; off <<= 1) {
-    const int v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  if (wid == 0) {
+    const int wc = lane < nw ? part[lane] : 0, wt = lane < nw ? part[32 + lane] : 0;
+    int jc = wc, jt = wt;
+    for (int off = 1; off < 32; off <<= 1) {
+      const int c = __shfl_up(jc, off, 64), t = __shfl_up(jt, off, 64);
+      if (lane >= off) { jc += c; jt += t; }
+    }
+    if (lane < nw) { part[64 + lane] = jc - wc; part[96 + lane] = jt - wt; }  // exclusive per wave
+    if (lane == nw - 1) *n_tiles = jt;
   }
-  int run_t = part[tid] - st;
-  if (tid == nt - 1) *n_tiles = part[tid];
+  __syncthreads();
+  int run_c = part[64 + wid] + ic - sc;
+  int run_t = part[96 + wid] + it - st;
   for (int e = e0; e < e1; ++e) {
     offsets[e] = run_c;
     tbase[e] = run_t;
