@@ -123,6 +123,23 @@ def test_dense_shapes_and_tokens(fn):
             assert row_rel_err(y, ref) <= TOL, (rows, cols, T)
 
 
+@pytest.mark.parametrize("b,g", [(8, 64), (8, 128), (12, 64), (12, 128)])
+def test_gemm_d2_thin_tiles_both_super_step_lengths(b, g):
+    """d = 2 thin tiles (T <= 32) take 128-column super-steps when the
+    columns are a multiple of 128 and 64-column ones otherwise (possible only
+    with 64-weight groups); against the oracle, several row tiles and a
+    ragged token count."""
+    from vq_dequant_matmul_gemv_amd import binding
+    for rows, cols in ((600, 1024), (600, 1088 if g == 64 else 1280)):
+        spec, arrs, w = _case(2, b, g, rows, cols, ("thin", b, g, cols))
+        for T in (1, 7, 32):
+            x = synth.activations((T, cols), "thin", b, g, cols, T)
+            announce("gemm-thin", b, g, rows, cols, T)
+            y = binding.gemm(w, to_dev(x)).cpu().numpy()
+            ref = O.gemv_ref(arrs["codes"][0], arrs["codebook"], arrs["scales"][0], x, cols, 2, b, g)
+            assert row_rel_err(y, ref) <= TOL, (b, g, cols, T)
+
+
 def test_gemv_wide_rows_split_into_column_slices():
     """More than 1024 16-code chunks per row: the GEMV runs column slices
     and accumulates them."""

@@ -23,8 +23,8 @@
 //    groups, not 2 bytes per row per super-step.
 //  * The contraction order over k is free, so each lane half (lanes 32h ..
 //    32h+31) takes a contiguous run of CG columns per "super-step" (CG = 32
-//    for d = 2, 64 for d = 4 and 8: half as many barriers and x stages per
-//    column where the format's column alignment allows it): a lane's codes
+//    for d = 2, 64 for d = 4 and 8, and for d = 2 thin tiles whose columns
+//    are a multiple of 128: half as many barriers and x stages per column): a lane's codes
 //    for one super-step are one small contiguous load and its x slices are
 //    contiguous.
 //  * x tiles (32*NB tokens x 2*CG columns) go through LDS, double-buffered,
@@ -60,9 +60,12 @@ struct LaneCodes {
 template <int NCL, int B>
 __device__ __forceinline__ void load_lane_codes(LaneCodes<NCL, B>& c, rsrc_t r, uint32_t off) {
   constexpr int W = LaneCodes<NCL, B>::kWords;
-  if constexpr (W == 4) {
-    u32x4 v = buf_load_b128(r, off);
-    c.w[0] = v.x; c.w[1] = v.y; c.w[2] = v.z; c.w[3] = v.w;
+  if constexpr (W % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < W / 4; ++q) {
+      u32x4 v = buf_load_b128(r, off + 16u * q);
+      c.w[4 * q] = v.x; c.w[4 * q + 1] = v.y; c.w[4 * q + 2] = v.z; c.w[4 * q + 3] = v.w;
+    }
   } else if constexpr (W == 2) {
     u32x2 v = buf_load_b64(r, off);
     c.w[0] = v.x; c.w[1] = v.y;
@@ -157,6 +160,12 @@ struct GemmShape {
   static constexpr int kTokens = 32 * NB;         // tokens per block tile
 };
 
+// Columns per lane half per super-step (a super-step is twice that): 64 for
+// d = 4 and 8, whose rows are multiples of 128 (256) columns; for d = 2 (rows
+// multiples of 64) 32, or 64 in the wide variant, which the host picks for
+// thin tiles when the columns are a multiple of 128.
+__host__ __device__ constexpr int gemm_cg(int D, bool wide) { return (D >= 4 || wide) ? 64 : 32; }
+
 // 16-bit element `pos` (0..7) of a 16-byte window.
 __device__ __forceinline__ uint32_t pick16(u32x4 v, int pos) {
   const uint32_t lo = (pos & 2) ? v.y : v.x;
@@ -165,10 +174,10 @@ __device__ __forceinline__ uint32_t pick16(u32x4 v, int pos) {
   return (pos & 1) ? d >> 16 : d & 0xffffu;
 }
 
-template <int D, int B, int G, class SH, bool MOE>
+template <int D, int B, int G, class SH, bool MOE, bool WIDE>
 __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
   using L = CodebookLayout<D, B>;
-  constexpr int CG = (D >= 4) ? 64 : 32;  // columns per lane half per super-step
+  constexpr int CG = gemm_cg(D, WIDE);    // columns per lane half per super-step
   constexpr int S = CG / 8;               // k-steps of 16 (8 per half) per super-step
   constexpr int NCL = CG / D;             // codes per lane per super-step
   constexpr int SS = 2 * CG;              // columns per super-step
@@ -345,7 +354,8 @@ __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
   // registers and run the MFMAs against the x tile in LDS buffer `buf`.  The
   // codebook gathers of k-step s + 1 are issued before the arithmetic of
   // k-step s, so their LDS latency overlaps the MFMAs.  Every super-step is
-  // whole: the API requires cols % (32 d) == 0 and SS divides 32 d.
+  // whole: the API requires cols % (32 d) == 0 and SS divides 32 d (the wide
+  // d = 2 variant runs only when cols % 128 == 0).
   auto compute = [&](int buf, const LaneCodes<NCL, B> (&cc)[MB], const uint16_t (&sc)[MB]) {
     const uint8_t* xb = xbuf + buf * (WN * XROW);
     half2_t s2[MB];
@@ -581,9 +591,21 @@ constexpr int kMoeTileTokens = GemmMoe::kTokens;
 
 int max_tiles_for(int npairs, int E) { return (npairs + kMoeTileTokens - 1) / kMoeTileTokens + E; }
 
+// d = 2 thin tiles (32 tokens) take 128-column super-steps when the columns
+// allow: half the barriers and x stages per column, 6-10 % faster there; the
+// 128-token tiles gain about 1 % and keep 64.
+template <int D, class SH>
+bool gemm_wide(int cols) { return D == 2 && SH::kTokens <= 32 && cols % 128 == 0; }
+
 template <int D, int B, int G, class SH, bool MOE>
 hipError_t gemm_launch(const GemmArgs& a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((vq_gemm_kernel<D, B, G, SH, MOE>), grid, dim3(SH::kThreads), 0, s, a);
+  if constexpr (D == 2 && SH::kTokens <= 32) {
+    if (gemm_wide<D, SH>(a.cols)) {
+      hipLaunchKernelGGL((vq_gemm_kernel<D, B, G, SH, MOE, true>), grid, dim3(SH::kThreads), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((vq_gemm_kernel<D, B, G, SH, MOE, false>), grid, dim3(SH::kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -622,21 +644,23 @@ hipError_t gemm_dense(GemmArgs a, hipStream_t s) {
   a.n_row_tiles = (a.rows + SH::kRows - 1) / SH::kRows;
   a.n_tok_tiles = (a.T + SH::kTokens - 1) / SH::kTokens;
   const int tiles = a.n_row_tiles * a.n_tok_tiles;
-  const int nks = (a.cols + (D == 8 ? 128 : 64) - 1) / (D == 8 ? 128 : 64);
+  // each K slice keeps at least 512 columns (1024 for d = 8), whatever the
+  // super-step length
+  const int max_split = std::max(1, a.cols / (D == 8 ? 1024 : 512));
   const int cus = num_cus();
   // Whole rounds of tiles run as whole tiles; the tiles of a last, partial
   // round are split along K over the CUs and added atomically into a zeroed
   // y (their fp32 addition order then varies between runs).
   // The split minimises the partial round's time in tile rounds,
   // ceil(rem * split / cus) / split, plus a small charge per extra slice for
-  // the atomic traffic; each slice keeps at least 8 super-steps.
+  // the atomic traffic.
   int full = (tiles / cus) * cus, rem = tiles - full, split = 1;
   if (rem > 0) {
     double best = 1e30;
     // the charge per slice scales with the tokens of a tile: the atomic adds
     // are T x rows per slice, negligible next to the weight stream at small T
     const double charge = 0.03 * std::min(1.0, (double)a.T / SH::kTokens);
-    for (int sp = 1; sp <= std::min(32, std::max(1, nks / 8)); ++sp) {
+    for (int sp = 1; sp <= std::min(32, max_split); ++sp) {
       const double c = (double)((rem * sp + cus - 1) / cus) / sp + charge * (sp - 1);
       if (c < best - 1e-9) {
         best = c;
