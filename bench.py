@@ -235,6 +235,20 @@ def configs_report(only=""):
         del reps
         torch.cuda.empty_cache()
 
+    def dequant_row(wl, name, spec, key):
+        """vq_dequant of the whole matrix: bytes = codes + scales + codebook
+        read + the fp16 weights written."""
+        host = synth.tensor(spec, *key)
+        nbytes = spec.rows * spec.words * 4 + spec.rows * (spec.cols // spec.group) * 2 + spec.k * spec.d * 2 \
+            + spec.rows * spec.cols * 2
+        reps = replicas(spec, host, nbytes)
+        out_w = torch.empty((spec.rows, spec.cols), dtype=torch.float16, device=dev)
+        calls = [(lambda w=reps[i % len(reps)]: binding.dequant(w, out=out_w)) for i in range(max(8, len(reps)))]
+        us = timed(calls)
+        row(wl, name, "vq_dequant", "-", us, nbytes, 0.0)
+        del reps
+        torch.cuda.empty_cache()
+
     def stacked_pair(wl, name, spec, keys):
         """Two tensors sharing x (gate and up), stacked as two experts with
         per-expert codebooks, in one vq_moe_gemv launch with ids {0, 1}."""
@@ -293,6 +307,7 @@ def configs_report(only=""):
     if keep(wl):
         stacked_pair(wl, "gate+up (two-expert stack, ids {0,1})", W[wl]["tensors"]["gate"],
                      ((wl, "gate"), (wl, "up")))
+        dequant_row(wl, "gate", W[wl]["tensors"]["gate"], (wl, "gate"))
     wl = "moe_e256_4096x1024_d4k256"
     for n in ("gate", "down") if keep(wl) else ():
         routed(wl, n, W[wl]["tensors"][n], W[wl]["top_k"], (1, 1024), n == "down", (wl, n))
@@ -305,6 +320,8 @@ def configs_report(only=""):
     for n in ("A", "B") if keep(wl) else ():
         Ts = W[wl]["tokens"]
         dense(wl, n, W[wl]["tensors"][n], Ts, Ts, (wl, n))
+    if keep(wl):
+        dequant_row(wl, "A", W[wl]["tensors"]["A"], (wl, "A"))
     if only:
         print("\n".join(out), flush=True)
         return
