@@ -270,6 +270,38 @@ def configs_report(only=""):
         del reps
         torch.cuda.empty_cache()
 
+    def routed_gate_up(wl, spec, top_k, key_g, key_u):
+        """Routed gate and up at T = 1 in one vq_moe_gemv: experts 2e / 2e + 1
+        of one stack (per-expert codebooks), ids 2e, 2e + 1 per slot.  Bytes
+        as for the two separate calls."""
+        tg = binding.VQTensor.from_host(synth.tensor(spec, *key_g), spec, device=dev)
+        tu = binding.VQTensor.from_host(synth.tensor(spec, *key_u), spec, device=dev)
+        E = spec.experts
+        base = binding.VQTensor(torch.stack([tg.codes, tu.codes], 1).reshape(2 * E, spec.rows, -1).contiguous(),
+                                torch.stack([tg.codebook, tu.codebook]).repeat(E, 1, 1).contiguous(),
+                                torch.stack([tg.scales, tu.scales], 1).reshape(2 * E, spec.rows, -1).contiguous(),
+                                spec.rows, spec.cols, spec.d, spec.log2_k, spec.group, 2 * E, True)
+        del tg, tu
+        per_expert = spec.rows * spec.words * 4 + spec.rows * (spec.cols // spec.group) * 2
+        reps = [base] + [binding.VQTensor(base.codes.clone(), base.codebook.clone(), base.scales.clone(),
+                                          spec.rows, spec.cols, spec.d, spec.log2_k, spec.group, 2 * E, True)
+                         for _ in range(int(max(0, min(7, -(-1.1e9 // (per_expert * 2 * E)) - 1))))]
+        draws = [synth.zipf_routing(1, E, top_k, *key_g, "ids", 1, r) for r in range(16)]
+        ids = [torch.from_numpy(np.stack([2 * d, 2 * d + 1], -1).reshape(1, 2 * top_k).astype(np.int32)).to(dev)
+               for d in draws]
+        x = torch.from_numpy(synth.activations((1, spec.cols), *key_g, "x", 1)).to(dev)
+        y = torch.empty((1, 2 * top_k, spec.rows), dtype=torch.float32, device=dev)
+        calls, nbytes = [], 0
+        for i in range(16):
+            calls.append(lambda w=reps[i % len(reps)], d=ids[i]: binding.moe_gemv(w, x, d, y=y))
+            hit = len(np.unique(draws[i]))
+            nbytes += 2 * (hit * per_expert + spec.k * spec.d * 2 + x.numel() * 2 + top_k * spec.rows * 4 + top_k * 4)
+        us = timed(calls)
+        row(wl, "gate+up (experts 2e / 2e+1 of one stack, top-16)", "vq_moe_gemv", 1, us, nbytes / 16,
+            2.0 * 2 * top_k * spec.rows * spec.cols)
+        del reps
+        torch.cuda.empty_cache()
+
     def routed(wl, name, spec, top_k, Ts, x_per_slot, key):
         host = synth.tensor(spec, *key)
         per_expert = spec.rows * spec.words * 4 + spec.rows * (spec.cols // spec.group) * 2
@@ -311,6 +343,8 @@ def configs_report(only=""):
     wl = "moe_e256_4096x1024_d4k256"
     for n in ("gate", "down") if keep(wl) else ():
         routed(wl, n, W[wl]["tensors"][n], W[wl]["top_k"], (1, 1024), n == "down", (wl, n))
+    if keep(wl):
+        routed_gate_up(wl, W[wl]["tensors"]["gate"], W[wl]["top_k"], (wl, "gate"), (wl, "up"))
     wl = "moe_mixed_tier_e256_2048x512"
     for tier in ("T1", "T2", "T3") if keep(wl) else ():
         for idx, n in ((0, "gate"), (2, "down")):

@@ -158,7 +158,10 @@ vq_status vq_gemm(const vq_tensor *w, const uint16_t *x, int32_t T, float *y, vo
  * stored as an expert stack (codebook_per_expert = 1 keeps each tensor's own
  * codebook) and run by this call in one launch, with expert_ids {0, 1, ...}
  * in every token: the same results as one vq_gemv per tensor, bit for bit,
- * at one launch's fixed cost.
+ * at one launch's fixed cost.  Routed gate and up projections likewise: with
+ * gate_e and up_e stored as experts 2e and 2e + 1 of one stack, expert_ids
+ * (2e, 2e + 1) per routed slot and top_k doubled give both outputs of every
+ * slot in one launch, bit for bit those of the two separate calls.
  */
 vq_status vq_moe_gemv(const vq_tensor *w, const uint16_t *x, int32_t x_per_slot,
                       const int32_t *expert_ids, int32_t T, int32_t top_k, float *y,

@@ -274,6 +274,31 @@ def test_gate_up_stack_in_one_routed_call(rows, cols):
         assert np.array_equal(ye[0], y[0, e]), e
 
 
+def test_routed_gate_up_interleaved_in_one_call():
+    """Routed gate and up projections (same x per token) stored as experts
+    2e and 2e + 1 of one stack, run by one vq_moe_gemv with ids 2e, 2e + 1
+    (top_k doubled): bit for bit the two separate routed calls."""
+    import torch
+    from vq_dequant_matmul_gemv_amd import binding
+    E, rows, cols, top_k, T = 12, 96, 256, 3, 4
+    specs = synth.Spec(rows=rows, cols=cols, d=4, log2_k=8, group=64, experts=E)
+    g = synth.tensor(specs, "gu-routed", "gate")
+    u = synth.tensor(specs, "gu-routed", "up")
+    wg, wu = upload(g, specs), upload(u, specs)
+    codes = torch.stack([wg.codes, wu.codes], 1).reshape(2 * E, rows, -1).contiguous()
+    scales = torch.stack([wg.scales, wu.scales], 1).reshape(2 * E, rows, -1).contiguous()
+    cbs = torch.stack([wg.codebook, wu.codebook]).repeat(E, 1, 1).contiguous()
+    w2 = binding.VQTensor(codes, cbs, scales, rows, cols, 4, 8, 64, 2 * E, True)
+    ids = synth.rng("ids-gu").integers(0, E, size=(T, top_k)).astype(np.int32)
+    ids2 = np.stack([2 * ids, 2 * ids + 1], -1).reshape(T, 2 * top_k).astype(np.int32)
+    x = to_dev(synth.activations((T, cols), "gu-routed"))
+    announce("routed gate+up interleaved")
+    yg = binding.moe_gemv(wg, x, to_dev(ids)).cpu().numpy()
+    yu = binding.moe_gemv(wu, x, to_dev(ids)).cpu().numpy()
+    y2 = binding.moe_gemv(w2, x, to_dev(ids2)).cpu().numpy()
+    assert np.array_equal(y2[:, 0::2], yg) and np.array_equal(y2[:, 1::2], yu)
+
+
 def test_moe_gemm_more_experts_than_lds_counters():
     """8200 experts: the routing kernel keeps its per-expert counters in the
     workspace rather than in LDS (which holds 8192)."""
