@@ -276,8 +276,8 @@ def test_gate_up_stack_in_one_routed_call(rows, cols):
 
 def test_routed_gate_up_interleaved_in_one_call():
     """Routed gate and up projections (same x per token) stored as experts
-    2e and 2e + 1 of one stack, run by one vq_moe_gemv with ids 2e, 2e + 1
-    (top_k doubled): bit for bit the two separate routed calls."""
+    2e and 2e + 1 of one stack, run by one call with ids 2e, 2e + 1 (top_k
+    doubled): bit for bit the two separate routed calls, GEMV and GEMM."""
     import torch
     from vq_dequant_matmul_gemv_amd import binding
     E, rows, cols, top_k, T = 12, 96, 256, 3, 4
@@ -297,6 +297,11 @@ def test_routed_gate_up_interleaved_in_one_call():
     yu = binding.moe_gemv(wu, x, to_dev(ids)).cpu().numpy()
     y2 = binding.moe_gemv(w2, x, to_dev(ids2)).cpu().numpy()
     assert np.array_equal(y2[:, 0::2], yg) and np.array_equal(y2[:, 1::2], yu)
+    # the grouped GEMM: a pair's row depends only on its expert and x row
+    zg = binding.moe_gemm(wg, x, to_dev(ids)).cpu().numpy()
+    zu = binding.moe_gemm(wu, x, to_dev(ids)).cpu().numpy()
+    z2 = binding.moe_gemm(w2, x, to_dev(ids2)).cpu().numpy()
+    assert np.array_equal(z2[:, 0::2], zg) and np.array_equal(z2[:, 1::2], zu)
 
 
 def test_moe_gemm_more_experts_than_lds_counters():
