@@ -181,6 +181,10 @@ size_t vq_moe_workspace_bytes(int32_t T, int32_t top_k, int32_t num_experts);
  *   bytes, 16-byte aligned, owned by the caller; contents on entry are
  *   ignored and on return are undefined.  Concurrent calls need separate
  *   workspaces.
+ * The stacked gate/up layouts described for vq_moe_gemv apply here too
+ * (workspace sized for the doubled top_k and expert count): each output row
+ * depends only on its expert and x row, so the results are bit for bit those
+ * of separate calls.
  */
 vq_status vq_moe_gemm(const vq_tensor *w, const uint16_t *x, int32_t x_per_slot,
                       const int32_t *expert_ids, int32_t T, int32_t top_k, float *y,
