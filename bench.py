@@ -270,10 +270,11 @@ def configs_report(only=""):
         del reps
         torch.cuda.empty_cache()
 
-    def routed_gate_up(wl, spec, top_k, key_g, key_u):
-        """Routed gate and up at T = 1 in one vq_moe_gemv: experts 2e / 2e + 1
-        of one stack (per-expert codebooks), ids 2e, 2e + 1 per slot.  Bytes
-        as for the two separate calls."""
+    def routed_gate_up(wl, spec, top_k, Ts, key_g, key_u):
+        """Routed gate and up in one call: experts 2e / 2e + 1 of one stack
+        (per-expert codebooks), ids 2e, 2e + 1 per slot (top_k doubled);
+        vq_moe_gemv at the first token count, vq_moe_gemm at the second.
+        Bytes and flops as for the two separate calls."""
         tg = binding.VQTensor.from_host(synth.tensor(spec, *key_g), spec, device=dev)
         tu = binding.VQTensor.from_host(synth.tensor(spec, *key_u), spec, device=dev)
         E = spec.experts
@@ -286,19 +287,26 @@ def configs_report(only=""):
         reps = [base] + [binding.VQTensor(base.codes.clone(), base.codebook.clone(), base.scales.clone(),
                                           spec.rows, spec.cols, spec.d, spec.log2_k, spec.group, 2 * E, True)
                          for _ in range(int(max(0, min(7, -(-1.1e9 // (per_expert * 2 * E)) - 1))))]
-        draws = [synth.zipf_routing(1, E, top_k, *key_g, "ids", 1, r) for r in range(16)]
-        ids = [torch.from_numpy(np.stack([2 * d, 2 * d + 1], -1).reshape(1, 2 * top_k).astype(np.int32)).to(dev)
-               for d in draws]
-        x = torch.from_numpy(synth.activations((1, spec.cols), *key_g, "x", 1)).to(dev)
-        y = torch.empty((1, 2 * top_k, spec.rows), dtype=torch.float32, device=dev)
-        calls, nbytes = [], 0
-        for i in range(16):
-            calls.append(lambda w=reps[i % len(reps)], d=ids[i]: binding.moe_gemv(w, x, d, y=y))
-            hit = len(np.unique(draws[i]))
-            nbytes += 2 * (hit * per_expert + spec.k * spec.d * 2 + x.numel() * 2 + top_k * spec.rows * 4 + top_k * 4)
-        us = timed(calls)
-        row(wl, "gate+up (experts 2e / 2e+1 of one stack, top-16)", "vq_moe_gemv", 1, us, nbytes / 16,
-            2.0 * 2 * top_k * spec.rows * spec.cols)
+        for fn, T in zip(("moe_gemv", "moe_gemm"), Ts):
+            draws = [synth.zipf_routing(T, E, top_k, *key_g, "ids", T, r) for r in range(16)]
+            ids = [torch.from_numpy(np.stack([2 * d, 2 * d + 1], -1).reshape(T, 2 * top_k).astype(np.int32))
+                   .to(dev) for d in draws]
+            x = torch.from_numpy(synth.activations((T, spec.cols), *key_g, "x", T)).to(dev)
+            y = torch.empty((T, 2 * top_k, spec.rows), dtype=torch.float32, device=dev)
+            ws = torch.empty(max(16, binding.workspace_bytes(T, 2 * top_k, 2 * E)), dtype=torch.uint8, device=dev)
+            calls, nbytes = [], 0
+            for i in range(16):
+                w = reps[i % len(reps)]
+                if fn == "moe_gemv":
+                    calls.append(lambda w=w, d=ids[i]: binding.moe_gemv(w, x, d, y=y))
+                else:
+                    calls.append(lambda w=w, d=ids[i]: binding.moe_gemm(w, x, d, y=y, workspace=ws))
+                hit = len(np.unique(draws[i]))
+                nbytes += 2 * (hit * per_expert + spec.k * spec.d * 2 + x.numel() * 2 + T * top_k * spec.rows * 4
+                               + T * top_k * 4)
+            us = timed(calls)
+            row(wl, "gate+up (experts 2e / 2e+1 of one stack, top-16)", "vq_" + fn, T, us, nbytes / 16,
+                2.0 * 2 * T * top_k * spec.rows * spec.cols)
         del reps
         torch.cuda.empty_cache()
 
@@ -344,7 +352,7 @@ def configs_report(only=""):
     for n in ("gate", "down") if keep(wl) else ():
         routed(wl, n, W[wl]["tensors"][n], W[wl]["top_k"], (1, 1024), n == "down", (wl, n))
     if keep(wl):
-        routed_gate_up(wl, W[wl]["tensors"]["gate"], W[wl]["top_k"], (wl, "gate"), (wl, "up"))
+        routed_gate_up(wl, W[wl]["tensors"]["gate"], W[wl]["top_k"], (1, 1024), (wl, "gate"), (wl, "up"))
     wl = "moe_mixed_tier_e256_2048x512"
     for tier in ("T1", "T2", "T3") if keep(wl) else ():
         for idx, n in ((0, "gate"), (2, "down")):
