@@ -174,6 +174,11 @@ __device__ __forceinline__ uint32_t pick16(u32x4 v, int pos) {
   return (pos & 1) ? d >> 16 : d & 0xffffu;
 }
 
+// Phase-offset main loop for d = 2 on the 128-token tiles, in clusters of
+// kGemmCluster k-steps (see the kernel).
+constexpr bool kGemmPhaseOffset = true;
+constexpr int kGemmCluster = 4;
+
 template <int D, int B, int G, class SH, bool MOE, bool WIDE>
 __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
   using L = CodebookLayout<D, B>;
@@ -408,6 +413,89 @@ __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
   store_x(0, xr);
   __syncthreads();
 
+  if constexpr (kGemmPhaseOffset && NB >= 4 && D == 2) {
+    // Phase-offset schedule for the 128-token tiles.  A super-step runs as
+    // clusters of KC k-steps, each split into a dequant phase (codebook
+    // gathers and fp16 multiplies for the cluster's W fragments, kept in
+    // registers) and an MFMA phase (x fragments from LDS, KC * MB * NB
+    // MFMAs), separated by block barriers.  The upper half of the waves
+    // enters one phase late, so on every SIMD (waves w and w + 4 share one)
+    // one wave runs its MFMAs while the other dequantizes.  Every wave passes
+    // the same number of barriers: the late half one extra at the start, the
+    // early half one at the end.  Used for d = 2 only: with the 128-column
+    // super-steps of d = 4 and 8, a cluster's fragments spill registers.
+    constexpr int KC = kGemmCluster < S ? kGemmCluster : S;
+    static_assert(S % KC == 0, "clusters tile the super-step");
+    const bool late = wave >= SH::kWaves / 2;
+    auto phase_sync = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // x of the next super-step is stored at the end of this super-step's
+    // last MFMA phase, behind a barrier that waits for it: the last reads of
+    // that buffer (the super-step before) end at least two barriers earlier,
+    // and the first reads of the new x (the next super-step's first MFMA
+    // phase) come at least one barrier later for both halves.
+    auto super_step = [&](int ks, int buf, const LaneCodes<NCL, B> (&cc)[MB], const uint16_t (&sc)[MB],
+                          LaneCodes<NCL, B> (&ccn)[MB], uint16_t (&scn)[MB]) {
+      load_x(ks + 1, xr);
+      load_codes(ks + 1, ccn, scn);
+      const uint8_t* xb = xbuf + buf * (WN * XROW);
+      half2_t s2[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) s2[mb] = as_half2((uint32_t)sc[mb] * 0x10001u);
+#pragma unroll
+      for (int s0 = 0; s0 < S; s0 += KC) {
+        half8_t af[KC][MB];
+        Entry<D> e[KC][MB][CPA];
+#pragma unroll
+        for (int k = 0; k < KC; ++k)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int c = 0; c < CPA; ++c)
+              e[k][mb][c] = lane_gather<D, B, NCL>(cb_lds, cc[mb], (s0 + k) * CPA + c, lane_off);
+#pragma unroll
+        for (int k = 0; k < KC; ++k)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            half2_t w[4];
+#pragma unroll
+            for (int c = 0; c < CPA; ++c)
+#pragma unroll
+              for (int j = 0; j < D / 2; ++j) w[c * (D / 2) + j] = e[k][mb][c].v[j] * s2[mb];
+            af[k][mb] = half8_t{w[0].x, w[0].y, w[1].x, w[1].y, w[2].x, w[2].y, w[3].x, w[3].y};
+          }
+        phase_sync();
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+          half8_t bf[NB];
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            bf[nb] = *reinterpret_cast<const half8_t*>(xb + (nb * 32 + l32) * XROW + (h * CG + 8 * (s0 + k)) * 2);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(bf[nb], af[k][mb], acc[mb][nb]);
+        }
+        if (s0 + KC == S) {
+          store_x(buf ^ 1, xr);
+          __builtin_amdgcn_sched_barrier(0);
+          lds_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+        } else {
+          phase_sync();
+        }
+      }
+    };
+    if (late) phase_sync();
+    for (int ks = ks_begin; ks < ks_end; ks += 2) {
+      super_step(ks, 0, ccA, scA, ccB, scB);
+      if (ks + 1 < ks_end) super_step(ks + 1, 1, ccB, scB, ccA, scA);
+    }
+    if (!late) phase_sync();
+  } else
   for (int ks = ks_begin; ks < ks_end; ks += 2) {
     load_x(ks + 1, xr);
     load_codes(ks + 1, ccB, scB);
