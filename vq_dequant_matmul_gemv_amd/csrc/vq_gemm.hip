@@ -422,8 +422,10 @@ __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
     // enters one phase late, so on every SIMD (waves w and w + 4 share one)
     // one wave runs its MFMAs while the other dequantizes.  Every wave passes
     // the same number of barriers: the late half one extra at the start, the
-    // early half one at the end.  Used for d = 2 only: with the 128-column
-    // super-steps of d = 4 and 8, a cluster's fragments spill registers.
+    // early half one at the end.  The MFMA phase runs at raised wave
+    // priority, so the SIMD's issue slots go to the MFMAs first.  Used for
+    // d = 2 only: with the 128-column super-steps of d = 4 and 8, a
+    // cluster's fragments spill registers.
     constexpr int KC = kGemmCluster < S ? kGemmCluster : S;
     static_assert(S % KC == 0, "clusters tile the super-step");
     const bool late = wave >= SH::kWaves / 2;
@@ -468,6 +470,7 @@ __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
             af[k][mb] = half8_t{w[0].x, w[0].y, w[1].x, w[1].y, w[2].x, w[2].y, w[3].x, w[3].y};
           }
         phase_sync();
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int k = 0; k < KC; ++k) {
           half8_t bf[NB];
@@ -479,6 +482,7 @@ __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(bf[nb], af[k][mb], acc[mb][nb]);
         }
+        __builtin_amdgcn_s_setprio(0);
         if (s0 + KC == S) {
           store_x(buf ^ 1, xr);
           __builtin_amdgcn_sched_barrier(0);
