@@ -174,7 +174,7 @@ __device__ __forceinline__ uint32_t pick16(u32x4 v, int pos) {
   return (pos & 1) ? d >> 16 : d & 0xffffu;
 }
 
-// Phase-offset main loop for d = 2 on the 128-token tiles, in clusters of
+// Phase-offset main loop on the 128-token tiles, in clusters of
 // kGemmCluster k-steps (see the kernel).
 constexpr bool kGemmPhaseOffset = true;
 constexpr int kGemmCluster = 4;
@@ -413,7 +413,7 @@ __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
   store_x(0, xr);
   __syncthreads();
 
-  if constexpr (kGemmPhaseOffset && NB >= 4 && D == 2) {
+  if constexpr (kGemmPhaseOffset && NB >= 4 && (D == 2 || (D == 4 && B == 8) || D == 8)) {
     // Phase-offset schedule for the 128-token tiles.  A super-step runs as
     // clusters of KC k-steps, each split into a dequant phase (codebook
     // gathers and fp16 multiplies for the cluster's W fragments, kept in
@@ -423,9 +423,9 @@ __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
     // one wave runs its MFMAs while the other dequantizes.  Every wave passes
     // the same number of barriers: the late half one extra at the start, the
     // early half one at the end.  The MFMA phase runs at raised wave
-    // priority, so the SIMD's issue slots go to the MFMAs first.  Used for
-    // d = 2 only: with the 128-column super-steps of d = 4 and 8, a
-    // cluster's fragments spill registers.
+    // priority, so the SIMD's issue slots go to the MFMAs first.  Not used
+    // for d = 4 with 12-bit codes, where a cluster's fragments spill
+    // registers.
     constexpr int KC = kGemmCluster < S ? kGemmCluster : S;
     static_assert(S % KC == 0, "clusters tile the super-step");
     const bool late = wave >= SH::kWaves / 2;
@@ -439,9 +439,29 @@ __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
     // that buffer (the super-step before) end at least two barriers earlier,
     // and the first reads of the new x (the next super-step's first MFMA
     // phase) come at least one barrier later for both halves.
+    // The next super-step's x stage travels in NCLU parts, one per cluster:
+    // part p is loaded at the start of cluster p's dequant phase and written
+    // to LDS at the end of its MFMA phase (the buffer's last reads end before
+    // the first part is written, and the barrier ending the super-step waits
+    // for every part's stores), so only one part occupies registers.
+    constexpr int NCLU = S / KC;
+    static_assert(XLD % NCLU == 0, "x segments split evenly over the clusters");
+    constexpr int XP = XLD / NCLU;
+    auto load_xp = [&](int ks, int p, u32x4 (&q)[XP]) {
+      const bool live = ks < ks_end;
+#pragma unroll
+      for (int i = 0; i < XP; ++i)
+        q[i] = buf_load_b128(rx, live ? xoff[p * XP + i] + (uint32_t)ks * SS * 2u : kOutOfRange);
+    };
+    auto store_xp = [&](int buf, int p, const u32x4 (&q)[XP]) {
+#pragma unroll
+      for (int i = 0; i < XP; ++i)
+        if (xdst[p * XP + i] >= 0) *reinterpret_cast<u32x4*>(xbuf + buf * (WN * XROW) + xdst[p * XP + i]) = q[i];
+    };
     auto super_step = [&](int ks, int buf, const LaneCodes<NCL, B> (&cc)[MB], const uint16_t (&sc)[MB],
                           LaneCodes<NCL, B> (&ccn)[MB], uint16_t (&scn)[MB]) {
-      load_x(ks + 1, xr);
+      u32x4 xq[XP];
+      load_xp(ks + 1, 0, xq);
       load_codes(ks + 1, ccn, scn);
       const uint8_t* xb = xbuf + buf * (WN * XROW);
       half2_t s2[MB];
@@ -449,6 +469,7 @@ __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
       for (int mb = 0; mb < MB; ++mb) s2[mb] = as_half2((uint32_t)sc[mb] * 0x10001u);
 #pragma unroll
       for (int s0 = 0; s0 < S; s0 += KC) {
+        if (s0 > 0) load_xp(ks + 1, s0 / KC, xq);
         half8_t af[KC][MB];
         Entry<D> e[KC][MB][CPA];
 #pragma unroll
@@ -483,8 +504,8 @@ __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
             for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(bf[nb], af[k][mb], acc[mb][nb]);
         }
         __builtin_amdgcn_s_setprio(0);
+        store_xp(buf ^ 1, s0 / KC, xq);
         if (s0 + KC == S) {
-          store_x(buf ^ 1, xr);
           __builtin_amdgcn_sched_barrier(0);
           lds_barrier();
           __builtin_amdgcn_sched_barrier(0);
