@@ -100,6 +100,27 @@ def test_dense_exact_inputs_bit_identical(fn, d, b, g):
         assert np.array_equal(y.astype(np.float64), ref), (fn, T)
 
 
+@pytest.mark.parametrize("d,b,g", GEOMS)
+def test_gemm_128_token_tiles_all_geometries(d, b, g):
+    """The 128-token tiles (T > 32) in every geometry: ragged rows and
+    tokens, an odd number of super-steps, and a K split whose slices hold an
+    odd number of super-steps (the main loop's second half-step is skipped)."""
+    from vq_dequant_matmul_gemv_amd import binding
+    ss = 64 if d == 2 else 128                      # columns per super-step
+    for rows, cols, Ts in ((301, _cols_for(d, g, 7), (40, 129)),
+                           (1030, ss * (25 if d == 2 else 13 if d == 4 else 18), (130,))):
+        if cols % g or (cols // d) % 32:
+            cols = _cols_for(d, g, cols // (32 * d))
+        spec, arrs, w = _case(d, b, g, rows, cols, ("t128", d, b, g, rows))
+        for T in Ts:
+            x = synth.activations((T, cols), "t128", d, b, g, rows, T)
+            announce("gemm", "t128", d, b, g, rows, cols, T)
+            y = binding.gemm(w, to_dev(x)).cpu().numpy()
+            ref = O.gemv_ref(arrs["codes"][0], arrs["codebook"], arrs["scales"][0], x, cols, d, b, g)
+            err = row_rel_err(y, ref)
+            assert err <= TOL, (rows, cols, T, err)
+
+
 @pytest.mark.parametrize("fn", ["gemv", "gemm"])
 def test_dense_shapes_and_tokens(fn):
     """Ragged tokens around the tile sizes, tiny and tall shapes, a column
