@@ -30,6 +30,10 @@
 //  * x tiles (32*NB tokens x 2*CG columns) go through LDS, double-buffered,
 //    one barrier per super-step; token rows are padded by 16 bytes so the
 //    16-byte fragment reads hit distinct banks.
+//  * On the 128-token tiles (except d = 4 with 12-bit codes) the main loop
+//    is phase-offset: clusters of 4 k-steps alternate a dequant phase and an
+//    MFMA phase between block barriers, half the waves one phase behind, so
+//    the two waves of a SIMD take turns on the MFMA pipe.
 //  * Codebook in LDS (replicated for K = 256, as in the GEMV); the gathers of
 //    the next k-step are issued ahead of the current k-step's MFMAs.
 //  * Tiles of a last, partial round of the grid (or of a grid with fewer
