@@ -264,8 +264,10 @@ __device__ __forceinline__ float row16_sum(float v) {
 }
 
 // Block barrier that orders LDS only: waits for this wave's LDS operations,
-// not for its global loads in flight (a plain __syncthreads waits for those
-// too, which would stall a prefetch issued before the barrier).
+// not for its global loads in flight, so a prefetch issued before the
+// barrier stays in flight across it.  (hipcc's __syncthreads compiles to the
+// same two instructions for gfx950; spelling them out keeps that property
+// from depending on how the compiler lowers the fence.)
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
