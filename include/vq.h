@@ -83,6 +83,9 @@ typedef enum {
  * the wrong length and is refused rather than read out of bounds (model card
  * "Qwen3.8-27B-VQ-4.5bpw", Multi-machine note: codebooks must be replicated,
  * never sliced, and a sliced one must fail loudly).
+ * Buffer lengths (else VQ_ERR_SHAPE): code_words == E * rows * Wr and
+ * scale_elems == E * rows * (cols / group), so codes packed for another
+ * geometry or a short buffer are refused instead of read past their end.
  * Alignment (else VQ_ERR_ALIGN): codes 16 bytes; codebook 16 bytes; scales 4
  * bytes.  Size limit (else VQ_ERR_SHAPE): one expert's codes and its scales
  * each fit in 2 GiB - 1 bytes (the kernels address them with 32-bit offsets).
@@ -99,6 +102,8 @@ typedef struct vq_tensor {
   int32_t num_experts;      /* E; 1 for a dense tensor                           */
   int32_t codebook_per_expert; /* 0: one codebook for the tensor; 1: one per expert */
   int64_t codebook_elems;   /* number of fp16 values behind `codebook`           */
+  int64_t code_words;       /* number of uint32 words behind `codes`             */
+  int64_t scale_elems;      /* number of fp16 values behind `scales`             */
 } vq_tensor;
 
 /* uint32 words per row of packed codes: ceil(cols/d/32) * log2_k.  Returns -1

@@ -96,6 +96,10 @@ def scale_bytes(rows: int, cols: int, group: int, experts: int = 1) -> int:
 
 
 def codebook_bytes(d: int, log2_k: int, n_codebooks: int = 1) -> int:
+    """Bytes of K entries of d fp16 values, times the number of codebooks
+    ([397B] Methodology: per-tensor fp16 codebook; [paper] §4.2: the d4
+    codebook of 65,536 entries is sixteen times a 32 KB threadgroup memory,
+    i.e. two bytes per value)."""
     return n_codebooks * (1 << log2_k) * d * 2
 
 

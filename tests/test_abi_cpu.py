@@ -48,6 +48,11 @@ def _t(b, **kw):
     base = dict(codes=0x10000, codebook=0x20000, scales=0x30000, rows=16, cols=256, d=2,
                 log2_k=8, group=64, num_experts=1, codebook_per_expert=0, codebook_elems=512)
     base.update(kw)
+    # buffer lengths consistent with the (possibly changed) shape unless given
+    E, rows, cols, d, lk, g = (base[k] for k in ("num_experts", "rows", "cols", "d", "log2_k", "group"))
+    wr = O.words_per_row(cols, d, lk) if d in (2, 4, 8) and cols > 0 else 0
+    base.setdefault("code_words", E * rows * wr)
+    base.setdefault("scale_elems", E * rows * (cols // g) if g > 0 else 0)
     return b.CTensor(**base)
 
 
@@ -68,6 +73,9 @@ def _gemv(b, t, x=0x40000, T=1, y=0x50000):
     (dict(codebook_elems=1024), "VQ_ERR_SHAPE"),
     (dict(num_experts=2), "VQ_ERR_SHAPE"),               # dense entry point, stacked tensor
     (dict(codebook_per_expert=2), "VQ_ERR_SHAPE"),
+    (dict(code_words=16 * 48), "VQ_ERR_SHAPE"),          # codes packed with 12-bit codes
+    (dict(code_words=511), "VQ_ERR_SHAPE"),              # short code buffer
+    (dict(scale_elems=32), "VQ_ERR_SHAPE"),              # scales for group 128
     (dict(codes=0x10004), "VQ_ERR_ALIGN"),
     (dict(codebook=0x20008), "VQ_ERR_ALIGN"),
     (dict(scales=0x30002), "VQ_ERR_ALIGN"),
@@ -154,3 +162,4 @@ def test_buffer_size_limits(b):
     t = _t(b, num_experts=4, cols=4096)
     st = b.LIB.vq_moe_gemv(ctypes.byref(t), 0x40000, 1, 0x70000, 1 << 16, 8, 0x50000, None)
     assert b.STATUS_NAMES[st] == "VQ_ERR_SHAPE" and "x holds" in b.LIB.vq_last_error().decode()
+

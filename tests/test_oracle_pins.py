@@ -123,6 +123,40 @@ def test_dense_trio_byte_counts():
     assert O.code_bytes(17408, 5120, 4, 8) == 22_282_240
 
 
+def _golden_cb():
+    rows = []
+    with open(os.path.join(GOLDEN, "codebook_bytes.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            d, k, nbytes = line.split()[:3]
+            rows.append((int(d), int(k), int(nbytes)))
+    return rows
+
+
+@pytest.mark.parametrize("d,k,nbytes", _golden_cb())
+def test_codebook_bytes_matches_pages(d, k, nbytes):
+    assert O.codebook_bytes(d, int(math.log2(k))) == nbytes
+
+
+def test_codebook_bytes_threadgroup_thresholds_and_staging_sizes():
+    # paper §3.1: a d4 codebook above K = 2048 and a d2 codebook above K = 4096
+    # outgrow the 32 KB threadgroup memory; the two thresholds are the same size
+    # (d * K equal) and the next codebook of either kind reaches 32 KB.
+    limit = 32 * 1024
+    assert O.codebook_bytes(4, 11) == O.codebook_bytes(2, 12) < limit
+    assert O.codebook_bytes(4, 12) >= limit and O.codebook_bytes(2, 13) >= limit
+    # the staging sizes of the geometries the kernels hold in LDS
+    assert O.codebook_bytes(2, 8) == 1024 and O.codebook_bytes(4, 8) == 2048
+    assert O.codebook_bytes(4, 12) == 32 * 1024 and O.codebook_bytes(8, 12) == 64 * 1024
+    # one codebook per expert: E times one tensor's
+    assert O.codebook_bytes(4, 8, n_codebooks=256) == 256 * O.codebook_bytes(4, 8)
+    # the codebook a synthetic tensor carries has exactly that many bytes
+    for d, b in ((2, 8), (4, 12), (8, 12)):
+        spec = synth.Spec(rows=4, cols=32 * d, d=d, log2_k=b, group=64 if d < 8 else 128)
+        assert synth.tensor(spec, "cb-bytes", d, b)["codebook"].nbytes == O.codebook_bytes(d, b)
+
+
 def test_words_per_row_pads_to_whole_blocks():
     assert O.words_per_row(64, 2, 8) == 8          # exactly one 32-code block
     assert O.words_per_row(66, 2, 8) == 16         # 33 codes -> 2 blocks

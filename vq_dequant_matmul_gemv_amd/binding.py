@@ -40,6 +40,8 @@ class CTensor(ctypes.Structure):
         ("num_experts", ctypes.c_int32),
         ("codebook_per_expert", ctypes.c_int32),
         ("codebook_elems", ctypes.c_int64),
+        ("code_words", ctypes.c_int64),
+        ("scale_elems", ctypes.c_int64),
     ]
 
 
@@ -106,12 +108,24 @@ def _ptr(t) -> ctypes.c_void_p:
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _dev_check(*ts):
+def _dev_check(*ts, device=None):
+    """Every tensor on the GPU (on `device` when given), contiguous."""
     for t in ts:
         if not t.is_cuda:
             raise ValueError("tensors must live on the GPU")
+        if device is not None and t.device != device:
+            raise ValueError(f"tensor on {t.device}, expected {device} (the weights' device)")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
+
+
+def _check_out(y, dtype, shape, name="y"):
+    torch = _torch()
+    if y.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {y.dtype}")
+    if tuple(y.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(y.shape)}")
+    del torch
 
 
 @dataclass
@@ -133,11 +147,23 @@ class VQTensor:
     num_experts: int = 1
     codebook_per_expert: bool = False
 
+    @property
+    def device(self):
+        return self.codes.device
+
     def cstruct(self) -> CTensor:
-        _dev_check(self.codes, self.codebook, self.scales)
+        """The C descriptor; buffer lengths travel with it so the library
+        refuses codes, scales or a codebook of the wrong size."""
+        torch = _torch()
+        _dev_check(self.codes, self.codebook, self.scales, device=self.codes.device)
+        if self.codebook.dtype != torch.float16 or self.scales.dtype != torch.float16:
+            raise ValueError("codebook and scales must be fp16")
+        if self.codes.element_size() * self.codes.numel() % 4:
+            raise ValueError("codes must hold whole uint32 words")
         return CTensor(self.codes.data_ptr(), self.codebook.data_ptr(), self.scales.data_ptr(),
                        self.rows, self.cols, self.d, self.log2_k, self.group, self.num_experts,
-                       int(self.codebook_per_expert), self.codebook.numel())
+                       int(self.codebook_per_expert), self.codebook.numel(),
+                       self.codes.numel() * self.codes.element_size() // 4, self.scales.numel())
 
     @classmethod
     def from_host(cls, arrays: dict, spec, device="cuda", codebook_per_expert=False):
@@ -156,7 +182,8 @@ def dequant(w: VQTensor, expert: int = 0, out=None, stream=None):
     torch = _torch()
     if out is None:
         out = torch.empty((w.rows, w.cols), dtype=torch.float16, device=w.codes.device)
-    _dev_check(out)
+    _check_out(out, torch.float16, (w.rows, w.cols), "out")
+    _dev_check(out, device=w.device)
     cs = w.cstruct()
     check(LIB.vq_dequant(ctypes.byref(cs), expert, _ptr(out), _stream(stream)))
     return out
@@ -169,7 +196,8 @@ def _dense(fn, w: VQTensor, x, y, stream):
     T = x.shape[0]
     if y is None:
         y = torch.empty((T, w.rows), dtype=torch.float32, device=x.device)
-    _dev_check(x, y)
+    _check_out(y, torch.float32, (T, w.rows))
+    _dev_check(x, y, device=w.device)
     cs = w.cstruct()
     check(fn(ctypes.byref(cs), _ptr(x), T, _ptr(y), _stream(stream)))
     return y
@@ -195,7 +223,8 @@ def _moe_prep(w, x, ids, x_per_slot, y):
         raise ValueError(f"x must be fp16 {want}")
     if y is None:
         y = torch.empty((T, top_k, w.rows), dtype=torch.float32, device=x.device)
-    _dev_check(x, ids, y)
+    _check_out(y, torch.float32, (T, top_k, w.rows))
+    _dev_check(x, ids, y, device=w.device)
     return T, top_k, y
 
 
@@ -213,7 +242,9 @@ def moe_gemm(w: VQTensor, x, ids, x_per_slot=False, y=None, workspace=None, stre
     need = workspace_bytes(T, top_k, w.num_experts)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _dev_check(workspace, device=w.device)
     cs = w.cstruct()
     check(LIB.vq_moe_gemm(ctypes.byref(cs), _ptr(x), int(bool(x_per_slot)), _ptr(ids), T, top_k,
                           _ptr(y), _ptr(workspace), workspace.numel(), _stream(stream)))
     return y
+

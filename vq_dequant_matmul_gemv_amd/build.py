@@ -32,7 +32,7 @@ ARCH = "gfx950"
 # GEMV's pointers, row count and row split: 14 SGPRs) arrive in SGPRs at wave
 # launch.
 COMMON = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Werror", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-mllvm", "-amdgpu-kernarg-preload-count=10",
     "-fno-gpu-rdc", "-I", INCLUDE, "-I", CSRC,

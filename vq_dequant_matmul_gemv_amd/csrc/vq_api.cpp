@@ -72,6 +72,17 @@ vq_status check_tensor(const vq_tensor* w, vqmi::TensorView* v) {
                 "codebook has %lld fp16 values but K*d%s = %lld: a sliced or partial codebook "
                 "cannot be used (codebooks must be replicated whole, never split)",
                 (long long)w->codebook_elems, w->codebook_per_expert ? "*E" : "", (long long)want);
+  const int64_t want_words = (int64_t)w->num_experts * w->rows * words_per_row(w->cols, w->d, w->log2_k);
+  if (w->code_words != want_words)
+    return fail(VQ_ERR_SHAPE,
+                "codes hold %lld words but E*rows*Wr = %lld (Wr = %d for cols=%d d=%d log2_k=%d): codes "
+                "packed for another geometry, or a short buffer",
+                (long long)w->code_words, (long long)want_words, words_per_row(w->cols, w->d, w->log2_k),
+                w->cols, w->d, w->log2_k);
+  const int64_t want_scales = (int64_t)w->num_experts * w->rows * (w->cols / w->group);
+  if (w->scale_elems != want_scales)
+    return fail(VQ_ERR_SHAPE, "scales hold %lld values but E*rows*cols/group = %lld",
+                (long long)w->scale_elems, (long long)want_scales);
   const int64_t elems = (int64_t)w->num_experts * w->rows * (int64_t)w->cols;
   if (elems > ((int64_t)1 << 40))
     return fail(VQ_ERR_SHAPE, "tensor too large (%lld weights)", (long long)elems);

@@ -669,7 +669,6 @@ hipError_t gemv_geom(const TensorView& w, const uint16_t* x, int T, float* y, co
 
 template <int D, int B, int G>
 hipError_t dequant_geom(const TensorView& w, int expert, uint16_t* out, hipStream_t s) {
-  using L = CodebookLayout<D, B>;
   DequantArgs a{};
   a.codes = w.codes + (int64_t)expert * w.rows * w.wr;
   a.codebook = w.codebook + (w.cb_per_expert ? (int64_t)expert * (1 << B) * D : 0);
