@@ -195,6 +195,24 @@ vq_status vq_moe_gemm(const vq_tensor *w, const uint16_t *x, int32_t x_per_slot,
                       const int32_t *expert_ids, int32_t T, int32_t top_k, float *y,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * vq_moe_gemm for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments and results as vq_moe_gemm, bit for bit, without the
+ * workspace.  Its routing scratch is a static device array of 4 MiB inside the
+ * library, one per GPU, held until the process ends; calls whose
+ * vq_moe_workspace_bytes(T, top_k, num_experts) exceeds 4 MiB return
+ * VQ_ERR_WORKSPACE (about 950 thousand (token, slot) pairs for 256 experts).  The
+ * scratch of the current device is used: `stream` must belong to it.  Nothing
+ * is allocated and the scratch needs no clearing (every call writes what it
+ * reads).  All calls on one GPU share that array: calls that overlap in time
+ * on one GPU (other streams, other threads) race and give wrong results;
+ * calls ordered on one stream are safe.
+ */
+vq_status vq_moe_gemm_no_alloc(const vq_tensor *w, const uint16_t *x, int32_t x_per_slot,
+                               const int32_t *expert_ids, int32_t T, int32_t top_k, float *y,
+                               void *stream);
+
 /* Text for the last non-OK status returned on this thread ("" if none). */
 const char *vq_last_error(void);
 

@@ -163,3 +163,14 @@ def test_buffer_size_limits(b):
     st = b.LIB.vq_moe_gemv(ctypes.byref(t), 0x40000, 1, 0x70000, 1 << 16, 8, 0x50000, None)
     assert b.STATUS_NAMES[st] == "VQ_ERR_SHAPE" and "x holds" in b.LIB.vq_last_error().decode()
 
+
+def test_no_alloc_refuses_sizes_beyond_its_scratch_on_the_host(b):
+    """The size check runs before any device call: more routing scratch than
+    the library's static 4 MiB is refused with VQ_ERR_WORKSPACE."""
+    t = _t(b, num_experts=4)
+    T, top_k = 1 << 17, 8
+    assert b.workspace_bytes(T, top_k, 4) > 4 << 20
+    st = b.LIB.vq_moe_gemm_no_alloc(ctypes.byref(t), 0x40000, 0, 0x70000, T, top_k, 0x50000, None)
+    assert b.STATUS_NAMES[st] == "VQ_ERR_WORKSPACE"
+    assert "static scratch" in b.LIB.vq_last_error().decode()
+    assert b.LIB.vq_moe_gemm_no_alloc(ctypes.byref(t), 0x40000, 0, 0x70000, 0, top_k, 0x50000, None) == b.VQ_OK

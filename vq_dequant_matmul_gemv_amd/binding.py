@@ -60,6 +60,7 @@ def _load():
         "vq_moe_gemv": (i32, [T, P, i32, P, i32, i32, P, P]),
         "vq_moe_workspace_bytes": (ctypes.c_size_t, [i32, i32, i32]),
         "vq_moe_gemm": (i32, [T, P, i32, P, i32, i32, P, P, ctypes.c_size_t, P]),
+        "vq_moe_gemm_no_alloc": (i32, [T, P, i32, P, i32, i32, P, P]),
         "vq_last_error": (ctypes.c_char_p, []),
         "vq_status_name": (ctypes.c_char_p, [i32]),
     }
@@ -73,7 +74,8 @@ def _load():
 LIB = _load()
 
 EXPORTED = ("vq_words_per_row", "vq_dequant", "vq_gemv", "vq_gemm", "vq_moe_gemv",
-            "vq_moe_workspace_bytes", "vq_moe_gemm", "vq_last_error", "vq_status_name")
+            "vq_moe_workspace_bytes", "vq_moe_gemm", "vq_moe_gemm_no_alloc", "vq_last_error",
+            "vq_status_name")
 
 
 def check(status: int) -> None:
@@ -248,3 +250,12 @@ def moe_gemm(w: VQTensor, x, ids, x_per_slot=False, y=None, workspace=None, stre
                           _ptr(y), _ptr(workspace), workspace.numel(), _stream(stream)))
     return y
 
+
+def moe_gemm_no_alloc(w: VQTensor, x, ids, x_per_slot=False, y=None, stream=None):
+    """vq_moe_gemm_no_alloc: vq_moe_gemm with the library's static scratch
+    instead of a workspace (allocates nothing when y is given)."""
+    T, top_k, y = _moe_prep(w, x, ids, x_per_slot, y)
+    cs = w.cstruct()
+    check(LIB.vq_moe_gemm_no_alloc(ctypes.byref(cs), _ptr(x), int(bool(x_per_slot)), _ptr(ids), T, top_k,
+                                   _ptr(y), _stream(stream)))
+    return y

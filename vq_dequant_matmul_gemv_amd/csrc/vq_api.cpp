@@ -261,4 +261,25 @@ vq_status vq_moe_gemm(const vq_tensor* w, const uint16_t* x, int32_t x_per_slot,
                     "vq_moe_gemm launch");
 }
 
+vq_status vq_moe_gemm_no_alloc(const vq_tensor* w, const uint16_t* x, int32_t x_per_slot,
+                                const int32_t* expert_ids, int32_t T, int32_t top_k, float* y,
+                                void* stream) {
+  vqmi::TensorView v;
+  vq_status st = check_moe(w, x, x_per_slot, expert_ids, T, top_k, y, &v);
+  if (st != VQ_OK || T == 0) return st;
+  if (w->num_experts > 1 << 20) return fail(VQ_ERR_SHAPE, "num_experts too large");
+  const size_t need = vqmi::moe_workspace_bytes(T, top_k, w->num_experts);
+  if (need > vqmi::kStaticScratchBytes)
+    return fail(VQ_ERR_WORKSPACE,
+                "vq_moe_gemm_no_alloc: T=%d top_k=%d num_experts=%d need %zu bytes of scratch, more than "
+                "the %zu bytes of the library's static scratch; use vq_moe_gemm with a workspace",
+                T, top_k, w->num_experts, need, vqmi::kStaticScratchBytes);
+  void* scratch = nullptr;
+  st = hip_status(vqmi::static_scratch(&scratch), "vq_moe_gemm_no_alloc: static scratch address");
+  if (st != VQ_OK) return st;
+  return hip_status(vqmi::launch_moe_gemm(v, x, x_per_slot, expert_ids, T, top_k, y, scratch,
+                                          (hipStream_t)stream),
+                    "vq_moe_gemm_no_alloc launch");
+}
+
 }  // extern "C"

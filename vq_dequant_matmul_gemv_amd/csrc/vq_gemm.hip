@@ -49,6 +49,7 @@
 #include "vq_kernels.h"
 
 #include <algorithm>
+#include <mutex>
 
 namespace vqmi {
 
@@ -844,6 +845,40 @@ hipError_t moe_gemm_geom(const TensorView& w, const uint16_t* x, int x_per_slot,
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// Static scratch for callers that cannot allocate (vq_moe_gemm_no_alloc): the
+// routing workspace lives in this file-scope device array, one copy per GPU,
+// held until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the device symbol): the device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current, and is kept per device.
+// ---------------------------------------------------------------------------
+
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 size_t moe_workspace_bytes(int T, int top_k, int num_experts) {
   const int64_t npairs = (int64_t)T * top_k;

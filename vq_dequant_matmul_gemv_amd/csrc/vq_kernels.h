@@ -27,6 +27,11 @@ hipError_t launch_gemv(const TensorView& w, const uint16_t* x, int T, float* y,
 hipError_t launch_gemm(const TensorView& w, const uint16_t* x, int T, float* y, hipStream_t s);
 
 size_t moe_workspace_bytes(int T, int top_k, int num_experts);
+
+// Bytes of the library's static device scratch array (one per GPU), and its
+// address on the current device (looked up once per device).
+constexpr size_t kStaticScratchBytes = (size_t)4 << 20;
+hipError_t static_scratch(void** out);
 hipError_t launch_moe_gemm(const TensorView& w, const uint16_t* x, int x_per_slot,
                            const int32_t* ids, int T, int top_k, float* y, void* ws,
                            hipStream_t s);
