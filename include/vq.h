@@ -106,6 +106,55 @@ typedef struct vq_tensor {
   int64_t scale_elems;      /* number of fp16 values behind `scales`             */
 } vq_tensor;
 
+/*
+ * Input/output types and fused output steps of one call (the *_ex entry
+ * points; the plain entry points are x fp16, y fp32, no epilogue).
+ *
+ *   x_dtype: VQ_DTYPE_F16 or VQ_DTYPE_BF16 (bit patterns).  The runtime the
+ *     paper scores takes and returns bf16 (paper, §7 Reproducibility: the v2
+ *     profile).  bf16 x is converted to fp16 as it is staged (round to nearest
+ *     even): exact for 2^-17 <= |x| <= 65504 and for 0; smaller magnitudes
+ *     lose low bits (at most 2^-25 absolutely), larger ones become +-inf.
+ *   y_dtype: VQ_DTYPE_F32, VQ_DTYPE_F16 or VQ_DTYPE_BF16: the fp32 results
+ *     (or the SwiGLU value below) rounded to nearest even on the final store.
+ *   epilogue:
+ *     VQ_EPILOGUE_NONE    y = x W^T as for the plain calls.
+ *     VQ_EPILOGUE_SWIGLU  the gate and up projections of an MLP stored as one
+ *       tensor of 2I interleaved rows (row 2i = gate row i, row 2i + 1 = up
+ *       row i; rows must be even): y[..][i] = silu(g_i) * u_i with g, u the
+ *       fp32 results and silu(g) = g / (1 + exp(-g)); y has rows / 2 values
+ *       per token (dense) or per (token, slot) (routed).  The paper (§2.1)
+ *       quantizes the MLP trio, the gate, up and down projections; the
+ *       activation between them is not stated, and SiLU gating (SwiGLU), that
+ *       of the model family the pages quantize, is the reading taken.  Gate
+ *       and up share x, so both are read in one pass and the activation
+ *       never leaves the kernel.
+ *     VQ_EPILOGUE_COMBINE routed calls only: y[t][r] = sum over the slots s
+ *       of token t with 0 <= ids[t][s] < E of route_weights[t][s] *
+ *       (W_e x_row)[r], the router-weighted top-k combine; y is [T][rows],
+ *       y_dtype must be VQ_DTYPE_F32.  The library zeroes y on the stream
+ *       first and the slots add into it atomically, so the fp32 addition
+ *       order over slots, and with it the last bits, may vary between runs.
+ *   route_weights: device [T][top_k] fp32, 4-byte aligned (COMBINE only;
+ *     otherwise ignored).
+ * Errors (VQ_ERR_SHAPE): an unknown dtype or epilogue; SWIGLU on odd rows;
+ * COMBINE on a dense call or with y_dtype != F32; VQ_ERR_NULL / VQ_ERR_ALIGN
+ * for route_weights.  The streaming GEMV holds at most 20480 input features
+ * per pass over x and adds further slices into an fp32 y, so vq_gemv_ex /
+ * vq_moe_gemv_ex with cols > 20480 accept only y_dtype F32 and no SWIGLU.
+ * A NULL io means the defaults.
+ */
+typedef enum { VQ_DTYPE_F32 = 0, VQ_DTYPE_F16 = 1, VQ_DTYPE_BF16 = 2 } vq_dtype;
+typedef enum { VQ_EPILOGUE_NONE = 0, VQ_EPILOGUE_SWIGLU = 1, VQ_EPILOGUE_COMBINE = 2 } vq_epilogue;
+
+typedef struct vq_io {
+  int32_t x_dtype;             /* vq_dtype: F16 (default) or BF16                  */
+  int32_t y_dtype;             /* vq_dtype: F32 (default), F16 or BF16             */
+  int32_t epilogue;            /* vq_epilogue                                     */
+  int32_t reserved;            /* must be 0                                       */
+  const float *route_weights;  /* COMBINE: device [T][top_k] fp32 router weights  */
+} vq_io;
+
 /* uint32 words per row of packed codes: ceil(cols/d/32) * log2_k.  Returns -1
  * for a non-positive cols or an unsupported d / log2_k. */
 int32_t vq_words_per_row(int32_t cols, int32_t d, int32_t log2_k);
@@ -172,6 +221,19 @@ vq_status vq_moe_gemv(const vq_tensor *w, const uint16_t *x, int32_t x_per_slot,
                       const int32_t *expert_ids, int32_t T, int32_t top_k, float *y,
                       void *stream);
 
+/*
+ * The calls above with the input/output types and epilogue of `io` (see
+ * vq_io).  x and y are typeless device pointers whose element types `io`
+ * names; shapes and alignment as for the plain calls, y's row length
+ * rows / 2 under SWIGLU and y [T][rows] under COMBINE.
+ */
+vq_status vq_gemv_ex(const vq_tensor *w, const vq_io *io, const void *x, int32_t T, void *y,
+                     void *stream);
+vq_status vq_gemm_ex(const vq_tensor *w, const vq_io *io, const void *x, int32_t T, void *y,
+                     void *stream);
+vq_status vq_moe_gemv_ex(const vq_tensor *w, const vq_io *io, const void *x, int32_t x_per_slot,
+                         const int32_t *expert_ids, int32_t T, int32_t top_k, void *y, void *stream);
+
 /* Bytes of workspace vq_moe_gemm needs for these sizes (0 if T*top_k == 0);
  * returns 0 and sets the error text for negative or overflowing sizes. */
 size_t vq_moe_workspace_bytes(int32_t T, int32_t top_k, int32_t num_experts);
@@ -194,6 +256,11 @@ size_t vq_moe_workspace_bytes(int32_t T, int32_t top_k, int32_t num_experts);
 vq_status vq_moe_gemm(const vq_tensor *w, const uint16_t *x, int32_t x_per_slot,
                       const int32_t *expert_ids, int32_t T, int32_t top_k, float *y,
                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* vq_moe_gemm with the input/output types and epilogue of `io`. */
+vq_status vq_moe_gemm_ex(const vq_tensor *w, const vq_io *io, const void *x, int32_t x_per_slot,
+                         const int32_t *expert_ids, int32_t T, int32_t top_k, void *y,
+                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * vq_moe_gemm for callers that cannot allocate device memory (code under HIP

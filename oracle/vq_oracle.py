@@ -38,6 +38,15 @@ size K, B = log2 K bits per code; W is [rows = out][cols = in]):
 3. matmul: ref[t][r] = sum_c f64(W[r][c]) * f64(x[t][c]) in float64.
 4. MoE: ref[t][s] = W_e @ xrow for e = ids[t][s] when 0 <= e < E, where xrow
    is x[t] (shared input) or x[t][s] (per-slot input); otherwise a zero row.
+5. bf16 activations ([paper] §7 Reproducibility: the scored runtime profile
+   takes and returns bf16): a bf16 bit pattern is the upper half of an IEEE
+   binary32 value; the matmul uses that value exactly.
+6. SwiGLU on the MLP trio's gate and up outputs ([paper] §2.1: the gate, up
+   and down projections; the activation is not on the pages, SiLU gating is
+   the reading): h_i = silu(g_i) * u_i, silu(g) = g / (1 + exp(-g)), with the
+   gate and up rows interleaved (row 2i gate, row 2i + 1 up) in one tensor.
+7. Router-weighted top-k combine: out[t] = sum over the valid slots s of
+   weights[t][s] * ref[t][s].
 
 Readings where the pages are silent (the plainest the rest supports):
   d consecutive weights run along the input dimension of one output row;
@@ -66,6 +75,10 @@ __all__ = [
     "matmul_f64",
     "gemv_ref",
     "moe_ref",
+    "bf16_to_f64",
+    "silu",
+    "swiglu_ref",
+    "moe_combine_ref",
     "ROW_BLOCK",
 ]
 
@@ -216,3 +229,40 @@ def moe_ref(words, codebook, scales, x16, ids, *, cols, d, log2_k, group,
         xrows = x[tt, ss] if x_per_slot else x[tt]
         ref[tt, ss] = matmul_f64(w, xrows)
     return ref
+
+
+# --------------------------------------------------------------------------
+# input / output types and the MLP epilogues
+# --------------------------------------------------------------------------
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Values of bf16 bit patterns (uint16): a bf16 value is the binary32
+    value whose upper 16 bits are the pattern and whose lower 16 are zero."""
+    wide = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return wide.view(np.float32).astype(np.float64)
+
+
+def silu(g) -> np.ndarray:
+    """silu(g) = g / (1 + exp(-g)) in float64."""
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def swiglu_ref(y) -> np.ndarray:
+    """h[..., i] = silu(y[..., 2i]) * y[..., 2i + 1]: the gate and up outputs
+    of a tensor whose rows interleave gate row i (2i) and up row i (2i + 1)."""
+    y = np.asarray(y, dtype=np.float64)
+    assert y.shape[-1] % 2 == 0
+    return silu(y[..., 0::2]) * y[..., 1::2]
+
+
+def moe_combine_ref(y_slots, weights, ids, num_experts: int) -> np.ndarray:
+    """out[t] = sum_s weights[t][s] * y_slots[t][s] over the slots whose id
+    is in [0, num_experts); y_slots [T][top_k][rows], weights and ids
+    [T][top_k].  float64."""
+    y = np.asarray(y_slots, dtype=np.float64)
+    ids = np.asarray(ids)
+    valid = (ids >= 0) & (ids < num_experts)
+    w = np.where(valid, np.asarray(weights, dtype=np.float64), 0.0)
+    return np.einsum("ts,tsr->tr", w, y)

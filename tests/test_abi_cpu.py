@@ -174,3 +174,45 @@ def test_no_alloc_refuses_sizes_beyond_its_scratch_on_the_host(b):
     assert b.STATUS_NAMES[st] == "VQ_ERR_WORKSPACE"
     assert "static scratch" in b.LIB.vq_last_error().decode()
     assert b.LIB.vq_moe_gemm_no_alloc(ctypes.byref(t), 0x40000, 0, 0x70000, 0, top_k, 0x50000, None) == b.VQ_OK
+
+
+def test_io_descriptor_checks(b):
+    """vq_io is validated on the host before anything is enqueued."""
+    L = b.LIB
+
+    def dense(io, fn=L.vq_gemm_ex, **kw):
+        t = _t(b, **kw)
+        return b.STATUS_NAMES[fn(ctypes.byref(t), ctypes.byref(io) if io is not None else None, 0x40000, 2,
+                                 0x50000, None)]
+
+    def routed(io, fn=L.vq_moe_gemv_ex, **kw):
+        t = _t(b, num_experts=4, **kw)
+        if fn is L.vq_moe_gemv_ex:
+            st = fn(ctypes.byref(t), ctypes.byref(io), 0x40000, 0, 0x70000, 2, 2, 0x50000, None)
+        else:
+            st = fn(ctypes.byref(t), ctypes.byref(io), 0x40000, 0, 0x70000, 2, 2, 0x50000, 0x80000, 1 << 20, None)
+        return b.STATUS_NAMES[st]
+
+    io = b.CIo
+    assert dense(io(3, 0, 0, 0, None)) == "VQ_ERR_SHAPE"                 # x dtype
+    assert dense(io(b.VQ_DTYPE_F32, 0, 0, 0, None)) == "VQ_ERR_SHAPE"    # fp32 x is not an input type
+    assert dense(io(1, 5, 0, 0, None)) == "VQ_ERR_SHAPE"                 # y dtype
+    assert dense(io(1, 0, 7, 0, None)) == "VQ_ERR_SHAPE"                 # epilogue
+    assert dense(io(1, 0, 0, 1, None)) == "VQ_ERR_SHAPE"                 # reserved
+    assert dense(io(1, 0, b.VQ_EPILOGUE_SWIGLU, 0, None), rows=15) == "VQ_ERR_SHAPE"   # odd rows
+    assert "interleaved" in L.vq_last_error().decode()
+    assert dense(io(1, 0, b.VQ_EPILOGUE_COMBINE, 0, 0x90000)) == "VQ_ERR_SHAPE"       # dense combine
+    assert routed(io(1, 1, b.VQ_EPILOGUE_COMBINE, 0, 0x90000)) == "VQ_ERR_SHAPE"      # combine -> fp32 only
+    assert routed(io(1, 0, b.VQ_EPILOGUE_COMBINE, 0, None)) == "VQ_ERR_NULL"
+    assert routed(io(1, 0, b.VQ_EPILOGUE_COMBINE, 0, 0x90002)) == "VQ_ERR_ALIGN"
+    # the streaming GEMV holds 20480 input features per pass: wider rows only
+    # with a plain fp32 y (the GEMM takes any output type)
+    wide = dict(cols=20480 + 128, codebook_elems=512)
+    assert dense(io(1, b.VQ_DTYPE_BF16, 0, 0, None), fn=L.vq_gemv_ex, **wide) == "VQ_ERR_SHAPE"
+    assert dense(io(1, 0, b.VQ_EPILOGUE_SWIGLU, 0, None), fn=L.vq_gemv_ex, **wide) == "VQ_ERR_SHAPE"
+    # valid descriptors pass validation (T = 0 enqueues nothing)
+    t = _t(b)
+    for good in (io(b.VQ_DTYPE_BF16, b.VQ_DTYPE_BF16, 0, 0, None), io(1, b.VQ_DTYPE_F16, 1, 0, None), None):
+        st = L.vq_gemv_ex(ctypes.byref(t), ctypes.byref(good) if good is not None else None, 0x40000, 0,
+                          0x50000, None)
+        assert st == b.VQ_OK, L.vq_last_error()

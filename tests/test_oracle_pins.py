@@ -492,3 +492,85 @@ def test_moe_per_expert_codebooks():
             e = ids[ti, s]
             want = O.gemv_ref(t["codes"][e], t["codebook"][e], t["scales"][e], x[ti][None], 64, 2, 8, 64)
             assert np.array_equal(ref[ti, s], want[0])
+
+
+# --------------------------------------------------------------------------
+# bf16 activations, SwiGLU and the router-weighted combine
+# --------------------------------------------------------------------------
+
+def _bf16_value_from_fields(h: int) -> float:
+    """Value of a bf16 pattern from its fields (1 sign, 8 exponent, 7
+    mantissa bits, bias 127), written from the format's definition."""
+    sign = -1.0 if h >> 15 else 1.0
+    exp = (h >> 7) & 0xFF
+    man = h & 0x7F
+    if exp == 0xFF:
+        return sign * math.inf if man == 0 else math.nan
+    if exp == 0:
+        return sign * math.ldexp(man, -133)          # subnormal: man * 2^(1 - 127 - 7)
+    return sign * math.ldexp(128 + man, exp - 134)   # (1 + man/128) * 2^(exp - 127)
+
+
+def test_bf16_values_from_the_format_definition():
+    pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = O.bf16_to_f64(pats)
+    want = np.array([_bf16_value_from_fields(int(h)) for h in pats])
+    finite = ~np.isnan(want)
+    assert np.array_equal(got[finite], want[finite])
+    assert np.all(np.isnan(got[~finite]))
+    assert O.bf16_to_f64([0x3F80, 0xC040, 0x4049])[:].tolist() == [1.0, -3.0, 3.140625]
+
+
+def test_silu_closed_forms():
+    assert O.silu(0.0) == 0.0
+    assert O.silu(1.0) == pytest.approx(1.0 / (1.0 + 1.0 / math.e), rel=1e-15)
+    x = np.linspace(-30, 30, 601)
+    # sigma(x) + sigma(-x) = 1, so silu(x) - silu(-x) = x
+    assert np.allclose(O.silu(x) - O.silu(-x), x, rtol=0, atol=1e-13)
+    assert O.silu(60.0) == 60.0 and 0 > O.silu(-60.0) > -1e-24
+    from scipy.special import expit                  # an independent logistic routine
+    assert np.allclose(O.silu(x), x * expit(x), rtol=1e-14, atol=1e-300)
+
+
+def test_swiglu_pairs_interleaved_gate_and_up_rows():
+    # rows: gate0, up0, gate1, up1 -> silu(gate_i) * up_i
+    y = np.array([[0.0, 5.0, 2.0, -1.0], [-3.0, 0.5, 1.0, 4.0]])
+    s2 = 2.0 / (1.0 + math.exp(-2.0))
+    want = np.array([[0.0, -s2], [-3.0 / (1.0 + math.exp(3.0)) * 0.5, 4.0 / (1.0 + math.exp(-1.0))]])
+    assert np.allclose(O.swiglu_ref(y), want, rtol=1e-15, atol=0)
+    # gate and up are not interchangeable
+    assert not np.allclose(O.swiglu_ref(y[:, [1, 0, 3, 2]]), want)
+
+
+def test_moe_combine_brute_force_and_skips():
+    rng = synth.rng("pin-combine")
+    T, k, rows, E = 5, 3, 7, 4
+    y = rng.normal(size=(T, k, rows))
+    w = rng.uniform(0, 1, size=(T, k))
+    ids = rng.integers(0, E, size=(T, k))
+    ids[1, 2] = -1
+    ids[3, 0] = E                                   # out of range
+    want = np.zeros((T, rows))
+    for t in range(T):
+        for s in range(k):
+            if 0 <= ids[t, s] < E:
+                for r in range(rows):
+                    want[t, r] += w[t, s] * y[t, s, r]
+    assert np.allclose(O.moe_combine_ref(y, w, ids, E), want, rtol=1e-14, atol=1e-14)
+    # the slot order does not matter
+    perm = [2, 0, 1]
+    assert np.allclose(O.moe_combine_ref(y[:, perm], w[:, perm], ids[:, perm], E), want, rtol=1e-14, atol=1e-14)
+
+
+def test_moe_combine_of_routed_dense_rows():
+    """Every slot of a token on one expert with weights summing to one: the
+    combine is that expert's dense product."""
+    spec = synth.Spec(rows=12, cols=64, d=2, log2_k=8, group=64, experts=3)
+    a = synth.tensor(spec, "pin-combine-dense")
+    x = synth.activations((4, 64), "pin-combine-dense")
+    ids = np.full((4, 2), 1)
+    w = np.array([[0.25, 0.75]] * 4)
+    ys = O.moe_ref(a["codes"], a["codebook"], a["scales"], x, ids, cols=64, d=2, log2_k=8, group=64,
+                   x_per_slot=False)
+    dense = O.gemv_ref(a["codes"][1], a["codebook"], a["scales"][1], x, 64, 2, 8, 64)
+    assert np.allclose(O.moe_combine_ref(ys, w, ids, 3), dense, rtol=1e-14, atol=1e-14)

@@ -26,6 +26,23 @@ class VQError(RuntimeError):
         self.message = message
 
 
+VQ_DTYPE_F32, VQ_DTYPE_F16, VQ_DTYPE_BF16 = 0, 1, 2
+VQ_EPILOGUE_NONE, VQ_EPILOGUE_SWIGLU, VQ_EPILOGUE_COMBINE = 0, 1, 2
+EPILOGUES = {None: VQ_EPILOGUE_NONE, "none": VQ_EPILOGUE_NONE, "swiglu": VQ_EPILOGUE_SWIGLU,
+             "combine": VQ_EPILOGUE_COMBINE}
+
+
+class CIo(ctypes.Structure):
+    """Mirror of `vq_io`."""
+    _fields_ = [
+        ("x_dtype", ctypes.c_int32),
+        ("y_dtype", ctypes.c_int32),
+        ("epilogue", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("route_weights", ctypes.c_void_p),
+    ]
+
+
 class CTensor(ctypes.Structure):
     """Mirror of `vq_tensor`."""
     _fields_ = [
@@ -52,7 +69,12 @@ def _load():
     P = ctypes.c_void_p
     i32 = ctypes.c_int32
     T = ctypes.POINTER(CTensor)
+    IO = ctypes.POINTER(CIo)
     sig = {
+        "vq_gemv_ex": (i32, [T, IO, P, i32, P, P]),
+        "vq_gemm_ex": (i32, [T, IO, P, i32, P, P]),
+        "vq_moe_gemv_ex": (i32, [T, IO, P, i32, P, i32, i32, P, P]),
+        "vq_moe_gemm_ex": (i32, [T, IO, P, i32, P, i32, i32, P, P, ctypes.c_size_t, P]),
         "vq_words_per_row": (i32, [i32, i32, i32]),
         "vq_dequant": (i32, [T, i32, P, P]),
         "vq_gemv": (i32, [T, P, i32, P, P]),
@@ -73,7 +95,8 @@ def _load():
 
 LIB = _load()
 
-EXPORTED = ("vq_words_per_row", "vq_dequant", "vq_gemv", "vq_gemm", "vq_moe_gemv",
+EXPORTED = ("vq_words_per_row", "vq_dequant", "vq_gemv", "vq_gemm", "vq_moe_gemv", "vq_gemv_ex",
+            "vq_gemm_ex", "vq_moe_gemv_ex", "vq_moe_gemm_ex",
             "vq_moe_workspace_bytes", "vq_moe_gemm", "vq_moe_gemm_no_alloc", "vq_last_error",
             "vq_status_name")
 
@@ -191,70 +214,131 @@ def dequant(w: VQTensor, expert: int = 0, out=None, stream=None):
     return out
 
 
-def _dense(fn, w: VQTensor, x, y, stream):
+def _dtype_code(dt):
     torch = _torch()
-    if x.dtype != torch.float16 or x.dim() != 2 or x.shape[1] != w.cols:
-        raise ValueError("x must be fp16 [T][cols]")
+    codes = {torch.float32: VQ_DTYPE_F32, torch.float16: VQ_DTYPE_F16, torch.bfloat16: VQ_DTYPE_BF16}
+    if dt not in codes:
+        raise ValueError(f"unsupported dtype {dt}")
+    return codes[dt]
+
+
+def _io(x, y_dtype, epilogue, route_weights):
+    """The vq_io of a call, or None for the plain call (fp16 x, fp32 y)."""
+    torch = _torch()
+    if epilogue not in EPILOGUES:
+        raise ValueError(f"epilogue must be one of {sorted(k for k in EPILOGUES if k)}")
+    epi = EPILOGUES[epilogue]
+    if x.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("x must be fp16 or bf16")
+    if x.dtype == torch.float16 and y_dtype == torch.float32 and epi == VQ_EPILOGUE_NONE:
+        return None
+    rw = 0
+    if epi == VQ_EPILOGUE_COMBINE:
+        if route_weights is None or route_weights.dtype != torch.float32:
+            raise ValueError("the combine needs fp32 route_weights [T][top_k]")
+        rw = route_weights.data_ptr()
+    return CIo(_dtype_code(x.dtype), _dtype_code(y_dtype), epi, 0, rw)
+
+
+def _dense(fn, fn_ex, w: VQTensor, x, y, stream, y_dtype=None, epilogue=None):
+    torch = _torch()
+    if x.dtype not in (torch.float16, torch.bfloat16) or x.dim() != 2 or x.shape[1] != w.cols:
+        raise ValueError("x must be fp16 or bf16 [T][cols]")
     T = x.shape[0]
+    y_dtype = y.dtype if (y is not None and y_dtype is None) else (y_dtype or torch.float32)
+    ycols = w.rows // 2 if epilogue == "swiglu" else w.rows
+    if epilogue == "combine":
+        raise ValueError("the combine applies to routed calls only")
     if y is None:
-        y = torch.empty((T, w.rows), dtype=torch.float32, device=x.device)
-    _check_out(y, torch.float32, (T, w.rows))
+        y = torch.empty((T, ycols), dtype=y_dtype, device=x.device)
+    _check_out(y, y_dtype, (T, ycols))
     _dev_check(x, y, device=w.device)
     cs = w.cstruct()
-    check(fn(ctypes.byref(cs), _ptr(x), T, _ptr(y), _stream(stream)))
+    io = _io(x, y_dtype, epilogue, None)
+    if io is None:
+        check(fn(ctypes.byref(cs), _ptr(x), T, _ptr(y), _stream(stream)))
+    else:
+        check(fn_ex(ctypes.byref(cs), ctypes.byref(io), _ptr(x), T, _ptr(y), _stream(stream)))
     return y
 
 
-def gemv(w: VQTensor, x, y=None, stream=None):
-    """y[T][rows] = x W^T through vq_gemv."""
-    return _dense(LIB.vq_gemv, w, x, y, stream)
+def gemv(w: VQTensor, x, y=None, stream=None, y_dtype=None, epilogue=None):
+    """y = x W^T through vq_gemv (vq_gemv_ex for bf16 x, a non-fp32 y or an
+    epilogue: "swiglu" on interleaved gate/up rows gives silu(gate) * up)."""
+    return _dense(LIB.vq_gemv, LIB.vq_gemv_ex, w, x, y, stream, y_dtype, epilogue)
 
 
-def gemm(w: VQTensor, x, y=None, stream=None):
-    """y[T][rows] = x W^T through vq_gemm (MFMA)."""
-    return _dense(LIB.vq_gemm, w, x, y, stream)
+def gemm(w: VQTensor, x, y=None, stream=None, y_dtype=None, epilogue=None):
+    """y = x W^T through vq_gemm (MFMA); options as for gemv."""
+    return _dense(LIB.vq_gemm, LIB.vq_gemm_ex, w, x, y, stream, y_dtype, epilogue)
 
 
-def _moe_prep(w, x, ids, x_per_slot, y):
+def _moe_prep(w, x, ids, x_per_slot, y, y_dtype=None, epilogue=None):
     torch = _torch()
     T, top_k = ids.shape
     if ids.dtype != torch.int32:
         raise ValueError("expert ids must be int32 [T][top_k]")
     want = (T, top_k, w.cols) if x_per_slot else (T, w.cols)
-    if x.dtype != torch.float16 or tuple(x.shape) != want:
-        raise ValueError(f"x must be fp16 {want}")
+    if x.dtype not in (torch.float16, torch.bfloat16) or tuple(x.shape) != want:
+        raise ValueError(f"x must be fp16 or bf16 {want}")
+    y_dtype = y.dtype if (y is not None and y_dtype is None) else (y_dtype or torch.float32)
+    if epilogue == "combine":
+        yshape = (T, w.rows)
+    else:
+        yshape = (T, top_k, w.rows // 2 if epilogue == "swiglu" else w.rows)
     if y is None:
-        y = torch.empty((T, top_k, w.rows), dtype=torch.float32, device=x.device)
-    _check_out(y, torch.float32, (T, top_k, w.rows))
+        y = torch.empty(yshape, dtype=y_dtype, device=x.device)
+    _check_out(y, y_dtype, yshape)
     _dev_check(x, ids, y, device=w.device)
-    return T, top_k, y
+    return T, top_k, y, y_dtype
 
 
-def moe_gemv(w: VQTensor, x, ids, x_per_slot=False, y=None, stream=None):
-    T, top_k, y = _moe_prep(w, x, ids, x_per_slot, y)
+def moe_gemv(w: VQTensor, x, ids, x_per_slot=False, y=None, stream=None, y_dtype=None, epilogue=None,
+             route_weights=None):
+    """Routed experts, decode-shaped (vq_moe_gemv / vq_moe_gemv_ex).  epilogue
+    "combine" with fp32 route_weights [T][top_k] gives y [T][rows] = the
+    router-weighted sum over each token's slots."""
+    T, top_k, y, y_dtype = _moe_prep(w, x, ids, x_per_slot, y, y_dtype, epilogue)
+    if route_weights is not None:
+        _dev_check(route_weights, device=w.device)
     cs = w.cstruct()
-    check(LIB.vq_moe_gemv(ctypes.byref(cs), _ptr(x), int(bool(x_per_slot)), _ptr(ids), T, top_k,
-                          _ptr(y), _stream(stream)))
+    io = _io(x, y_dtype, epilogue, route_weights)
+    if io is None:
+        check(LIB.vq_moe_gemv(ctypes.byref(cs), _ptr(x), int(bool(x_per_slot)), _ptr(ids), T, top_k,
+                              _ptr(y), _stream(stream)))
+    else:
+        check(LIB.vq_moe_gemv_ex(ctypes.byref(cs), ctypes.byref(io), _ptr(x), int(bool(x_per_slot)), _ptr(ids),
+                                 T, top_k, _ptr(y), _stream(stream)))
     return y
 
 
-def moe_gemm(w: VQTensor, x, ids, x_per_slot=False, y=None, workspace=None, stream=None):
+def moe_gemm(w: VQTensor, x, ids, x_per_slot=False, y=None, workspace=None, stream=None, y_dtype=None,
+             epilogue=None, route_weights=None):
+    """Routed experts, prefill-shaped (vq_moe_gemm / vq_moe_gemm_ex); options
+    as for moe_gemv."""
     torch = _torch()
-    T, top_k, y = _moe_prep(w, x, ids, x_per_slot, y)
+    T, top_k, y, y_dtype = _moe_prep(w, x, ids, x_per_slot, y, y_dtype, epilogue)
+    if route_weights is not None:
+        _dev_check(route_weights, device=w.device)
     need = workspace_bytes(T, top_k, w.num_experts)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
     _dev_check(workspace, device=w.device)
     cs = w.cstruct()
-    check(LIB.vq_moe_gemm(ctypes.byref(cs), _ptr(x), int(bool(x_per_slot)), _ptr(ids), T, top_k,
-                          _ptr(y), _ptr(workspace), workspace.numel(), _stream(stream)))
+    io = _io(x, y_dtype, epilogue, route_weights)
+    if io is None:
+        check(LIB.vq_moe_gemm(ctypes.byref(cs), _ptr(x), int(bool(x_per_slot)), _ptr(ids), T, top_k,
+                              _ptr(y), _ptr(workspace), workspace.numel(), _stream(stream)))
+    else:
+        check(LIB.vq_moe_gemm_ex(ctypes.byref(cs), ctypes.byref(io), _ptr(x), int(bool(x_per_slot)), _ptr(ids),
+                                 T, top_k, _ptr(y), _ptr(workspace), workspace.numel(), _stream(stream)))
     return y
 
 
 def moe_gemm_no_alloc(w: VQTensor, x, ids, x_per_slot=False, y=None, stream=None):
     """vq_moe_gemm_no_alloc: vq_moe_gemm with the library's static scratch
     instead of a workspace (allocates nothing when y is given)."""
-    T, top_k, y = _moe_prep(w, x, ids, x_per_slot, y)
+    T, top_k, y, _ = _moe_prep(w, x, ids, x_per_slot, y)
     cs = w.cstruct()
     check(LIB.vq_moe_gemm_no_alloc(ctypes.byref(cs), _ptr(x), int(bool(x_per_slot)), _ptr(ids), T, top_k,
                                    _ptr(y), _stream(stream)))

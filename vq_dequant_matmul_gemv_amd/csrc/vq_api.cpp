@@ -122,8 +122,50 @@ vq_status hip_status(hipError_t e, const char* what) {
   return fail(VQ_ERR_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
 }
 
+// Largest input width the streaming GEMV covers in one pass over x; wider
+// rows run in column slices that add into an fp32 y.
+constexpr int32_t kGemvOnePassCols = 20480;
+
+enum class Call { kGemv, kGemm, kMoeGemv, kMoeGemm };
+
+// Validates an I/O descriptor (NULL = defaults) for a call on `w`.
+vq_status check_io(const vq_io* io, const vq_tensor* w, Call call, vqmi::IoSpec* out) {
+  *out = vqmi::IoSpec{};
+  if (!io) return VQ_OK;
+  const bool routed = call == Call::kMoeGemv || call == Call::kMoeGemm;
+  if (io->x_dtype != VQ_DTYPE_F16 && io->x_dtype != VQ_DTYPE_BF16)
+    return fail(VQ_ERR_SHAPE, "io->x_dtype=%d: x must be VQ_DTYPE_F16 or VQ_DTYPE_BF16", io->x_dtype);
+  if (io->y_dtype != VQ_DTYPE_F32 && io->y_dtype != VQ_DTYPE_F16 && io->y_dtype != VQ_DTYPE_BF16)
+    return fail(VQ_ERR_SHAPE, "io->y_dtype=%d is not a vq_dtype", io->y_dtype);
+  if (io->epilogue != VQ_EPILOGUE_NONE && io->epilogue != VQ_EPILOGUE_SWIGLU && io->epilogue != VQ_EPILOGUE_COMBINE)
+    return fail(VQ_ERR_SHAPE, "io->epilogue=%d is not a vq_epilogue", io->epilogue);
+  if (io->reserved != 0) return fail(VQ_ERR_SHAPE, "io->reserved must be 0");
+  if (io->epilogue == VQ_EPILOGUE_SWIGLU && w->rows % 2 != 0)
+    return fail(VQ_ERR_SHAPE, "SWIGLU needs interleaved (gate, up) row pairs: rows=%d is odd", w->rows);
+  if (io->epilogue == VQ_EPILOGUE_COMBINE) {
+    if (!routed) return fail(VQ_ERR_SHAPE, "COMBINE applies to routed calls (vq_moe_*) only");
+    if (io->y_dtype != VQ_DTYPE_F32)
+      return fail(VQ_ERR_SHAPE, "COMBINE adds the slots into an fp32 y: y_dtype must be VQ_DTYPE_F32");
+    if (!io->route_weights) return fail(VQ_ERR_NULL, "COMBINE needs route_weights");
+    if (!aligned(io->route_weights, 4)) return fail(VQ_ERR_ALIGN, "route_weights is not 4-byte aligned");
+  }
+  const bool plain_f32 = io->y_dtype == VQ_DTYPE_F32 && io->epilogue != VQ_EPILOGUE_SWIGLU;
+  if ((call == Call::kGemv || call == Call::kMoeGemv) && w->cols > kGemvOnePassCols && !plain_f32)
+    return fail(VQ_ERR_SHAPE,
+                "cols=%d: the streaming GEMV adds column slices above %d input features into an fp32 y, so "
+                "it takes y_dtype F32 without SWIGLU there (use the GEMM entry point)",
+                w->cols, kGemvOnePassCols);
+  out->x_bf16 = io->x_dtype == VQ_DTYPE_BF16;
+  out->y_kind = io->y_dtype == VQ_DTYPE_F32 ? vqmi::kOutF32 : io->y_dtype == VQ_DTYPE_F16 ? vqmi::kOutF16
+                                                                                          : vqmi::kOutBF16;
+  out->epi = io->epilogue == VQ_EPILOGUE_SWIGLU ? vqmi::kEpiSwiglu
+             : io->epilogue == VQ_EPILOGUE_COMBINE ? vqmi::kEpiCombine : vqmi::kEpiNone;
+  out->route_w = io->route_weights;
+  return VQ_OK;
+}
+
 vq_status check_moe(const vq_tensor* w, const void* x, int32_t x_per_slot, const int32_t* ids,
-                    int32_t T, int32_t top_k, const float* y, vqmi::TensorView* v) {
+                    int32_t T, int32_t top_k, const void* y, vqmi::TensorView* v) {
   vq_status st = check_tensor(w, v);
   if (st != VQ_OK) return st;
   if (T < 0) return fail(VQ_ERR_SHAPE, "T=%d must be >= 0", T);
@@ -189,50 +231,64 @@ static int gemv_token_limit(const vqmi::TensorView& v) {
   return 1;
 }
 
-vq_status vq_gemv(const vq_tensor* w, const uint16_t* x, int32_t T, float* y, void* stream) {
+static vq_status dense_call(const vq_tensor* w, const vq_io* io, const void* x, int32_t T, void* y,
+                           void* stream, bool gemv) {
   vqmi::TensorView v;
   vq_status st = check_tensor(w, &v);
   if (st != VQ_OK) return st;
+  const char* name = gemv ? "vq_gemv" : "vq_gemm";
   if (w->num_experts != 1)
-    return fail(VQ_ERR_SHAPE, "vq_gemv needs a dense tensor (num_experts=%d); use vq_moe_gemv",
+    return fail(VQ_ERR_SHAPE, "%s needs a dense tensor (num_experts=%d); use the routed call", name,
                 w->num_experts);
+  vqmi::IoSpec ios;
+  st = check_io(io, w, gemv ? Call::kGemv : Call::kGemm, &ios);
+  if (st != VQ_OK) return st;
   if (T < 0) return fail(VQ_ERR_SHAPE, "T=%d must be >= 0", T);
   if (T > (1 << 24)) return fail(VQ_ERR_SHAPE, "T=%d too large", T);
   if (T == 0) return VQ_OK;
   st = check_xy(x, y, "y");
   if (st != VQ_OK) return st;
-  if (T > gemv_token_limit(v))  // above the crossover the MFMA kernel is faster
-    return hip_status(vqmi::launch_gemm(v, x, T, y, (hipStream_t)stream), "vq_gemv (MFMA path) launch");
-  return hip_status(vqmi::launch_gemv(v, x, T, y, nullptr, 0, 0, (hipStream_t)stream),
-                    "vq_gemv launch");
+  if (!gemv || T > gemv_token_limit(v))  // above the crossover the MFMA kernel is faster
+    return hip_status(vqmi::launch_gemm(v, ios, x, T, y, (hipStream_t)stream),
+                      gemv ? "vq_gemv (MFMA path) launch" : "vq_gemm launch");
+  return hip_status(vqmi::launch_gemv(v, ios, x, T, y, nullptr, 0, 0, (hipStream_t)stream), "vq_gemv launch");
+}
+
+vq_status vq_gemv(const vq_tensor* w, const uint16_t* x, int32_t T, float* y, void* stream) {
+  return dense_call(w, nullptr, x, T, y, stream, true);
 }
 
 vq_status vq_gemm(const vq_tensor* w, const uint16_t* x, int32_t T, float* y, void* stream) {
+  return dense_call(w, nullptr, x, T, y, stream, false);
+}
+
+vq_status vq_gemv_ex(const vq_tensor* w, const vq_io* io, const void* x, int32_t T, void* y, void* stream) {
+  return dense_call(w, io, x, T, y, stream, true);
+}
+
+vq_status vq_gemm_ex(const vq_tensor* w, const vq_io* io, const void* x, int32_t T, void* y, void* stream) {
+  return dense_call(w, io, x, T, y, stream, false);
+}
+
+vq_status vq_moe_gemv_ex(const vq_tensor* w, const vq_io* io, const void* x, int32_t x_per_slot,
+                         const int32_t* expert_ids, int32_t T, int32_t top_k, void* y, void* stream) {
   vqmi::TensorView v;
-  vq_status st = check_tensor(w, &v);
+  vq_status st = check_moe(w, x, x_per_slot, expert_ids, T, top_k, y, &v);
   if (st != VQ_OK) return st;
-  if (w->num_experts != 1)
-    return fail(VQ_ERR_SHAPE, "vq_gemm needs a dense tensor (num_experts=%d); use vq_moe_gemm",
-                w->num_experts);
-  if (T < 0) return fail(VQ_ERR_SHAPE, "T=%d must be >= 0", T);
-  if (T > (1 << 24)) return fail(VQ_ERR_SHAPE, "T=%d too large", T);
-  if (T == 0) return VQ_OK;
-  st = check_xy(x, y, "y");
-  if (st != VQ_OK) return st;
-  return hip_status(vqmi::launch_gemm(v, x, T, y, (hipStream_t)stream), "vq_gemm launch");
+  vqmi::IoSpec ios;
+  st = check_io(io, w, Call::kMoeGemv, &ios);
+  if (st != VQ_OK || T == 0) return st;
+  if ((int64_t)T * top_k > 65535)
+    return fail(VQ_ERR_SHAPE, "vq_moe_gemv: T*top_k=%lld exceeds 65535 pairs; use vq_moe_gemm",
+                (long long)T * top_k);
+  return hip_status(vqmi::launch_gemv(v, ios, x, T, y, expert_ids, top_k, x_per_slot, (hipStream_t)stream),
+                    "vq_moe_gemv launch");
 }
 
 vq_status vq_moe_gemv(const vq_tensor* w, const uint16_t* x, int32_t x_per_slot,
                       const int32_t* expert_ids, int32_t T, int32_t top_k, float* y,
                       void* stream) {
-  vqmi::TensorView v;
-  vq_status st = check_moe(w, x, x_per_slot, expert_ids, T, top_k, y, &v);
-  if (st != VQ_OK || T == 0) return st;
-  if ((int64_t)T * top_k > 65535)
-    return fail(VQ_ERR_SHAPE, "vq_moe_gemv: T*top_k=%lld exceeds 65535 pairs; use vq_moe_gemm",
-                (long long)T * top_k);
-  return hip_status(vqmi::launch_gemv(v, x, T, y, expert_ids, top_k, x_per_slot, (hipStream_t)stream),
-                    "vq_moe_gemv launch");
+  return vq_moe_gemv_ex(w, nullptr, x, x_per_slot, expert_ids, T, top_k, y, stream);
 }
 
 size_t vq_moe_workspace_bytes(int32_t T, int32_t top_k, int32_t num_experts) {
@@ -244,11 +300,14 @@ size_t vq_moe_workspace_bytes(int32_t T, int32_t top_k, int32_t num_experts) {
   return vqmi::moe_workspace_bytes(T, top_k, num_experts);
 }
 
-vq_status vq_moe_gemm(const vq_tensor* w, const uint16_t* x, int32_t x_per_slot,
-                      const int32_t* expert_ids, int32_t T, int32_t top_k, float* y,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+vq_status vq_moe_gemm_ex(const vq_tensor* w, const vq_io* io, const void* x, int32_t x_per_slot,
+                         const int32_t* expert_ids, int32_t T, int32_t top_k, void* y,
+                         void* workspace, size_t workspace_bytes, void* stream) {
   vqmi::TensorView v;
   vq_status st = check_moe(w, x, x_per_slot, expert_ids, T, top_k, y, &v);
+  if (st != VQ_OK) return st;
+  vqmi::IoSpec ios;
+  st = check_io(io, w, Call::kMoeGemm, &ios);
   if (st != VQ_OK || T == 0) return st;
   if (w->num_experts > 1 << 20) return fail(VQ_ERR_SHAPE, "num_experts too large");
   const size_t need = vqmi::moe_workspace_bytes(T, top_k, w->num_experts);
@@ -256,9 +315,16 @@ vq_status vq_moe_gemm(const vq_tensor* w, const uint16_t* x, int32_t x_per_slot,
   if (workspace_bytes < need)
     return fail(VQ_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes, need);
   if (!aligned(workspace, 16)) return fail(VQ_ERR_ALIGN, "workspace is not 16-byte aligned");
-  return hip_status(vqmi::launch_moe_gemm(v, x, x_per_slot, expert_ids, T, top_k, y, workspace,
+  return hip_status(vqmi::launch_moe_gemm(v, ios, x, x_per_slot, expert_ids, T, top_k, y, workspace,
                                           (hipStream_t)stream),
                     "vq_moe_gemm launch");
+}
+
+vq_status vq_moe_gemm(const vq_tensor* w, const uint16_t* x, int32_t x_per_slot,
+                      const int32_t* expert_ids, int32_t T, int32_t top_k, float* y,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return vq_moe_gemm_ex(w, nullptr, x, x_per_slot, expert_ids, T, top_k, y, workspace, workspace_bytes,
+                        stream);
 }
 
 vq_status vq_moe_gemm_no_alloc(const vq_tensor* w, const uint16_t* x, int32_t x_per_slot,
@@ -277,7 +343,7 @@ vq_status vq_moe_gemm_no_alloc(const vq_tensor* w, const uint16_t* x, int32_t x_
   void* scratch = nullptr;
   st = hip_status(vqmi::static_scratch(&scratch), "vq_moe_gemm_no_alloc: static scratch address");
   if (st != VQ_OK) return st;
-  return hip_status(vqmi::launch_moe_gemm(v, x, x_per_slot, expert_ids, T, top_k, y, scratch,
+  return hip_status(vqmi::launch_moe_gemm(v, vqmi::IoSpec{}, x, x_per_slot, expert_ids, T, top_k, y, scratch,
                                           (hipStream_t)stream),
                     "vq_moe_gemm_no_alloc launch");
 }

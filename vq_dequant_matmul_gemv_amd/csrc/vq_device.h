@@ -276,4 +276,39 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
 
+// ---------------------------------------------------------------------------
+// input / output conversions and the fused output step
+// ---------------------------------------------------------------------------
+
+// Two bf16 values (low half first) to two fp16 values, round to nearest even:
+// a bf16 value widens to fp32 exactly, and fp32 -> fp16 rounds once.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  const float lo = __builtin_bit_cast(float, w << 16);
+  const float hi = __builtin_bit_cast(float, w & 0xffff0000u);
+  return as_u32(half2_t{(_Float16)lo, (_Float16)hi});
+}
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
+  return u32x4{bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w)};
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// y[i] = v in the output type (0 fp32, 1 fp16, 2 bf16; round to nearest even).
+__device__ __forceinline__ void store_out(void* out, int64_t i, float v, int kind) {
+  if (kind == 0) reinterpret_cast<float*>(out)[i] = v;
+  else if (kind == 1) reinterpret_cast<_Float16*>(out)[i] = (_Float16)v;
+  else reinterpret_cast<uint16_t*>(out)[i] = f32_to_bf16_bits(v);
+}
+
+// SwiGLU gate: silu(g) * u with silu(g) = g / (1 + exp(-g)).
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g / (1.0f + __expf(-g)) * u;
+}
+
 }  // namespace vqmi

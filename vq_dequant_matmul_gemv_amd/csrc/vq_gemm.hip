@@ -116,7 +116,9 @@ struct GemmArgs {
   const uint16_t* codebook;
   const uint16_t* scales;
   const uint16_t* x;
-  float* y;
+  void* y;                // element type y_kind; shape per epi
+  const float* route_w;   // epi == combine: router weight per pair
+  int x_bf16, y_kind, epi;  // IoSpec
   // routed experts
   const int32_t* tiles;   // [max_tiles][3]: expert, first (into pair list), count
   const int32_t* n_tiles; // device scalar
@@ -303,10 +305,12 @@ __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < XLD; ++i) xr[i] = buf_load_b128(rx, live ? xoff[i] + (uint32_t)ks * SS * 2u : kOutOfRange);
   };
+  const bool x_bf16 = a.x_bf16 != 0;  // bf16 x: converted to fp16 on its way into LDS
   auto store_x = [&](int buf, const u32x4 (&xr)[XLD]) {
 #pragma unroll
     for (int i = 0; i < XLD; ++i)
-      if (xdst[i] >= 0) *reinterpret_cast<u32x4*>(xbuf + buf * (WN * XROW) + xdst[i]) = xr[i];
+      if (xdst[i] >= 0)
+        *reinterpret_cast<u32x4*>(xbuf + buf * (WN * XROW) + xdst[i]) = x_bf16 ? bf16x8_to_f16x8(xr[i]) : xr[i];
   };
   // Scales come in 16-byte windows of 8 groups per row (one load per lane
   // per 8 groups instead of one per super-step; a row's scales are used a
@@ -461,7 +465,9 @@ __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
     auto store_xp = [&](int buf, int p, const u32x4 (&q)[XP]) {
 #pragma unroll
       for (int i = 0; i < XP; ++i)
-        if (xdst[p * XP + i] >= 0) *reinterpret_cast<u32x4*>(xbuf + buf * (WN * XROW) + xdst[p * XP + i]) = q[i];
+        if (xdst[p * XP + i] >= 0)
+          *reinterpret_cast<u32x4*>(xbuf + buf * (WN * XROW) + xdst[p * XP + i]) =
+              x_bf16 ? bf16x8_to_f16x8(q[i]) : q[i];
     };
     auto super_step = [&](int ks, int buf, const LaneCodes<NCL, B> (&cc)[MB], const uint16_t (&sc)[MB],
                           LaneCodes<NCL, B> (&ccn)[MB], uint16_t (&scn)[MB]) {
@@ -545,7 +551,13 @@ __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
   // (l32, h) holds W row row_base + 32*mb + l32 for tokens 32*nb + 8*(i/4) +
   // 4*h + (i%4): for each i a half-wave covers 32 consecutive y elements of
   // one token (128 contiguous bytes), for stores and atomics alike.
+  // Output step (block-uniform branches): SwiGLU pairs rows 2i (gate, even
+  // lane) and 2i + 1 (up, the odd neighbour, fetched by a DPP swap; both
+  // lanes of a pair hold the same tokens) into y[.][i]; the combine adds
+  // router weight x row into y[token]; otherwise y[.][r] in y's type, or an
+  // atomic fp32 add for the K slices of a split tile.
   const int row = row_base + l32;  // + 32 * mb
+  const int epi = a.epi, y_kind = a.y_kind;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
@@ -555,13 +567,22 @@ __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
       int yr;
       if constexpr (MOE) yr = a.pairs[first + tok];
       else yr = tok_base + tok;
-      float* yrow = a.y + (int64_t)yr * a.rows;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const int r = row + 32 * mb;
-        if (r < a.rows) {
-          if (nslices > 1) atomicAdd(yrow + r, acc[mb][nb][i]);  // block-uniform branch
-          else yrow[r] = acc[mb][nb][i];
+        const float v = acc[mb][nb][i];
+        if (epi == kEpiSwiglu) {
+          const float up = dpp_mov<0xB1>(v);  // quad_perm [1,0,3,2]: the odd neighbour's row
+          if ((l32 & 1) == 0 && r < a.rows) store_out(a.y, (int64_t)yr * (a.rows >> 1) + (r >> 1), swiglu(v, up), y_kind);
+        } else if (r < a.rows) {
+          if (epi == kEpiCombine) {
+            if constexpr (MOE)
+              atomicAdd(reinterpret_cast<float*>(a.y) + (int64_t)(yr / a.top_k) * a.rows + r, a.route_w[yr] * v);
+          } else if (nslices > 1) {
+            atomicAdd(reinterpret_cast<float*>(a.y) + (int64_t)yr * a.rows + r, v);
+          } else {
+            store_out(a.y, (int64_t)yr * a.rows + r, v, y_kind);
+          }
         }
       }
     }
@@ -592,6 +613,15 @@ __global__ __launch_bounds__(256) void vq_zero_tiles_kernel(float* y, int rows, 
   }
 }
 
+// Zero n 32-bit words (16-byte stores where aligned), grid-stride.
+__global__ __launch_bounds__(256) void vq_zero_kernel(uint32_t* p, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n4 = ((reinterpret_cast<uintptr_t>(p) & 15) == 0) ? n / 4 : 0;
+  for (int64_t i = i0; i < n4; i += stride) reinterpret_cast<u32x4*>(p)[i] = u32x4{0u, 0u, 0u, 0u};
+  for (int64_t i = 4 * n4 + i0; i < n; i += stride) p[i] = 0u;
+}
+
 // ---------------------------------------------------------------------------
 // routing: group (token, slot) pairs by expert and emit the token-tile list.
 // One block; pairs and experts are walked in strides of the block size.
@@ -602,7 +632,8 @@ __global__ __launch_bounds__(256) void vq_zero_tiles_kernel(float* y, int rows, 
 struct RouteArgs {
   const int32_t* ids;
   int32_t* ws;
-  float* y;
+  void* y;            // skipped slots' output rows are zeroed (nullptr: none to zero)
+  int y_row_halves;   // 16-bit words per output row
   int npairs, num_experts, rows, tile_tokens, max_tiles;
 };
 
@@ -678,9 +709,9 @@ __device__ __forceinline__ void route_pairs(const RouteArgs& a, int32_t* counts,
     if (e >= 0 && e < E) {
       const int pos = offsets[e] + atomicAdd(&fill[e], 1);
       pairs[pos] = p;
-    } else {
-      float* yr = a.y + (int64_t)p * a.rows;  // skipped slot: zero row
-      for (int r = 0; r < a.rows; ++r) yr[r] = 0.f;
+    } else if (a.y) {
+      uint16_t* yr = static_cast<uint16_t*>(a.y) + (int64_t)p * a.y_row_halves;  // skipped slot: zero row
+      for (int r = 0; r < a.y_row_halves; ++r) yr[r] = 0;
     }
   }
 }
@@ -738,13 +769,17 @@ int num_cus() {
   return n;
 }
 
-GemmArgs base_args(const TensorView& w, const uint16_t* x, float* y, int G, int D, int B) {
+GemmArgs base_args(const TensorView& w, const IoSpec& io, const void* x, void* y, int G, int D, int B) {
   GemmArgs a{};
   a.codes = w.codes;
   a.codebook = w.codebook;
   a.scales = w.scales;
-  a.x = x;
+  a.x = static_cast<const uint16_t*>(x);
   a.y = y;
+  a.route_w = io.route_w;
+  a.x_bf16 = io.x_bf16;
+  a.y_kind = io.y_kind;
+  a.epi = io.epi;
   a.code_estride = (int64_t)w.rows * w.wr;
   a.scale_estride = (int64_t)w.rows * (w.cols / G);
   a.cb_estride = w.cb_per_expert ? (int64_t)(1 << B) * D : 0;
@@ -786,6 +821,8 @@ hipError_t gemm_dense(GemmArgs a, hipStream_t s) {
       }
     }
   }
+  // K slices add fp32 partial sums: only a plain fp32 output can take them
+  if (a.epi != kEpiNone || a.y_kind != kOutF32) split = 1;
   if (split == 1) {
     full = tiles;
     rem = 0;
@@ -793,7 +830,8 @@ hipError_t gemm_dense(GemmArgs a, hipStream_t s) {
   a.n_full = full;
   a.rem_split = split;
   if (rem > 0) {
-    hipLaunchKernelGGL(vq_zero_tiles_kernel, dim3(rem, std::max(1, 2 * cus / rem)), dim3(256), 0, s, a.y, a.rows,
+    hipLaunchKernelGGL(vq_zero_tiles_kernel, dim3(rem, std::max(1, 2 * cus / rem)), dim3(256), 0, s,
+                       static_cast<float*>(a.y), a.rows,
                        a.T, full, a.n_row_tiles, a.n_tok_tiles, SH::kRows, SH::kTokens);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -802,16 +840,16 @@ hipError_t gemm_dense(GemmArgs a, hipStream_t s) {
 }
 
 template <int D, int B, int G>
-hipError_t gemm_geom(const TensorView& w, const uint16_t* x, int T, float* y, hipStream_t s) {
-  GemmArgs a = base_args(w, x, y, G, D, B);
+hipError_t gemm_geom(const TensorView& w, const IoSpec& io, const void* x, int T, void* y, hipStream_t s) {
+  GemmArgs a = base_args(w, io, x, y, G, D, B);
   a.T = T;
   if (T <= 32) return gemm_dense<D, B, G, GemmSmallT>(a, s);
   return gemm_dense<D, B, G, GemmLargeT>(a, s);
 }
 
 template <int D, int B, int G>
-hipError_t moe_gemm_geom(const TensorView& w, const uint16_t* x, int x_per_slot,
-                         const int32_t* ids, int T, int top_k, float* y, void* ws, hipStream_t s) {
+hipError_t moe_gemm_geom(const TensorView& w, const IoSpec& io, const void* x, int x_per_slot,
+                         const int32_t* ids, int T, int top_k, void* y, void* ws, hipStream_t s) {
   const int npairs = T * top_k;
   const int E = w.num_experts;
   const int mt = max_tiles_for(npairs, E);
@@ -819,7 +857,8 @@ hipError_t moe_gemm_geom(const TensorView& w, const uint16_t* x, int x_per_slot,
   RouteArgs r{};
   r.ids = ids;
   r.ws = wsi;
-  r.y = y;
+  r.y = io.epi == kEpiCombine ? nullptr : y;   // combine: skipped slots add nothing
+  r.y_row_halves = (io.epi == kEpiSwiglu ? w.rows / 2 : w.rows) * (io.y_kind == kOutF32 ? 2 : 1);
   r.npairs = npairs;
   r.num_experts = E;
   r.rows = w.rows;
@@ -829,7 +868,11 @@ hipError_t moe_gemm_geom(const TensorView& w, const uint16_t* x, int x_per_slot,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  GemmArgs a = base_args(w, x, y, G, D, B);
+  if (io.epi == kEpiCombine) {  // the slots add into y: zero it first
+    hipError_t ez = launch_zero(y, (size_t)T * w.rows * sizeof(float), s);
+    if (ez != hipSuccess) return ez;
+  }
+  GemmArgs a = base_args(w, io, x, y, G, D, B);
   int32_t* n_tiles = wsi + 4 * E;
   int32_t* pairs = wsi + ((4 * E + 1 + 3) & ~3);
   int32_t* tiles = pairs + ((npairs + 3) & ~3);
@@ -880,6 +923,14 @@ hipError_t static_scratch(void** out) {
   return hipSuccess;
 }
 
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  const int64_t n = (int64_t)(bytes / 4);
+  if (n == 0) return hipSuccess;
+  const int blocks = (int)std::min<int64_t>((n / 4 + 255) / 256 + 1, (int64_t)num_cus() * 4);
+  hipLaunchKernelGGL(vq_zero_kernel, dim3(blocks), dim3(256), 0, s, static_cast<uint32_t*>(p), n);
+  return hipGetLastError();
+}
+
 size_t moe_workspace_bytes(int T, int top_k, int num_experts) {
   const int64_t npairs = (int64_t)T * top_k;
   if (npairs <= 0) return 0;
@@ -893,20 +944,19 @@ size_t moe_workspace_bytes(int T, int top_k, int num_experts) {
   X(4, 8, 64) X(4, 8, 128) X(4, 12, 64) X(4, 12, 128) \
   X(8, 8, 64) X(8, 8, 128) X(8, 12, 64) X(8, 12, 128)
 
-hipError_t launch_gemm(const TensorView& w, const uint16_t* x, int T, float* y, hipStream_t s) {
+hipError_t launch_gemm(const TensorView& w, const IoSpec& io, const void* x, int T, void* y, hipStream_t s) {
 #define X(D, B, G) \
-  if (w.d == D && w.log2_k == B && w.group == G) return gemm_geom<D, B, G>(w, x, T, y, s);
+  if (w.d == D && w.log2_k == B && w.group == G) return gemm_geom<D, B, G>(w, io, x, T, y, s);
   VQMI_GEOMS(X)
 #undef X
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_moe_gemm(const TensorView& w, const uint16_t* x, int x_per_slot,
-                           const int32_t* ids, int T, int top_k, float* y, void* ws,
-                           hipStream_t s) {
+hipError_t launch_moe_gemm(const TensorView& w, const IoSpec& io, const void* x, int x_per_slot,
+                           const int32_t* ids, int T, int top_k, void* y, void* ws, hipStream_t s) {
 #define X(D, B, G)                                   \
   if (w.d == D && w.log2_k == B && w.group == G)     \
-    return moe_gemm_geom<D, B, G>(w, x, x_per_slot, ids, T, top_k, y, ws, s);
+    return moe_gemm_geom<D, B, G>(w, io, x, x_per_slot, ids, T, top_k, y, ws, s);
   VQMI_GEOMS(X)
 #undef X
   return hipErrorInvalidValue;

@@ -53,8 +53,9 @@ struct GemvArgs {
   const uint16_t* codebook;
   const uint16_t* scales;
   const uint16_t* x;
-  float* y;
+  void* y;                // output, element type y_kind (see epi for its shape)
   const int32_t* ids;     // routed: [pairs]; dense: nullptr
+  const float* route_w;   // epi == combine: router weight per pair
   int64_t code_estride;   // words between experts
   int64_t scale_estride;  // fp16 between experts
   int64_t cb_estride;     // fp16 between per-expert codebooks (0: shared)
@@ -69,6 +70,9 @@ struct GemvArgs {
   int top_k;
   int num_experts;
   int x_per_slot;
+  int x_bf16;             // x holds bf16 (converted to fp16 as it is staged)
+  int y_kind;             // OutKind
+  int epi;                // Epilogue: none; swiglu (rows 2i, 2i + 1 -> y[i]); combine (y[token] += w * row)
 };
 
 constexpr int kGemvWaves = 8;                  // two waves per SIMD
@@ -107,7 +111,8 @@ template <int D, int B, int G, int C, int XS, bool MOE>
 // routing, accumulation) is only needed later and stays in the struct.
 //   xs: x of token tok0 (dense) or x (routed); shape = nq | lanes_log2 << 12 |
 //   passes << 15 | pass width << 23 (chunks per pass, at most L * C); cols =
-//   spr * G.
+//   spr * G; rows_extra: blocks below it own one more row unit, the unit (one
+//   row, or a row pair under the SwiGLU epilogue) being 1 + bit 30.
 __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
     const uint32_t* __restrict__ codes_in, const uint16_t* __restrict__ cb_in,
     const uint16_t* __restrict__ scales_in, const uint16_t* __restrict__ xs, int rows, int rows_base,
@@ -143,22 +148,29 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
 
   // ---- this block's rows ----
   const int bid = blockIdx.x;
-  const int brow0 = bid * rows_base + min(bid, rows_extra);
-  const int brows = rows_base + (bid < rows_extra ? 1 : 0);
+  const int unit = 1 + (rows_extra >> 30);
+  const int extra = rows_extra & 0x3fffffff;
+  const int brow0 = bid * rows_base + min(bid, extra) * unit;
+  const int brows = rows_base + (bid < extra ? unit : 0);
   const int ngroups = (brows + R - 1) / R;
 
   const uint32_t* codes = codes_in;
   const uint16_t* scales = scales_in;
   const uint16_t* cb = cb_in;
   const uint16_t* xb;
-  float* yb;
+  // output: row `yrow` of y, of `yrows` values (rows / 2 under SwiGLU)
+  const int yrows = a.epi == kEpiSwiglu ? rows >> 1 : rows;
+  int64_t yrow;
   if constexpr (MOE) {
     const int pair = blockIdx.y;
     const int e = a.ids[pair];
-    yb = a.y + (int64_t)pair * rows;
+    yrow = a.epi == kEpiCombine ? pair / a.top_k : pair;
     if (e < 0 || e >= a.num_experts) {  // skipped slot: zero rows (block-uniform exit)
-      if (!a.accumulate)
-        for (int r = tid; r < brows; r += NT) yb[brow0 + r] = 0.f;
+      if (!a.accumulate && a.epi != kEpiCombine) {
+        const int y0 = a.epi == kEpiSwiglu ? brow0 >> 1 : brow0;
+        const int yn = a.epi == kEpiSwiglu ? brows >> 1 : brows;
+        for (int r = tid; r < yn; r += NT) store_out(a.y, yrow * yrows + y0 + r, 0.f, a.y_kind);
+      }
       return;
     }
     codes += (int64_t)e * a.code_estride;
@@ -167,7 +179,7 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
     xb = xs + (int64_t)(a.x_per_slot ? pair : pair / a.top_k) * cols;
   } else {
     xb = xs + (int64_t)blockIdx.y * cols;  // one token per grid slice
-    yb = a.y + (int64_t)(a.tok0 + blockIdx.y) * rows;
+    yrow = a.tok0 + blockIdx.y;
   }
 
   // ---- small loads first: x slice, codebook entries, the block's scales ----
@@ -307,10 +319,11 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
       reinterpret_cast<u32x4*>(cb_lds)[wave * 512 + 64 * k + lane] = v;
     }
   }
+  const bool x_bf16 = a.x_bf16 != 0;
 #pragma unroll
   for (int q = 0; q < XL; ++q) {
     const uint32_t o = (uint32_t)(tid + q * NT) * 16u;
-    if (o < (uint32_t)XBYTES) *reinterpret_cast<u32x4*>(x_lds + o) = xg[q];
+    if (o < (uint32_t)XBYTES) *reinterpret_cast<u32x4*>(x_lds + o) = x_bf16 ? bf16x8_to_f16x8(xg[q]) : xg[q];
   }
 #pragma unroll
   for (int q = 0; q < SL; ++q) {
@@ -422,11 +435,26 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
 
   {  // y: each row's pass pieces added in pass order (deterministic)
     __syncthreads();
-    for (int r = tid; r < brows; r += NT) {
+    auto row_sum = [&](int r) {
       float v = 0.f;
       for (int c = 0; c < passes; ++c) v += pieces[r * passes + c];
-      float* dst = yb + brow0 + r;
-      *dst = a.accumulate ? *dst + v : v;
+      return v;
+    };
+    const int64_t ybase = yrow * yrows;
+    if (a.epi == kEpiSwiglu) {  // rows 2i (gate) and 2i + 1 (up) -> y[i]
+      for (int i = tid; 2 * i < brows; i += NT)
+        store_out(a.y, ybase + (brow0 >> 1) + i, swiglu(row_sum(2 * i), row_sum(2 * i + 1)), a.y_kind);
+    } else if (a.epi == kEpiCombine) {  // y[token] += router weight * row
+      if constexpr (MOE) {
+        const float wgt = a.route_w[blockIdx.y];
+        float* yc = reinterpret_cast<float*>(a.y) + ybase + brow0;
+        for (int r = tid; r < brows; r += NT) atomicAdd(yc + r, wgt * row_sum(r));
+      }
+    } else if (a.accumulate) {  // a column slice after the first (fp32 y)
+      float* yf = reinterpret_cast<float*>(a.y) + ybase + brow0;
+      for (int r = tid; r < brows; r += NT) yf[r] += row_sum(r);
+    } else {
+      for (int r = tid; r < brows; r += NT) store_out(a.y, ybase + brow0 + r, row_sum(r), a.y_kind);
     }
   }
 }
@@ -575,7 +603,7 @@ LaneTiling plan_tiling(int nq, int max_c, int waves, bool cu_bound) {
 
 template <int D, int B, int G, int C, int XS, bool MOE>
 hipError_t gemv_launch_c(const GemvArgs& a, dim3 grid, hipStream_t s) {
-  const uint16_t* xs = MOE ? a.x : a.x + (int64_t)a.tok0 * a.cols;
+  const uint16_t* xs = MOE ? a.x : a.x + (int64_t)a.tok0 * a.cols;  // fp16 or bf16: 2 bytes a value
   const int pw = (a.nq + a.passes - 1) / a.passes;
   if (a.nq > 0xfff || a.lanes_log2 > 7 || a.passes > 0xff || pw > 0x1ff || pw > C << a.lanes_log2)
     return hipErrorInvalidValue;
@@ -620,10 +648,13 @@ hipError_t gemv_run(GemvArgs a, int P, int ycount, hipStream_t s) {
     a.passes = t.passes;
     const int64_t by_scales = std::max<int64_t>(1, (kGemvScaleBytes - 16) / (2 * (int64_t)a.spr));
     const int64_t by_pieces = std::max<int64_t>(1, kGemvPieces / (int64_t)t.passes);
-    const int64_t rows_max = std::min(by_scales, by_pieces);
-    const int64_t blocks = std::min<int64_t>(a.rows, std::max<int64_t>(blocks_fill, (a.rows + rows_max - 1) / rows_max));
-    a.rows_base = (int)(a.rows / blocks);
-    a.rows_extra = (int)(a.rows - (int64_t)a.rows_base * blocks);
+    // under SwiGLU a block owns whole (gate, up) row pairs
+    const int unit = a.epi == kEpiSwiglu ? 2 : 1;
+    const int64_t rows_max = std::max<int64_t>(unit, std::min(by_scales, by_pieces) / unit * unit);
+    const int64_t units = a.rows / unit;
+    const int64_t blocks = std::min<int64_t>(units, std::max<int64_t>(blocks_fill, (a.rows + rows_max - 1) / rows_max));
+    a.rows_base = (int)(units / blocks) * unit;
+    a.rows_extra = (int)(units - units / blocks * blocks) | (unit == 2 ? 1 << 30 : 0);
     const int XS = (int64_t)a.nq * 32 * D <= 2 * 8192 ? 2 : 5;
     // dense: at most 65535 token slices per launch
     for (int y0 = 0; y0 < ycount; y0 += 65535) {
@@ -639,15 +670,19 @@ hipError_t gemv_run(GemvArgs a, int P, int ycount, hipStream_t s) {
 }
 
 template <int D, int B, int G>
-hipError_t gemv_geom(const TensorView& w, const uint16_t* x, int T, float* y, const int32_t* ids,
+hipError_t gemv_geom(const TensorView& w, const IoSpec& io, const void* x, int T, void* y, const int32_t* ids,
                      int top_k, int x_per_slot, hipStream_t s) {
   GemvArgs a{};
   a.codes = w.codes;
   a.codebook = w.codebook;
   a.scales = w.scales;
-  a.x = x;
+  a.x = static_cast<const uint16_t*>(x);
   a.y = y;
   a.ids = ids;
+  a.route_w = io.route_w;
+  a.x_bf16 = io.x_bf16;
+  a.y_kind = io.y_kind;
+  a.epi = io.epi;
   a.code_estride = (int64_t)w.rows * w.wr;
   a.scale_estride = (int64_t)w.rows * (w.cols / G);
   a.cb_estride = w.cb_per_expert ? (int64_t)(1 << B) * D : 0;
@@ -693,11 +728,15 @@ hipError_t dequant_geom(const TensorView& w, int expert, uint16_t* out, hipStrea
   X(4, 8, 64) X(4, 8, 128) X(4, 12, 64) X(4, 12, 128) \
   X(8, 8, 64) X(8, 8, 128) X(8, 12, 64) X(8, 12, 128)
 
-hipError_t launch_gemv(const TensorView& w, const uint16_t* x, int T, float* y,
+hipError_t launch_gemv(const TensorView& w, const IoSpec& io, const void* x, int T, void* y,
                        const int32_t* ids, int top_k, int x_per_slot, hipStream_t s) {
+  if (io.epi == kEpiCombine) {  // the slots add into y: zero it first
+    hipError_t e = launch_zero(y, (size_t)T * w.rows * sizeof(float), s);
+    if (e != hipSuccess) return e;
+  }
 #define X(D, B, G)                                                   \
   if (w.d == D && w.log2_k == B && w.group == G)                     \
-    return gemv_geom<D, B, G>(w, x, T, y, ids, top_k, x_per_slot, s);
+    return gemv_geom<D, B, G>(w, io, x, T, y, ids, top_k, x_per_slot, s);
   VQMI_GEOMS(X)
 #undef X
   return hipErrorInvalidValue;

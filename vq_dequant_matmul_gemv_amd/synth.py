@@ -104,6 +104,26 @@ def activations(shape, *key, exact: bool = False) -> np.ndarray:
     return g.normal(0.0, 1.0, size=shape).astype(np.float16)
 
 
+def activations_bf16(shape, *key, exact: bool = False) -> np.ndarray:
+    """bf16 activations as uint16 bit patterns: N(0, 1) drawn in fp32 and
+    rounded to the nearest bf16 (ties to even); exact: values in {-1, 0, 1}."""
+    g = rng("x-bf16", *key)
+    if exact:
+        f = g.integers(-1, 2, size=shape).astype(np.float32)
+    else:
+        f = g.normal(0.0, 1.0, size=shape).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def router_weights(tokens: int, top_k: int, *key) -> np.ndarray:
+    """fp32 [tokens][top_k] router weights: positive, summing to one per token
+    (a softmax-like draw over the chosen slots)."""
+    g = rng("router-w", *key)
+    w = g.exponential(1.0, size=(tokens, top_k))
+    return (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
 def zipf_routing(tokens: int, num_experts: int, top_k: int, *key, alpha: float = 1.1) -> np.ndarray:
     """int32 [tokens][top_k]: distinct expert ids per token, Zipf(alpha) over ranks."""
     g = rng("route", *key)
