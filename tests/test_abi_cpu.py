@@ -41,7 +41,9 @@ def test_words_per_row_matches_oracle(b):
         assert b.words_per_row(cols, d, k) == O.words_per_row(cols, d, k)
     assert b.words_per_row(0, 2, 8) == -1
     assert b.words_per_row(64, 3, 8) == -1
-    assert b.words_per_row(64, 2, 10) == -1
+    assert b.words_per_row(64, 2, 15) == -1
+    assert b.words_per_row(64, 2, 3) == -1
+    assert b.words_per_row(64, 2, 9) == O.words_per_row(64, 2, 9)
 
 
 def _t(b, **kw):
@@ -64,7 +66,8 @@ def _gemv(b, t, x=0x40000, T=1, y=0x50000):
     (dict(codes=0), "VQ_ERR_NULL"),
     (dict(scales=0), "VQ_ERR_NULL"),
     (dict(d=3), "VQ_ERR_GEOMETRY"),
-    (dict(log2_k=10), "VQ_ERR_GEOMETRY"),
+    (dict(log2_k=15), "VQ_ERR_GEOMETRY"),
+    (dict(log2_k=3), "VQ_ERR_GEOMETRY"),
     (dict(group=32), "VQ_ERR_GEOMETRY"),
     (dict(rows=0), "VQ_ERR_SHAPE"),
     (dict(cols=320, group=128), "VQ_ERR_SHAPE"),          # cols % group

@@ -21,6 +21,8 @@ from vq_dequant_matmul_gemv_amd import synth
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 GEOMS = [(d, b, g) for d in (2, 4, 8) for b in (8, 12) for g in (64, 128)]
+# the other code widths (K = 16 ... 16384), one group size each
+GEOMS_WIDE = [(d, b, 64 if (b + d) % 2 else 128) for d in (2, 4, 8) for b in (4, 5, 9, 10, 11, 13, 14)]
 
 
 # --------------------------------------------------------------------------
@@ -214,7 +216,7 @@ def test_uint8_codes_are_the_packed8_layout():
     assert np.array_equal(O.pack_codes(codes, 8), words)
 
 
-@pytest.mark.parametrize("bits", [8, 12])
+@pytest.mark.parametrize("bits", list(range(4, 15)))
 def test_unpack_matches_bitstring_on_random_words(bits):
     g = np.random.default_rng(bits)
     d = 4
@@ -222,6 +224,21 @@ def test_unpack_matches_bitstring_on_random_words(bits):
     codes = O.unpack_codes(words, 64 * d, d, bits)
     for r in range(3):
         assert codes[r].tolist() == bitstring_codes(words[r], 64, bits)
+
+
+@pytest.mark.parametrize("bits", [4, 5, 7, 9, 10, 11, 13, 14])
+def test_pack_matches_bitstring_construction_other_widths(bits):
+    """Codes of every width the kernels take (paper §1 Notation: builds from
+    d2/K16 to d4/K16384), packed by the oracle and by the independent
+    bit-string construction: ramps, all ones, and random codes."""
+    g = np.random.default_rng(100 + bits)
+    for codes in ([j % (1 << bits) for j in range(32)], [(1 << bits) - 1] * 32,
+                  g.integers(0, 1 << bits, size=64).tolist()):
+        packed = O.pack_codes(np.array([codes]), bits)[0]
+        assert [int(w) for w in packed] == bitstring_pack(codes, bits)
+        assert len(packed) == len(codes) // 32 * bits
+        d = 2
+        assert O.unpack_codes(packed[None], len(codes) * d, d, bits)[0].tolist() == codes
 
 
 def test_pack_unpack_roundtrip_property():
@@ -380,7 +397,7 @@ def brute_force(words, codebook, scales, x, cols, d, b, g):
     return out
 
 
-@pytest.mark.parametrize("d,b,g", GEOMS)
+@pytest.mark.parametrize("d,b,g", GEOMS + GEOMS_WIDE)
 def test_brute_force_all_geometries(d, b, g):
     spec = synth.Spec(rows=3, cols=max(32 * d, g) * (1 if d == 8 else 2), d=d, log2_k=b, group=g)
     t = synth.tensor(spec, "pin-bf", d, b, g)

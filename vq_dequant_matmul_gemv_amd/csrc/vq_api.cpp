@@ -35,7 +35,7 @@ constexpr int64_t kMaxBufferBytes = 0x7fffffff;
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 int32_t words_per_row(int32_t cols, int32_t d, int32_t log2_k) {
-  if (cols <= 0 || (d != 2 && d != 4 && d != 8) || (log2_k != 8 && log2_k != 12)) return -1;
+  if (cols <= 0 || (d != 2 && d != 4 && d != 8) || log2_k < vqmi::kMinBits || log2_k > vqmi::kMaxBits) return -1;
   const int64_t n_codes = cols / d;
   const int64_t blocks = (n_codes + 31) / 32;
   return (int32_t)(blocks * log2_k);
@@ -47,11 +47,11 @@ vq_status check_tensor(const vq_tensor* w, vqmi::TensorView* v) {
   if (!w->codes || !w->codebook || !w->scales)
     return fail(VQ_ERR_NULL, "tensor has a NULL pointer (codes=%p codebook=%p scales=%p)",
                 (const void*)w->codes, (const void*)w->codebook, (const void*)w->scales);
-  if ((w->d != 2 && w->d != 4 && w->d != 8) || (w->log2_k != 8 && w->log2_k != 12) ||
+  if ((w->d != 2 && w->d != 4 && w->d != 8) || w->log2_k < vqmi::kMinBits || w->log2_k > vqmi::kMaxBits ||
       (w->group != 64 && w->group != 128))
     return fail(VQ_ERR_GEOMETRY,
                 "unsupported geometry d=%d log2_k=%d group=%d (supported: d in {2,4,8}, "
-                "log2_k in {8,12}, group in {64,128})",
+                "log2_k in [4, 14], group in {64,128})",
                 w->d, w->log2_k, w->group);
   if (w->rows < 1 || w->cols < 1)
     return fail(VQ_ERR_SHAPE, "rows=%d cols=%d must be positive", w->rows, w->cols);

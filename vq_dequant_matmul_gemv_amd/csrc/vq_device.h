@@ -7,8 +7,11 @@
 // "Qwen3.5-397B-A17B-VQ-2.4bpw", Methodology): code j of a row is the B bits
 // starting at bit j*B of the row's little-endian code stream; rows hold whole
 // 32-code blocks of B uint32 words.  Kernels work on "chunks" of 16
-// consecutive codes of one row: 16*B bits = B/2 words (16 bytes for B = 8,
-// 24 bytes for B = 12), always starting on an 8-byte boundary.
+// consecutive codes of one row: 16*B bits, starting at byte 2*B*q of the row
+// for chunk q.  For B = 8 and 12 that is 16 / 24 bytes from a 16- / 8-byte
+// boundary.  Any other width is read as a window of whole words from the
+// 4-byte boundary at or below the chunk (for odd B, odd chunks start 16 bits
+// into a word) and shifted into place once the words have arrived.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -57,38 +60,97 @@ __device__ __forceinline__ uint16_t buf_load_b16(rsrc_t r, uint32_t off) {
 // codes
 // ---------------------------------------------------------------------------
 
-// Words of one 16-code chunk.
+// Code widths with whole-word chunks on their natural boundaries.
+template <int B>
+constexpr bool kAlignedChunks = (B == 8 || B == 12);
+
+// Words of one 16-code chunk: B / 2 for 8 and 12 bits; otherwise the
+// (B + 1) / 2 words that cover 16*B bits from the 4-byte boundary at or below
+// the chunk.
 template <int B>
 struct Chunk {
-  static constexpr int kWords = B / 2;  // 8-bit: 4 words, 12-bit: 6 words
+  static constexpr int kWords = kAlignedChunks<B> ? B / 2 : (B + 1) / 2;
   uint32_t w[kWords];
 };
 
+// Byte offset (4-byte aligned) of the words of chunk q within its row, and
+// the bit offset of the chunk's first code in its first word (0 or 16).
+template <int B>
+__host__ __device__ constexpr uint32_t chunk_byte(uint32_t q) { return (2u * B * q) & ~3u; }
+template <int B>
+__device__ __forceinline__ uint32_t chunk_shift(uint32_t q) { return (B & 1) ? (q & 1u) * 16u : 0u; }
+
+// N consecutive words from a 4-byte aligned byte offset (soffset: a
+// wave-uniform part of the offset), in as few loads as the count allows.
+template <int N>
+__device__ __forceinline__ void load_words(uint32_t* w, rsrc_t r, uint32_t off, uint32_t soff = 0) {
+  int k = 0;
+#pragma unroll
+  for (; k + 4 <= N; k += 4) {
+    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 4u * k, soff, 0));
+    w[k] = v.x; w[k + 1] = v.y; w[k + 2] = v.z; w[k + 3] = v.w;
+  }
+  if constexpr (N % 4 == 3) {
+    typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+    const u32x3 v = __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(r, off + 4u * k, soff, 0));
+    w[k] = v.x; w[k + 1] = v.y; w[k + 2] = v.z;
+  } else if constexpr (N % 4 == 2) {
+    const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off + 4u * k, soff, 0));
+    w[k] = v.x; w[k + 1] = v.y;
+  } else if constexpr (N % 4 == 1) {
+    w[k] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4u * k, soff, 0);
+  }
+}
+
+// Shift N words right by sh bits (0..31) as one little-endian bit string, so
+// that the window's first code starts at bit 0.
+template <int N>
+__device__ __forceinline__ void align_words(uint32_t* w, uint32_t sh) {
+#pragma unroll
+  for (int k = 0; k + 1 < N; ++k) w[k] = __builtin_amdgcn_alignbit(w[k + 1], w[k], sh);
+  w[N - 1] = __builtin_amdgcn_alignbit(0u, w[N - 1], sh);
+}
+
+// Chunk at byte `off` (chunk_byte) of the buffer.
 template <int B>
 __device__ __forceinline__ void load_chunk(Chunk<B>& c, rsrc_t r, uint32_t off) {
   if constexpr (B == 8) {
     u32x4 v = buf_load_b128(r, off);  // 16-byte aligned
     c.w[0] = v.x; c.w[1] = v.y; c.w[2] = v.z; c.w[3] = v.w;
-  } else {
+  } else if constexpr (B == 12) {
     u32x2 a = buf_load_b64(r, off);   // 24 bytes on an 8-byte boundary
     u32x2 b = buf_load_b64(r, off + 8);
     u32x2 d = buf_load_b64(r, off + 16);
     c.w[0] = a.x; c.w[1] = a.y; c.w[2] = b.x; c.w[3] = b.y; c.w[4] = d.x; c.w[5] = d.y;
+  } else {
+    load_words<Chunk<B>::kWords>(c.w, r, off);
   }
 }
 
+// Chunk q of a row whose words start at p (any width; shifted into place).
 template <int B>
-__device__ __forceinline__ void load_chunk(Chunk<B>& c, const uint32_t* p) {
+__device__ __forceinline__ void load_chunk(Chunk<B>& c, const uint32_t* row, uint32_t q) {
+  const uint32_t* p = row + chunk_byte<B>(q) / 4;
   if constexpr (B == 8) {
     u32x4 v = *reinterpret_cast<const u32x4*>(p);  // 16-byte aligned
     c.w[0] = v.x; c.w[1] = v.y; c.w[2] = v.z; c.w[3] = v.w;
-  } else {
+  } else if constexpr (B == 12) {
     // 24 bytes on an 8-byte boundary
     u32x2 a = *reinterpret_cast<const u32x2*>(p);
     u32x2 b = *reinterpret_cast<const u32x2*>(p + 2);
     u32x2 d = *reinterpret_cast<const u32x2*>(p + 4);
     c.w[0] = a.x; c.w[1] = a.y; c.w[2] = b.x; c.w[3] = b.y; c.w[4] = d.x; c.w[5] = d.y;
+  } else {
+#pragma unroll
+    for (int k = 0; k < Chunk<B>::kWords; ++k) c.w[k] = p[k];
+    if constexpr (B & 1) align_words<Chunk<B>::kWords>(c.w, chunk_shift<B>(q));
   }
+}
+
+// Bring a chunk loaded at chunk_byte(q) into place (odd widths, odd q).
+template <int B>
+__device__ __forceinline__ void align_chunk(Chunk<B>& c, uint32_t sh) {
+  if constexpr ((B & 1) && !kAlignedChunks<B>) align_words<Chunk<B>::kWords>(c.w, sh);
 }
 
 // Code i (0..15, compile-time after unrolling) of a chunk.
@@ -119,14 +181,22 @@ __device__ __forceinline__ uint32_t chunk_code(const Chunk<B>& c, int i) {
 // 64 KiB for every D.
 //
 // Plain (any K): entry e at e * (2*D) bytes; random gathers may conflict.
-// Used for K = 4096 (32 KiB for d4, 64 KiB for d8, 16 KiB for d2).
+// Used for every other K whose codebook takes at most 64 KiB (K = 4096: 16,
+// 32 and 64 KiB for d = 2, 4, 8; K = 16384 at d = 2: 64 KiB).
+//
+// Device memory (codebooks above 64 KiB: d = 4 with K = 16384, d = 8 with K =
+// 8192 or 16384): not staged; each gather reads the entry from the codebook
+// in device memory, where it stays resident in the L2 caches.  The slower
+// path, as the paper's device-memory codebook variant (§3.4), for the
+// codebooks that do not fit next to the kernels' other LDS buffers.
 
 template <int D, int B>
 struct CodebookLayout {
   static constexpr int kEntryBytes = 2 * D;
   static constexpr bool kReplicated = (B == 8);
+  static constexpr bool kGlobal = !kReplicated && (1 << B) * kEntryBytes > 64 * 1024;
   static constexpr int kCopies = kReplicated ? 256 / kEntryBytes : 1;
-  static constexpr int kBytes = kReplicated ? 256 * 256 : (1 << B) * kEntryBytes;
+  static constexpr int kBytes = kReplicated ? 256 * 256 : (kGlobal ? 16 : (1 << B) * kEntryBytes);
 };
 
 // Stage `cb` (global, [K][D] fp16, 16-byte aligned) into `lds`.
@@ -137,7 +207,9 @@ template <int D, int B>
 __device__ __forceinline__ void stage_codebook(uint8_t* lds, const uint16_t* cb, int tid,
                                                int nthreads) {
   using L = CodebookLayout<D, B>;
-  if constexpr (L::kReplicated) {
+  if constexpr (L::kGlobal) {
+    return;  // gathered from device memory
+  } else if constexpr (L::kReplicated) {
     // 4096 slots of 16 bytes; slot q holds copies of entry q / 16.  Lanes
     // write consecutive slots (conflict-free); the 16 lanes sharing an entry
     // read the same global address (one L1 line).
@@ -206,6 +278,8 @@ template <> struct Entry<2> { half2_t v[1]; };
 template <> struct Entry<4> { half2_t v[2]; };
 template <> struct Entry<8> { half2_t v[4]; };
 
+// The d fp16 values of the entry at byte `off` of the codebook at `lds` (LDS,
+// or device memory for the large codebooks).
 template <int D>
 __device__ __forceinline__ Entry<D> lds_entry(const uint8_t* lds, uint32_t off) {
   Entry<D> e;

@@ -28,6 +28,22 @@ struct IoSpec {
   const float* route_w = nullptr;  // kEpiCombine: [pairs] router weights
 };
 
+// Code widths the kernels are built for: B = log2 K = 4 ... 14 (K = 16 ...
+// 16384), each in its own translation units (vq_gemv_bNN.hip, vq_gemm_bNN.hip).
+#define VQMI_BITS(X) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14)
+constexpr int kMinBits = 4;
+constexpr int kMaxBits = 14;
+
+#define VQMI_DECLARE_WIDTH(B)                                                                                \
+  hipError_t gemv_b##B(const TensorView& w, const IoSpec& io, const void* x, int T, void* y,                \
+                       const int32_t* ids, int top_k, int x_per_slot, hipStream_t s);                        \
+  hipError_t dequant_b##B(const TensorView& w, int expert, uint16_t* out, hipStream_t s);                   \
+  hipError_t gemm_b##B(const TensorView& w, const IoSpec& io, const void* x, int T, void* y, hipStream_t s); \
+  hipError_t moe_gemm_b##B(const TensorView& w, const IoSpec& io, const void* x, int x_per_slot, int T,     \
+                           int top_k, void* y, int32_t* ws, hipStream_t s);
+VQMI_BITS(VQMI_DECLARE_WIDTH)
+#undef VQMI_DECLARE_WIDTH
+
 hipError_t launch_dequant(const TensorView& w, int expert, uint16_t* out, hipStream_t s);
 
 // Dense (ids == nullptr, T tokens) or routed (ids != nullptr, T*top_k pairs).
@@ -41,6 +57,21 @@ hipError_t launch_gemm(const TensorView& w, const IoSpec& io, const void* x, int
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
 size_t moe_workspace_bytes(int T, int top_k, int num_experts);
+
+// Routed GEMM: (token, slot) pairs go in tiles of this many per expert.
+constexpr int kMoeTileTokens = 32;
+
+// Routing workspace (int32): counts[E] | offsets[E] | fill[E] | tile_base[E] |
+// n_tiles | pad to 4 | pairs[npairs] | tiles[max_tiles][3] (expert, first
+// pair, count).  At most ceil(npairs / tile) + E tiles.
+__host__ __device__ inline int moe_max_tiles(int npairs, int E) {
+  return (npairs + kMoeTileTokens - 1) / kMoeTileTokens + E;
+}
+__host__ __device__ inline int32_t* moe_ws_n_tiles(int32_t* ws, int E) { return ws + 4 * E; }
+__host__ __device__ inline int32_t* moe_ws_pairs(int32_t* ws, int E) { return ws + ((4 * E + 1 + 3) & ~3); }
+__host__ __device__ inline int32_t* moe_ws_tiles(int32_t* ws, int E, int npairs) {
+  return moe_ws_pairs(ws, E) + ((npairs + 3) & ~3);
+}
 
 // Bytes of the library's static device scratch array (one per GPU), and its
 // address on the current device (looked up once per device).
