@@ -280,6 +280,40 @@ vq_status vq_moe_gemm_no_alloc(const vq_tensor *w, const uint16_t *x, int32_t x_
                                const int32_t *expert_ids, int32_t T, int32_t top_k, float *y,
                                void *stream);
 
+/*
+ * The fit that produces a VQ tensor from fp32 weights (paper, §2.2 The fit:
+ * d-dimensional subvectors, each group of `group` weights of a row scaled by
+ * its maximum absolute value, a K-entry codebook fit by k-means with k-means++
+ * initialization on a random subsample and plain Lloyd iterations; §2.3:
+ * codes packed to their true bit width; §2.6: relative reconstruction error
+ * ||W - W_hat|| / ||W||).  Outputs are the layout of vq_tensor (dense, one
+ * codebook), so the result feeds vq_gemv / vq_gemm directly.
+ *   w: device [rows][cols] fp32, 16-byte aligned; geometry and shape rules as
+ *     for vq_tensor (d, log2_k, group supported; cols % group == 0;
+ *     (cols / d) % 32 == 0); rows * cols / d <= 2^30 subvectors;
+ *   sample_idx: device [n_sample] int32, the subvectors (row-major order)
+ *     k-means++ draws from, 1 <= n_sample <= 2^24 (an index outside the
+ *     subvector range is reduced modulo their count);
+ *   uniforms: device [K] fp64 in [0, 1): the draws of k-means++ (the first
+ *     centre is sample point floor(u_0 * n_sample));
+ *   iters >= 0 Lloyd iterations (a converged iteration changes nothing);
+ *   codes: device [rows][Wr] uint32, 16-byte aligned; codebook: device [K][d]
+ *   fp16, 16-byte aligned; scales: device [rows][cols/group] fp16, 4-byte
+ *   aligned; relerr: device, one fp64;
+ *   workspace: device, >= vq_encode_workspace_bytes(...) bytes, 256-byte
+ *   aligned, owned by the caller (about rows * cols * 8 bytes).
+ * The random numbers are inputs, so a fit is reproducible: its arithmetic is
+ * fixed (fp32 squared distances summed in coordinate order without fused
+ * multiply-add, ties to the lowest centroid; k-means++ draws and Lloyd means
+ * from exact integer sums of values in units of 2^-32), and codes, codebook
+ * and scales are the same bits on every run.
+ */
+size_t vq_encode_workspace_bytes(int32_t rows, int32_t cols, int32_t d, int32_t log2_k, int32_t n_sample);
+vq_status vq_encode(const float *w, int32_t rows, int32_t cols, int32_t d, int32_t log2_k, int32_t group,
+                    const int32_t *sample_idx, int32_t n_sample, const double *uniforms, int32_t iters,
+                    uint32_t *codes, uint16_t *codebook, uint16_t *scales, double *relerr, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
 /* Text for the last non-OK status returned on this thread ("" if none). */
 const char *vq_last_error(void);
 

@@ -219,3 +219,32 @@ def test_io_descriptor_checks(b):
         st = L.vq_gemv_ex(ctypes.byref(t), ctypes.byref(good) if good is not None else None, 0x40000, 0,
                           0x50000, None)
         assert st == b.VQ_OK, L.vq_last_error()
+
+
+def test_encode_checks(b):
+    L = b.LIB
+    ok = dict(w=0x10000, rows=8, cols=256, d=4, k=8, g=64, idx=0x20000, ns=100, u=0x30000, it=3,
+              codes=0x40000, cb=0x50000, sc=0x60000, rel=0x70000, ws=0x100000, wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return b.STATUS_NAMES[L.vq_encode(a["w"], a["rows"], a["cols"], a["d"], a["k"], a["g"], a["idx"], a["ns"],
+                                          a["u"], a["it"], a["codes"], a["cb"], a["sc"], a["rel"], a["ws"],
+                                          a["wsb"], None)]
+
+    assert call(d=3) == "VQ_ERR_GEOMETRY"
+    assert call(k=15) == "VQ_ERR_GEOMETRY"
+    assert call(cols=192) == "VQ_ERR_SHAPE"          # not a multiple of the group
+    assert call(cols=320, g=64, d=8) == "VQ_ERR_SHAPE"   # (cols/d) % 32
+    assert call(ns=0) == "VQ_ERR_SHAPE"
+    assert call(it=-1) == "VQ_ERR_SHAPE"
+    assert call(w=0) == "VQ_ERR_NULL"
+    assert call(u=0x30004) == "VQ_ERR_ALIGN"
+    assert call(codes=0x40004) == "VQ_ERR_ALIGN"
+    assert call(ws=0) == "VQ_ERR_WORKSPACE"
+    assert call(wsb=16) == "VQ_ERR_WORKSPACE"
+    assert call(ws=0x100010) == "VQ_ERR_ALIGN"
+    need = L.vq_encode_workspace_bytes(8, 256, 4, 8, 100)
+    assert need >= 8 * 256 * 8 and need % 256 == 0
+    assert L.vq_encode_workspace_bytes(8, 250, 4, 8, 100) == 0

@@ -83,6 +83,8 @@ def _load():
         "vq_moe_workspace_bytes": (ctypes.c_size_t, [i32, i32, i32]),
         "vq_moe_gemm": (i32, [T, P, i32, P, i32, i32, P, P, ctypes.c_size_t, P]),
         "vq_moe_gemm_no_alloc": (i32, [T, P, i32, P, i32, i32, P, P]),
+        "vq_encode_workspace_bytes": (ctypes.c_size_t, [i32, i32, i32, i32, i32]),
+        "vq_encode": (i32, [P, i32, i32, i32, i32, i32, P, i32, P, i32, P, P, P, P, P, ctypes.c_size_t, P]),
         "vq_last_error": (ctypes.c_char_p, []),
         "vq_status_name": (ctypes.c_char_p, [i32]),
     }
@@ -97,8 +99,8 @@ LIB = _load()
 
 EXPORTED = ("vq_words_per_row", "vq_dequant", "vq_gemv", "vq_gemm", "vq_moe_gemv", "vq_gemv_ex",
             "vq_gemm_ex", "vq_moe_gemv_ex", "vq_moe_gemm_ex",
-            "vq_moe_workspace_bytes", "vq_moe_gemm", "vq_moe_gemm_no_alloc", "vq_last_error",
-            "vq_status_name")
+            "vq_moe_workspace_bytes", "vq_moe_gemm", "vq_moe_gemm_no_alloc", "vq_encode_workspace_bytes",
+            "vq_encode", "vq_last_error", "vq_status_name")
 
 
 def check(status: int) -> None:
@@ -343,3 +345,35 @@ def moe_gemm_no_alloc(w: VQTensor, x, ids, x_per_slot=False, y=None, stream=None
     check(LIB.vq_moe_gemm_no_alloc(ctypes.byref(cs), _ptr(x), int(bool(x_per_slot)), _ptr(ids), T, top_k,
                                    _ptr(y), _stream(stream)))
     return y
+
+
+def encode(w, d: int, log2_k: int, group: int, sample_idx, uniforms, iters: int, workspace=None, stream=None):
+    """vq_encode: fit a VQ tensor to fp32 weights w [rows][cols] on the GPU.
+    sample_idx: int32 [n_sample] subvector indices for k-means++; uniforms:
+    fp64 [K] draws.  Returns (VQTensor, relerr as a 0-d fp64 device tensor)."""
+    torch = _torch()
+    if w.dtype != torch.float32 or w.dim() != 2:
+        raise ValueError("w must be fp32 [rows][cols]")
+    if sample_idx.dtype != torch.int32 or uniforms.dtype != torch.float64:
+        raise ValueError("sample_idx must be int32 and uniforms fp64")
+    rows, cols = w.shape
+    K = 1 << log2_k
+    if uniforms.numel() != K:
+        raise ValueError(f"uniforms must hold K = {K} values")
+    dev = w.device
+    _dev_check(w, sample_idx, uniforms, device=dev)
+    wr = words_per_row(cols, d, log2_k)
+    if wr < 0:
+        raise ValueError("unsupported geometry")
+    codes = torch.empty((rows, wr), dtype=torch.int32, device=dev)
+    codebook = torch.empty((K, d), dtype=torch.float16, device=dev)
+    scales = torch.empty((rows, cols // group), dtype=torch.float16, device=dev)
+    relerr = torch.empty((), dtype=torch.float64, device=dev)
+    need = LIB.vq_encode_workspace_bytes(rows, cols, d, log2_k, sample_idx.numel())
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _dev_check(workspace, device=dev)
+    check(LIB.vq_encode(_ptr(w), rows, cols, d, log2_k, group, _ptr(sample_idx), sample_idx.numel(), _ptr(uniforms),
+                        iters, _ptr(codes), _ptr(codebook), _ptr(scales), _ptr(relerr), _ptr(workspace),
+                        workspace.numel(), _stream(stream)))
+    return VQTensor(codes, codebook, scales, rows, cols, d, log2_k, group), relerr

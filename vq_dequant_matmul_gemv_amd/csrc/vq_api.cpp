@@ -348,4 +348,48 @@ vq_status vq_moe_gemm_no_alloc(const vq_tensor* w, const uint16_t* x, int32_t x_
                     "vq_moe_gemm_no_alloc launch");
 }
 
+// Shape of an encode call (no pointers).
+static vq_status check_encode_shape(int32_t rows, int32_t cols, int32_t d, int32_t log2_k, int32_t group,
+                                    int32_t n_sample) {
+  if ((d != 2 && d != 4 && d != 8) || log2_k < vqmi::kMinBits || log2_k > vqmi::kMaxBits ||
+      (group != 64 && group != 128))
+    return fail(VQ_ERR_GEOMETRY, "vq_encode: unsupported geometry d=%d log2_k=%d group=%d", d, log2_k, group);
+  if (rows < 1 || cols < 1 || cols % group != 0 || (cols / d) % 32 != 0)
+    return fail(VQ_ERR_SHAPE, "vq_encode: rows=%d cols=%d: need cols %% group == 0 and (cols/d) %% 32 == 0", rows,
+                cols);
+  if ((int64_t)rows * cols / d > ((int64_t)1 << 30))
+    return fail(VQ_ERR_SHAPE, "vq_encode: more than 2^30 subvectors");
+  if (n_sample < 1 || n_sample > (1 << 24))
+    return fail(VQ_ERR_SHAPE, "vq_encode: n_sample=%d outside [1, 2^24]", n_sample);
+  return VQ_OK;
+}
+
+size_t vq_encode_workspace_bytes(int32_t rows, int32_t cols, int32_t d, int32_t log2_k, int32_t n_sample) {
+  if (check_encode_shape(rows, cols, d, log2_k, (cols % 64 == 0) ? 64 : 128, n_sample) != VQ_OK) return 0;
+  return vqmi::encode_workspace_bytes(rows, cols, d, log2_k, n_sample);
+}
+
+vq_status vq_encode(const float* w, int32_t rows, int32_t cols, int32_t d, int32_t log2_k, int32_t group,
+                    const int32_t* sample_idx, int32_t n_sample, const double* uniforms, int32_t iters,
+                    uint32_t* codes, uint16_t* codebook, uint16_t* scales, double* relerr, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  vq_status st = check_encode_shape(rows, cols, d, log2_k, group, n_sample);
+  if (st != VQ_OK) return st;
+  if (iters < 0) return fail(VQ_ERR_SHAPE, "vq_encode: iters=%d must be >= 0", iters);
+  if (!w || !sample_idx || !uniforms || !codes || !codebook || !scales || !relerr)
+    return fail(VQ_ERR_NULL, "vq_encode: a required pointer is NULL");
+  if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(codebook, 16) || !aligned(scales, 4) ||
+      !aligned(sample_idx, 4) || !aligned(uniforms, 8) || !aligned(relerr, 8))
+    return fail(VQ_ERR_ALIGN, "vq_encode: w, codes, codebook need 16-byte alignment; scales, sample_idx 4; "
+                              "uniforms, relerr 8");
+  const size_t need = vqmi::encode_workspace_bytes(rows, cols, d, log2_k, n_sample);
+  if (!workspace) return fail(VQ_ERR_WORKSPACE, "vq_encode: workspace is NULL (need %zu bytes)", need);
+  if (workspace_bytes < need)
+    return fail(VQ_ERR_WORKSPACE, "vq_encode: workspace has %zu bytes, need %zu", workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(VQ_ERR_ALIGN, "vq_encode: workspace is not 256-byte aligned");
+  return hip_status(vqmi::launch_encode(w, rows, cols, d, log2_k, group, sample_idx, n_sample, uniforms, iters, codes,
+                                        codebook, scales, relerr, workspace, (hipStream_t)stream),
+                    "vq_encode launch");
+}
+
 }  // extern "C"

@@ -80,4 +80,10 @@ hipError_t static_scratch(void** out);
 hipError_t launch_moe_gemm(const TensorView& w, const IoSpec& io, const void* x, int x_per_slot,
                            const int32_t* ids, int T, int top_k, void* y, void* ws, hipStream_t s);
 
+// The fit of one tensor (vq_encode.hip).
+size_t encode_workspace_bytes(int rows, int cols, int d, int log2_k, int n_sample);
+hipError_t launch_encode(const float* w, int rows, int cols, int d, int log2_k, int group, const int32_t* sample_idx,
+                         int n_sample, const double* uniforms, int iters, uint32_t* codes, uint16_t* codebook,
+                         uint16_t* scales, double* relerr, void* workspace, hipStream_t s);
+
 }  // namespace vqmi

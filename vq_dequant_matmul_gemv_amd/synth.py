@@ -124,6 +124,20 @@ def router_weights(tokens: int, top_k: int, *key) -> np.ndarray:
     return (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
 
 
+def weights(rows: int, cols: int, *key, std: float = 0.02) -> np.ndarray:
+    """fp32 [rows][cols] synthetic weights, N(0, std): the tensors the
+    encoder fits (the pages fit real model weights, which are not here)."""
+    return rng("weights", *key).normal(0.0, std, size=(rows, cols)).astype(np.float32)
+
+
+def fit_draws(n_subvectors: int, n_sample: int, k: int, *key):
+    """The random numbers of one fit: k-means++ subsample indices (int32
+    [n_sample], without replacement) and its k uniforms (fp64 [k])."""
+    g = rng("fit", *key)
+    idx = g.choice(n_subvectors, size=n_sample, replace=False).astype(np.int32)
+    return idx, g.uniform(size=k)
+
+
 def zipf_routing(tokens: int, num_experts: int, top_k: int, *key, alpha: float = 1.1) -> np.ndarray:
     """int32 [tokens][top_k]: distinct expert ids per token, Zipf(alpha) over ranks."""
     g = rng("route", *key)
