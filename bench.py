@@ -56,6 +56,10 @@ def parse():
                     help="rows of the gate matrix the CPU oracle sample covers")
     ap.add_argument("--profile-gate", action="store_true",
                     help="run only a few gate GEMV and GEMM launches (for rocprofv3 --pmc passes)")
+    ap.add_argument("--profile-sweep", choices=["A", "B"], default=None,
+                    help="run only a few config-4 launches of matrix A (17408x5120) or B (5120x17408), d=4 K=256: "
+                         "GEMV at T=1 and GEMM at T=4096 (for rocprofv3 --pmc passes)")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the config-4 sweep rooflines")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain device copy of known size (counter calibration)")
     ap.add_argument("--configs", nargs="?", const="", default=None, metavar="FILTER",
@@ -88,9 +92,10 @@ def copy_probe():
                       "launches": 4}), flush=True)
 
 
-def _pmc_value(fname, counter, kernel_prefix):
+def _pmc_value(fname, counter, kernel_prefix, grid=None):
     """Average per-dispatch value of `counter` for the first kernel whose
-    name starts with kernel_prefix, from a profsum pmc summary."""
+    name starts with kernel_prefix (and whose grid is `grid`, when given),
+    from a profsum pmc summary."""
     path = os.path.join(PROFILES, fname)
     if not os.path.exists(path):
         return None, None
@@ -99,20 +104,20 @@ def _pmc_value(fname, counter, kernel_prefix):
         for line in fh:
             if line.startswith("kernel source digest:"):
                 digest = line.split(":", 1)[1].strip()
-            if line.startswith(kernel_prefix):
+            if line.startswith(kernel_prefix) and (grid is None or f" grid={grid} " in line):
                 for part in line.split():
                     if part.startswith(counter + "="):
                         return float(part.split("=", 1)[1]), digest
     return None, digest
 
 
-def measured_traffic(kernel_prefix, tag):
+def measured_traffic(kernel_prefix, tag, grid=None):
     """HBM bytes per launch of the named kernel from the committed FETCH_SIZE
     and WRITE_SIZE passes, each scaled by the same counter's reading for the
     1 GiB copy; None when a pass is missing or the kernels changed since."""
     from vq_dequant_matmul_gemv_amd.profsum import source_digest
-    f, fd = _pmc_value(f"pmc_fetch_size_{tag}.txt", "FETCH_SIZE", kernel_prefix)
-    w, wd = _pmc_value(f"pmc_write_size_{tag}.txt", "WRITE_SIZE", kernel_prefix)
+    f, fd = _pmc_value(f"pmc_fetch_size_{tag}.txt", "FETCH_SIZE", kernel_prefix, grid)
+    w, wd = _pmc_value(f"pmc_write_size_{tag}.txt", "WRITE_SIZE", kernel_prefix, grid)
     cf, _ = _pmc_value(f"pmc_fetch_size_{COPY_TAG}.txt", "FETCH_SIZE", "torch copy")
     cw, _ = _pmc_value(f"pmc_write_size_{COPY_TAG}.txt", "WRITE_SIZE", "torch copy")
     if None in (f, w, cf, cw) or fd != source_digest() or wd != source_digest():
@@ -120,6 +125,80 @@ def measured_traffic(kernel_prefix, tag):
     fetch_scale = (COPY_READ_BYTES / 1024) / cf     # true KiB per counted KiB
     write_scale = (COPY_WRITE_BYTES / 1024) / cw
     return round((f * fetch_scale + w * write_scale) * 1024)
+
+
+SWEEP = "sweep_17408x5120_d4k256"
+SWEEP_TAG = "sweep_d4k256_17408x5120_and_5120x17408"   # profiles/pmc_*_<tag>.txt of the sweep kernels
+SWEEP_REPLICAS = 16                                   # 16 x 25 MB per matrix: every call streams from HBM
+
+
+def sweep_rooflines(profile_only=None):
+    """Config-4 kernels on one GPU: W_A [17408][5120] and W_B [5120][17408],
+    d=4 K=256 g=64, the GEMV at T = 1 (HBM-bound) and the GEMM at T = 4096
+    (MFMA-bound).  Per-launch durations from bursts of back-to-back launches
+    in one graph (16 GEMVs / 4 GEMMs, rotating over weight replicas), timed
+    with events on the launch stream, median of 5 bursts."""
+    import torch
+    from vq_dequant_matmul_gemv_amd import binding, synth
+    dev = torch.device("cuda", 0)
+    wl = synth.WORKLOADS[SWEEP]
+    out = {}
+    for name in ((profile_only,) if profile_only else ("A", "B")):
+        spec = wl["tensors"][name]
+        base = binding.VQTensor.from_host(synth.tensor(spec, SWEEP, name), spec, device=dev)
+        reps = [base] + [binding.VQTensor(base.codes.clone(), base.codebook.clone(), base.scales.clone(), spec.rows,
+                                          spec.cols, spec.d, spec.log2_k, spec.group)
+                         for _ in range(SWEEP_REPLICAS - 1)]
+        x1 = torch.from_numpy(synth.activations((1, spec.cols), SWEEP, name, "x", 1)).to(dev)
+        xT = torch.from_numpy(synth.activations((4096, spec.cols), SWEEP, name, "x", 4096)).to(dev)
+        y1 = torch.empty((1, spec.rows), dtype=torch.float32, device=dev)
+        yT = torch.empty((4096, spec.rows), dtype=torch.float32, device=dev)
+        gemv = [lambda w=reps[i % SWEEP_REPLICAS]: binding.gemv(w, x1, y1) for i in range(16)]
+        gemm = [lambda w=reps[i % SWEEP_REPLICAS]: binding.gemm(w, xT, yT) for i in range(4)]
+        if profile_only:
+            for c in gemv[:4] + gemm[:2]:
+                c()
+            torch.cuda.synchronize()
+            continue
+        for c in gemv + gemm:   # warm
+            c()
+        torch.cuda.synchronize()
+        res = {}
+        for key, calls in (("gemv_T1", gemv), ("gemm_T4096", gemm)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for c in calls:
+                    c()
+            times = []
+            for _ in range(5):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda._sleep(1_000_000)
+                a.record()
+                g.replay()
+                b.record()
+                torch.cuda.synchronize()
+                times.append(a.elapsed_time(b) * 1e-3 / len(calls))
+            res[key] = sorted(times)[2]
+            del g
+        nb = tensor_bytes(spec, 1)
+        flops = 2.0 * 4096 * spec.rows * spec.cols
+        gbps = nb / res["gemv_T1"] / 1e9
+        tflops = flops / res["gemm_T4096"] / 1e12
+        out[f"{name}_{spec.rows}x{spec.cols}"] = {
+            "gemv_T1": {"bound": "hbm", "us": round(res["gemv_T1"] * 1e6, 2), "achieved": round(gbps, 2),
+                        "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                        "algorithmic_bytes": nb,
+                        "traffic": measured_traffic("vq_gemv_kernel<4, 8, 64", SWEEP_TAG + "_" + name)},
+            "gemm_T4096": {"bound": "mfma", "us": round(res["gemm_T4096"] * 1e6, 2), "achieved": round(tflops, 2),
+                           "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                           "algorithmic_bytes": tensor_bytes(spec, 4096),
+                           "traffic": measured_traffic("vq_gemm_kernel<4, 8, 64", SWEEP_TAG + "_" + name)}}
+        del reps, base, xT, yT
+        torch.cuda.empty_cache()
+    if profile_only:
+        print(f"profile-sweep {profile_only}: 4 GEMVs (T=1) and 2 GEMMs (T=4096)", flush=True)
+    return out
 
 
 def tensor_bytes(spec, T):
@@ -173,7 +252,8 @@ def configs_report(only=""):
 
     dev = torch.device("cuda", 0)
     from vq_dequant_matmul_gemv_amd.profsum import source_digest
-    out = [f"command: {REPORT_CMD}", f"kernel source digest: {source_digest()}", "",
+    out = [f"command: {REPORT_CMD}", f"kernel source digest: {source_digest()}",
+           f"encoder source digest: {source_digest('encoder')}", "",
            "vq_gemv hands token counts above its measured crossover to the MFMA kernel (the rows with",
            "larger T under vq_gemv time that kernel); vq_gemm always runs the MFMA kernel.", "",
            "| workload | tensor | call | T | per call us (median, p10, p90) | GB/s | % of 8 TB/s | TFLOP/s | % of 2.5 PF |",
@@ -364,6 +444,112 @@ def configs_report(only=""):
         dense(wl, n, W[wl]["tensors"][n], Ts, Ts, (wl, n))
     if keep(wl):
         dequant_row(wl, "A", W[wl]["tensors"]["A"], (wl, "A"))
+
+    # ---- the next rows: fused MLP epilogues, the bf16 profile, other code
+    # widths, the encoder ----------------------------------------------------
+    def mlp_chain(wl_name, gu_spec, dn_spec, T, routed_top_k=None):
+        """gate/up stored as one tensor of interleaved rows with the SwiGLU
+        epilogue (fp16 h), then down taking h; routed: down with the
+        router-weighted combine.  Bytes: both tensors (distinct experts hit)
+        + x + h + y; flops: both products."""
+        key = ("next", wl_name)
+        hg = synth.tensor(gu_spec, *key, "gu")
+        hd = synth.tensor(dn_spec, *key, "dn")
+        wgu = binding.VQTensor.from_host(hg, gu_spec, device=dev)
+        wdn = binding.VQTensor.from_host(hd, dn_spec, device=dev)
+        per_gu = gu_spec.rows * gu_spec.words * 4 + gu_spec.rows * (gu_spec.cols // gu_spec.group) * 2
+        per_dn = dn_spec.rows * dn_spec.words * 4 + dn_spec.rows * (dn_spec.cols // dn_spec.group) * 2
+        nrep = 1 if routed_top_k else int(max(1, -(-1.1e9 // (per_gu + per_dn))))
+        reps = [(wgu, wdn)] + [(binding.VQTensor(wgu.codes.clone(), wgu.codebook.clone(), wgu.scales.clone(),
+                                                 gu_spec.rows, gu_spec.cols, gu_spec.d, gu_spec.log2_k, gu_spec.group,
+                                                 gu_spec.experts),
+                                binding.VQTensor(wdn.codes.clone(), wdn.codebook.clone(), wdn.scales.clone(),
+                                                 dn_spec.rows, dn_spec.cols, dn_spec.d, dn_spec.log2_k, dn_spec.group,
+                                                 dn_spec.experts)) for _ in range(nrep - 1)]
+        x = torch.from_numpy(synth.activations((T, gu_spec.cols), *key, "x", T)).to(dev)
+        I = gu_spec.rows // 2
+        calls, nbytes = [], 0
+        if routed_top_k:
+            k = routed_top_k
+            draws = [synth.zipf_routing(T, gu_spec.experts, k, *key, "ids", T, r) for r in range(8)]
+            ids = [torch.from_numpy(d.astype(np.int32)).to(dev) for d in draws]
+            rw = torch.from_numpy(synth.router_weights(T, k, *key, "rw")).to(dev)
+            h = torch.empty((T, k, I), dtype=torch.float16, device=dev)
+            y = torch.empty((T, dn_spec.rows), dtype=torch.float32, device=dev)
+            fn = binding.moe_gemv if T == 1 else binding.moe_gemm
+            ws = torch.empty(max(16, binding.workspace_bytes(T, k, gu_spec.experts)), dtype=torch.uint8, device=dev)
+            extra = {} if T == 1 else {"workspace": ws}
+            for i in range(8):
+                def c(d=ids[i]):
+                    fn(wgu, x, d, y=h, epilogue="swiglu", **extra)
+                    fn(wdn, h, d, x_per_slot=True, y=y, epilogue="combine", route_weights=rw, **extra)
+                calls.append(c)
+                hit = len(np.unique(draws[i]))
+                nbytes += hit * (per_gu + per_dn) + x.numel() * 2 + 2 * h.numel() * 2 + y.numel() * 4
+            flops = 2.0 * T * k * (gu_spec.rows * gu_spec.cols + dn_spec.rows * dn_spec.cols)
+            nbytes /= 8
+        else:
+            h = torch.empty((T, I), dtype=torch.float16, device=dev)
+            y = torch.empty((T, dn_spec.rows), dtype=torch.float32, device=dev)
+            fn = binding.gemv if T == 1 else binding.gemm
+            for i in range(max(8, nrep)):
+                def c(p=reps[i % len(reps)]):
+                    fn(p[0], x, y=h, epilogue="swiglu")
+                    fn(p[1], h, y=y)
+                calls.append(c)
+            nbytes = per_gu + per_dn + x.numel() * 2 + 2 * h.numel() * 2 + y.numel() * 4
+            flops = 2.0 * T * (gu_spec.rows * gu_spec.cols + dn_spec.rows * dn_spec.cols)
+        us = timed(calls)
+        call = ("vq_moe_gemv" if T == 1 else "vq_moe_gemm") if routed_top_k else ("vq_gemv" if T == 1 else "vq_gemm")
+        row(wl_name, "MLP: gate/up SwiGLU (interleaved rows, fp16 h) -> down" +
+            (" with router-weighted combine" if routed_top_k else ""), call + " x2", T, us, nbytes, flops)
+        del reps, wgu, wdn
+        torch.cuda.empty_cache()
+
+    def bf16_rows(wl_name, spec, key):
+        """The bf16 profile: bf16 x in, bf16 y out, against fp16 x / fp32 y."""
+        host = synth.tensor(spec, *key)
+        reps = replicas(spec, host, tensor_bytes(spec, 1), cap=24)
+        for T, fn in ((1, "gemv"), (2048, "gemm")):
+            xb = synth.activations_bf16((T, spec.cols), *key, "xb", T)
+            x = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+            y = torch.empty((T, spec.rows), dtype=torch.bfloat16, device=dev)
+            n = 16 if T == 1 else 8
+            calls = [(lambda w=reps[i % len(reps)]: getattr(binding, fn)(w, x, y)) for i in range(n)]
+            us = timed(calls)
+            row(wl_name, f"{spec.rows}x{spec.cols} bf16 x, bf16 y", "vq_" + fn, T, us,
+                tensor_bytes(spec, T) - T * spec.rows * 2, 2.0 * T * spec.rows * spec.cols)
+        del reps
+        torch.cuda.empty_cache()
+
+    def encode_row(rows, cols, d, b, g, n_s, iters):
+        """vq_encode of one tensor (per call; the k-means++ seeding runs in
+        one workgroup, the Lloyd iterations grid-wide); flops counted are the
+        assignment's 3 d operations per (subvector, centroid) per pass."""
+        w = torch.from_numpy(synth.weights(rows, cols, "bench-enc")).to(dev)
+        idx, u = synth.fit_draws(rows * cols // d, n_s, 1 << b, "bench-enc")
+        idx, u = torch.from_numpy(idx).to(dev), torch.from_numpy(u).to(dev)
+        wsz = binding.LIB.vq_encode_workspace_bytes(rows, cols, d, b, n_s)
+        ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
+        us = timed([lambda: binding.encode(w, d, b, g, idx, u, iters, workspace=ws)], reps=5)
+        n = rows * cols // d
+        ops = 3.0 * d * n * (1 << b) * (iters + 1)
+        row("encoder", f"fit {rows}x{cols} d{d}/K{1 << b}/g{g}, sample {n_s}, {iters} Lloyd iterations",
+            "vq_encode", "-", us, rows * cols * 4, ops)
+
+    nx = "next_rows"
+    if keep(nx):
+        S = synth.Spec
+        mlp_chain(nx, S(2 * 17408, 5120, 2, 8, 64), S(5120, 17408, 2, 8, 64), 1)
+        mlp_chain(nx, S(2 * 17408, 5120, 2, 8, 64), S(5120, 17408, 2, 8, 64), 2048)
+        mlp_chain(nx, S(2 * 1024, 4096, 4, 8, 64, experts=256), S(4096, 1024, 4, 8, 64, experts=256), 1, 8)
+        mlp_chain(nx, S(2 * 1024, 4096, 4, 8, 64, experts=256), S(4096, 1024, 4, 8, 64, experts=256), 1024, 8)
+        bf16_rows(nx, S(17408, 5120, 2, 8, 64), (nx, "bf16"))
+        for (d, b) in ((2, 9), (4, 11), (4, 14), (8, 14)):
+            spec = S(17408, 5120, d, b, 64)
+            dense(nx, f"17408x5120 d{d}/K{1 << b}", spec, [1], [2048], (nx, d, b))
+    if keep("encoder"):
+        encode_row(1024, 4096, 4, 8, 64, 16384, 10)
     if only:
         print("\n".join(out), flush=True)
         return
@@ -404,6 +590,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.profile_sweep:
+        sweep_rooflines(profile_only=args.profile_sweep)
         return
     if args.configs is not None:
         configs_report(args.configs)
@@ -610,6 +799,12 @@ def main():
                              "traffic": measured_traffic("vq_gemm_kernel<2, 8, 64", GATE_TAG),
                              "algorithmic_bytes": tensor_bytes(specs["gate"], PREFILL_T)},
     }
+    if not args.no_sweep:
+        # config 4 (the 17408x5120 / 5120x17408 d=4 K=256 sweep): its barred
+        # points, GEMV at T = 1 and GEMM at T = 4096, on the same GPU
+        del reps, g_dec, g_dec_all, g_pre, g_burst
+        torch.cuda.empty_cache()
+        out["roofline_sweep_config"] = sweep_rooflines()
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(host["gate"], specs["gate"], args.cpu_rows)
     print(json.dumps(out), flush=True)

@@ -52,6 +52,30 @@ __device__ __forceinline__ float sqdist(const float* x, const float* c) {
 
 __device__ __forceinline__ int64_t to_fixed(float v) { return __double2ll_rn((double)v * kFixedOne); }
 
+// D floats at byte voff + soff of a buffer (soff wave-uniform): one address
+// register per lane whatever the point, so many loads can be in flight.  (The
+// loaded words are reinterpreted as a whole float vector: bit-casting single
+// elements of the loaded vector lost all but the first element in this
+// compiler.)
+template <int D>
+__device__ __forceinline__ void load_point(float* x, rsrc_t r, uint32_t voff, uint32_t soff) {
+  typedef float float2_v __attribute__((ext_vector_type(2)));
+  if constexpr (D == 2) {
+    const float2_v f = __builtin_bit_cast(float2_v, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+    x[0] = f.x;
+    x[1] = f.y;
+  } else {
+#pragma unroll
+    for (int q = 0; q < D / 4; ++q) {
+      const float4_t f = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16u * q, soff, 0));
+      x[4 * q] = f.x;
+      x[4 * q + 1] = f.y;
+      x[4 * q + 2] = f.z;
+      x[4 * q + 3] = f.w;
+    }
+  }
+}
+
 // ---- 1. scales and subvectors: one wave per (row, group) -------------------
 __global__ __launch_bounds__(256) void enc_scale_kernel(const float* __restrict__ w, int64_t n_groups, int group,
                                                         uint16_t* __restrict__ scales, float* __restrict__ pts) {
@@ -80,16 +104,24 @@ __global__ __launch_bounds__(256) void enc_scale_kernel(const float* __restrict_
 }
 
 // ---- 2. the subsample -------------------------------------------------------
+// Sample point i goes to slot i, or, when `per` > 0 (the register seeding
+// kernel, thread t owning points t*per ... t*per + per - 1), to slot
+// (i % per) * 1024 + i / per, so that the threads' k-th points are adjacent.
+__host__ __device__ inline int64_t sample_slot(int64_t i, int per) {
+  return per > 0 ? (i % per) * 1024 + i / per : i;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void enc_gather_kernel(const float* __restrict__ pts, int64_t n_pts,
-                                                         const int32_t* __restrict__ idx, int n_s,
+                                                         const int32_t* __restrict__ idx, int n_s, int per,
                                                          float* __restrict__ sample) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n_s) return;
   int64_t j = idx[i] % n_pts;  // indices outside [0, n) are reduced modulo n
   if (j < 0) j += n_pts;
+  const int64_t slot = sample_slot(i, per);
 #pragma unroll
-  for (int t = 0; t < D; ++t) sample[(int64_t)i * D + t] = pts[j * D + t];
+  for (int t = 0; t < D; ++t) sample[slot * D + t] = pts[j * D + t];
 }
 
 // Inclusive scan of an int64 over the block (1024 threads, 16 waves).
@@ -173,6 +205,215 @@ __global__ __launch_bounds__(1024) void enc_kmeanspp_kernel(const float* __restr
       for (int t = 0; t < D; ++t) x[t] = sample[(int64_t)i * D + t];
       const float dist = sqdist<D>(x, c);
       d2[i] = j == 0 ? dist : fminf(d2[i], dist);
+    }
+    __syncthreads();
+  }
+}
+
+// The same seeding with each thread's squared distances in registers: up to
+// P sample points per thread (n <= NT * P; the sample stored transposed, so
+// the threads' k-th points are adjacent), and for d = 2 the points
+// themselves in registers too, so that a step makes no global load: the
+// thread owning the drawn point hands its coordinates over through LDS.  The
+// draw and the arithmetic are the kernel's above, step for step.
+template <int D, int P, int NT>
+__global__ __launch_bounds__(NT) void enc_kmeanspp_reg_kernel(const float* __restrict__ sample, int n, int K,
+                                                              const double* __restrict__ u,
+                                                              float* __restrict__ cent) {
+  constexpr bool XREG = D == 2;
+  __shared__ int64_t part[32];
+  __shared__ int chosen;
+  __shared__ int from_regs;
+  __shared__ float cs[D];
+  const int tid = threadIdx.x;
+  const int per = (n + NT - 1) / NT;
+  const int i0 = min(n, tid * per), cnt = min(n, i0 + per) - i0;
+  auto draw_uniform = [&](double uj) {
+    const int64_t k = (int64_t)floor(uj * (double)n);
+    return (int)min<int64_t>(max<int64_t>(k, 0), n - 1);
+  };
+  const rsrc_t rs = make_rsrc(sample, (uint64_t)NT * P * D * 4);
+  const uint32_t voff = (uint32_t)tid * D * 4u;  // this thread's k-th point: slot k * NT + tid
+  auto point = [&](int k, float* x) {
+    if (k < cnt) load_point<D>(x, rs, voff, (uint32_t)k * NT * D * 4u);
+    else
+#pragma unroll
+      for (int t = 0; t < D; ++t) x[t] = 0.f;
+  };
+  float d2[P];
+  float xr[XREG ? P : 1][D];
+#pragma unroll
+  for (int k = 0; k < P; ++k) {
+    d2[k] = 0.f;
+    if constexpr (XREG) point(k, xr[k]);
+  }
+  for (int j = 0; j < K; ++j) {
+    if (tid == 0) from_regs = 0;
+    if (j == 0) {
+      if (tid == 0) chosen = draw_uniform(u[j]);
+    } else {
+      int64_t local = 0;
+#pragma unroll
+      for (int k = 0; k < P; ++k)
+        if (k < cnt) local += to_fixed(d2[k]);
+      int64_t total;
+      const int64_t incl = block_scan_i64(local, part, total);
+      // the search recomputes the fixed-point weights: without this the
+      // compiler keeps every point's int64 weight alive across the scan
+#pragma unroll
+      for (int k = 0; k < P; ++k) asm volatile("" : "+v"(d2[k]));
+      if (total == 0) {
+        if (tid == 0) chosen = draw_uniform(u[j]);
+      } else {
+        int64_t target = (int64_t)floor(u[j] * (double)total);
+        target = min<int64_t>(max<int64_t>(target, 0), total - 1);
+        const int64_t excl = incl - local;
+        if (excl <= target && target < incl) {
+          int64_t run = excl;
+          bool found = false;
+#pragma unroll
+          for (int k = 0; k < P; ++k) {
+            if (k < cnt && !found) {
+              run += to_fixed(d2[k]);
+              if (run > target) {
+                found = true;
+                chosen = i0 + k;
+                if constexpr (XREG) {
+#pragma unroll
+                  for (int t = 0; t < D; ++t) cs[t] = xr[k][t];
+                  from_regs = 1;
+                }
+              }
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < D && !from_regs) cs[tid] = sample[sample_slot(chosen, per) * D + tid];
+    __syncthreads();
+    float c[D];
+#pragma unroll
+    for (int t = 0; t < D; ++t) c[t] = cs[t];
+    if (tid < D) cent[(int64_t)j * D + tid] = cs[tid];
+    if constexpr (XREG) {
+#pragma unroll
+      for (int k = 0; k < P; ++k) {
+        if (k < cnt) {
+          const float dist = sqdist<D>(xr[k], c);
+          d2[k] = j == 0 ? dist : fminf(d2[k], dist);
+        }
+      }
+    } else {
+      // batches of 32 / D points: their loads in flight together, the
+      // scheduling barrier keeps the compiler from hoisting every batch's
+      // loads at once
+      constexpr int BP = 32 / D;
+#pragma unroll
+      for (int kb = 0; kb < P; kb += BP) {
+        float x[BP][D];
+#pragma unroll
+        for (int k = 0; k < BP; ++k) point(kb + k, x[k]);
+#pragma unroll
+        for (int k = 0; k < BP; ++k) {
+          if (kb + k < cnt) {
+            const float dist = sqdist<D>(x[k], c);
+            d2[kb + k] = j == 0 ? dist : fminf(d2[kb + k], dist);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// The seeding for d = 4 and 8 (whose points do not fit in registers beside
+// everything else): squared distances in registers, the thread's points
+// loaded from the transposed sample every step, in batches.
+template <int D, int P, int NT>
+__global__ __launch_bounds__(NT) void enc_kmeanspp_regd_kernel(const float* __restrict__ sample, int n, int K,
+                                                               const double* __restrict__ u,
+                                                               float* __restrict__ cent) {
+  __shared__ int64_t part[32];
+  __shared__ int chosen;
+  __shared__ float cs[D];
+  const int tid = threadIdx.x;
+  const int per = (n + NT - 1) / NT;
+  const int i0 = min(n, tid * per), cnt = min(n, i0 + per) - i0;
+  auto draw_uniform = [&](double uj) {
+    const int64_t k = (int64_t)floor(uj * (double)n);
+    return (int)min<int64_t>(max<int64_t>(k, 0), n - 1);
+  };
+  const rsrc_t rs = make_rsrc(sample, (uint64_t)NT * P * D * 4);
+  const uint32_t voff = (uint32_t)tid * D * 4u;  // this thread's k-th point: slot k * NT + tid
+  float d2[P];
+#pragma unroll
+  for (int k = 0; k < P; ++k) d2[k] = 0.f;
+  for (int j = 0; j < K; ++j) {
+    if (j == 0) {
+      if (tid == 0) chosen = draw_uniform(u[0]);
+    } else {
+      int64_t local = 0;
+#pragma unroll
+      for (int k = 0; k < P; ++k)
+        if (k < cnt) local += to_fixed(d2[k]);
+      int64_t total;
+      const int64_t incl = block_scan_i64(local, part, total);
+#pragma unroll
+      for (int k = 0; k < P; ++k) asm volatile("" : "+v"(d2[k]));
+      if (total == 0) {
+        if (tid == 0) chosen = draw_uniform(u[j]);
+      } else {
+        int64_t target = (int64_t)floor(u[j] * (double)total);
+        target = min<int64_t>(max<int64_t>(target, 0), total - 1);
+        const int64_t excl = incl - local;
+        if (excl <= target && target < incl) {
+          int64_t run = excl;
+          int pick = i0 + cnt - 1;
+          bool found = false;
+#pragma unroll
+          for (int k = 0; k < P; ++k) {
+            if (k < cnt && !found) {
+              run += to_fixed(d2[k]);
+              if (run > target) {
+                pick = i0 + k;
+                found = true;
+              }
+            }
+          }
+          chosen = pick;
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < D) {
+      cs[tid] = sample[sample_slot(chosen, per) * D + tid];
+      cent[(int64_t)j * D + tid] = cs[tid];
+    }
+    __syncthreads();
+    float c[D];
+#pragma unroll
+    for (int t = 0; t < D; ++t) c[t] = cs[t];
+    constexpr int BP = 32 / D;
+#pragma unroll
+    for (int kb = 0; kb < P; kb += BP) {
+      float x[BP][D];
+#pragma unroll
+      for (int k = 0; k < BP; ++k) {
+        if (kb + k < cnt) load_point<D>(x[k], rs, voff, (uint32_t)(kb + k) * NT * D * 4u);
+        else
+#pragma unroll
+          for (int t = 0; t < D; ++t) x[k][t] = 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < BP; ++k) {
+        if (kb + k < cnt) {
+          const float dist = sqdist<D>(x[k], c);
+          d2[kb + k] = j == 0 ? dist : fminf(d2[kb + k], dist);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
   }
@@ -370,10 +611,21 @@ hipError_t encode_d(const float* w, int rows, int cols, int log2_k, int group, c
   hipLaunchKernelGGL(enc_scale_kernel, dim3((unsigned)((n_groups + 3) / 4)), dim3(256), 0, s, w, n_groups, group,
                      scales_out, ws.pts);
   VQMI_CHECK(hipGetLastError());
+  const bool reg_seeding = n_s <= 1024 * 16;  // the register seeding kernel reads the sample transposed
   hipLaunchKernelGGL(enc_gather_kernel<D>, dim3((n_s + 255) / 256), dim3(256), 0, s, ws.pts, n_pts, sample_idx, n_s,
-                     ws.sample);
+                     reg_seeding ? (n_s + 1023) / 1024 : 0, ws.sample);
   VQMI_CHECK(hipGetLastError());
-  hipLaunchKernelGGL(enc_kmeanspp_kernel<D>, dim3(1), dim3(1024), 0, s, ws.sample, n_s, K, uniforms, ws.cent, ws.d2);
+  // seeding: squared distances in registers for up to 16,384 sample points
+  // (16 per thread), in the workspace beyond that
+  if (reg_seeding) {
+    if constexpr (D == 2)
+      hipLaunchKernelGGL((enc_kmeanspp_reg_kernel<D, 16, 1024>), dim3(1), dim3(1024), 0, s, ws.sample, n_s, K,
+                         uniforms, ws.cent);
+    else
+      hipLaunchKernelGGL((enc_kmeanspp_regd_kernel<D, 16, 1024>), dim3(1), dim3(1024), 0, s, ws.sample, n_s, K,
+                         uniforms, ws.cent);
+  } else
+    hipLaunchKernelGGL(enc_kmeanspp_kernel<D>, dim3(1), dim3(1024), 0, s, ws.sample, n_s, K, uniforms, ws.cent, ws.d2);
   VQMI_CHECK(hipGetLastError());
   const unsigned assign_blocks = (unsigned)((n_pts + kAssignThreads - 1) / kAssignThreads);
   const bool lds = (int64_t)K * (D + 1) * 8 <= kAccumLds;

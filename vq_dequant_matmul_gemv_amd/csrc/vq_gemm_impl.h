@@ -582,38 +582,88 @@ __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
   // (l32, h) holds W row row_base + 32*mb + l32 for tokens 32*nb + 8*(i/4) +
   // 4*h + (i%4): for each i a half-wave covers 32 consecutive y elements of
   // one token (128 contiguous bytes), for stores and atomics alike.
-  // Output step (block-uniform branches): SwiGLU pairs rows 2i (gate, even
-  // lane) and 2i + 1 (up, the odd neighbour, fetched by a DPP swap; both
-  // lanes of a pair hold the same tokens) into y[.][i]; the combine adds
-  // router weight x row into y[token]; otherwise y[.][r] in y's type, or an
-  // atomic fp32 add for the K slices of a split tile.
+  // Output step.  Lane (l32, h) holds W row row_base + 32*mb + l32 for tokens
+  // 32*nb + 8*(i/4) + 4*h + (i%4).  Each output kind has a loop nest of its
+  // own (block-uniform branch outside the loops), so every nest unrolls and
+  // the accumulators stay in registers.
   const int row = row_base + l32;  // + 32 * mb
-  const int epi = a.epi, y_kind = a.y_kind;
+  auto out_row = [&](int tok) {
+    if constexpr (MOE) return a.pairs[first + tok];
+    else return tok_base + tok;
+  };
+  if (a.epi == kEpiNone && a.y_kind == kOutF32) {
+    // plain fp32: for each i a half-wave covers 32 consecutive y elements of
+    // one token (128 contiguous bytes), for stores and atomics alike
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
+    for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int tok = nb * 32 + 8 * (i / 4) + 4 * h + (i % 4);
-      if (tok >= count) continue;
-      int yr;
-      if constexpr (MOE) yr = a.pairs[first + tok];
-      else yr = tok_base + tok;
+      for (int i = 0; i < 16; ++i) {
+        const int tok = nb * 32 + 8 * (i / 4) + 4 * h + (i % 4);
+        if (tok >= count) continue;
+        float* yrow = reinterpret_cast<float*>(a.y) + (int64_t)out_row(tok) * a.rows;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int r = row + 32 * mb;
-        const float v = acc[mb][nb][i];
-        if (epi == kEpiSwiglu) {
-          const float up = dpp_mov<0xB1>(v);  // quad_perm [1,0,3,2]: the odd neighbour's row
-          if ((l32 & 1) == 0 && r < a.rows) store_out(a.y, (int64_t)yr * (a.rows >> 1) + (r >> 1), swiglu(v, up), y_kind);
-        } else if (r < a.rows) {
-          if (epi == kEpiCombine) {
-            if constexpr (MOE)
-              atomicAdd(reinterpret_cast<float*>(a.y) + (int64_t)(yr / a.top_k) * a.rows + r, a.route_w[yr] * v);
-          } else if (nslices > 1) {
-            atomicAdd(reinterpret_cast<float*>(a.y) + (int64_t)yr * a.rows + r, v);
-          } else {
-            store_out(a.y, (int64_t)yr * a.rows + r, v, y_kind);
+        for (int mb = 0; mb < MB; ++mb) {
+          const int r = row + 32 * mb;
+          if (r < a.rows) {
+            if (nslices > 1) atomicAdd(yrow + r, acc[mb][nb][i]);  // block-uniform branch
+            else yrow[r] = acc[mb][nb][i];
           }
+        }
+      }
+    }
+  } else if (a.epi == kEpiSwiglu) {
+    // rows 2i (gate, even lane) and 2i + 1 (up, the odd neighbour, fetched by
+    // a DPP swap; both lanes of a pair hold the same tokens) -> y[.][i]
+    const int y_kind = a.y_kind, half_rows = a.rows >> 1;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int tok = nb * 32 + 8 * (i / 4) + 4 * h + (i % 4);
+        if (tok >= count) continue;
+        const int64_t ybase = (int64_t)out_row(tok) * half_rows;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int r = row + 32 * mb;
+          const float up = dpp_mov<0xB1>(acc[mb][nb][i]);  // quad_perm [1,0,3,2]
+          if ((l32 & 1) == 0 && r < a.rows) store_out(a.y, ybase + (r >> 1), swiglu(acc[mb][nb][i], up), y_kind);
+        }
+      }
+    }
+  } else if (a.epi == kEpiCombine) {
+    // routed only: y[token] += router weight x row
+    if constexpr (MOE) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int tok = nb * 32 + 8 * (i / 4) + 4 * h + (i % 4);
+          if (tok >= count) continue;
+          const int pair = out_row(tok);
+          const float wgt = a.route_w[pair];
+          float* yrow = reinterpret_cast<float*>(a.y) + (int64_t)(pair / a.top_k) * a.rows;
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const int r = row + 32 * mb;
+            if (r < a.rows) atomicAdd(yrow + r, wgt * acc[mb][nb][i]);
+          }
+        }
+      }
+    }
+  } else {
+    // fp16 / bf16 y (such tiles are never split along K)
+    const int y_kind = a.y_kind;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int tok = nb * 32 + 8 * (i / 4) + 4 * h + (i % 4);
+        if (tok >= count) continue;
+        const int64_t ybase = (int64_t)out_row(tok) * a.rows;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int r = row + 32 * mb;
+          if (r < a.rows) store_out(a.y, ybase + r, acc[mb][nb][i], y_kind);
         }
       }
     }

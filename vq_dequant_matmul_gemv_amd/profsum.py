@@ -12,7 +12,8 @@ profiles/.
 
 Only the library's kernels (and, for the copy calibration, the copy kernel)
 are listed.  The kernel source digest printed with each summary lets a reader
-see whether the kernels have changed since the counters were taken.
+see whether the kernels have changed since the counters were taken (the
+matmul kernels and the encoder have digests of their own).
 """
 
 from __future__ import annotations
@@ -28,13 +29,22 @@ from collections import defaultdict
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
-def source_digest() -> str:
-    """sha256 over the kernel sources (csrc/*.hip and csrc/*.h), 12 hex chars.
-    The C-ABI wrapper and the public header are left out: they launch the
-    kernels but do not change what a launch does on the GPU."""
+ENCODER_SOURCES = ("vq_encode.hip",)
+
+
+def source_digest(part: str = "matmul") -> str:
+    """sha256 over kernel sources, 12 hex chars: "matmul" = every csrc/*.hip
+    and csrc/*.h except the encoder's, "encoder" = the encoder's source and
+    the shared headers.  The C-ABI wrapper and the public header are left
+    out: they launch the kernels but do not change what a launch does on the
+    GPU."""
     h = hashlib.sha256()
     files = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")) +
                    glob.glob(os.path.join(HERE, "csrc", "*.h")))
+    if part == "matmul":
+        files = [f for f in files if os.path.basename(f) not in ENCODER_SOURCES]
+    else:
+        files = [f for f in files if os.path.basename(f) in ENCODER_SOURCES or f.endswith(".h")]
     for f in files:
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode())
@@ -121,7 +131,8 @@ def main():
     ap.add_argument("--cmd", required=True, help="the full command that produced DIR")
     ap.add_argument("--copy", action="store_true", help="also list torch's copy kernel")
     a = ap.parse_args()
-    lines = [f"command: {a.cmd}", f"kernel source digest: {source_digest()}", ""]
+    lines = [f"command: {a.cmd}", f"kernel source digest: {source_digest()}",
+             f"encoder source digest: {source_digest('encoder')}", ""]
     lines += trace(a.dir, a.copy) if a.mode == "trace" else pmc(a.dir, a.copy)
     print("\n".join(lines))
 
