@@ -128,8 +128,13 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
   static_assert(C <= gemv_max_c(D), "tile does not fit the VGPR budget");
 
   __shared__ __align__(16) uint8_t cb_lds[LY::kBytes];
-  constexpr int XBYTES = XS * 8192;
-  __shared__ __align__(16) uint8_t x_lds[XBYTES];                   // [nq * 16 * D] fp16
+  constexpr int XBYTES = XS * 8192;                                 // x bytes staged at most
+  // In LDS each chunk's 32 D bytes of x are followed by 16 bytes of padding:
+  // the lanes of a row read consecutive chunks' x at once, and unpadded the
+  // 32 D-byte stride would put 8 to 16 of them on the same banks.
+  constexpr int XCB = 32 * D;
+  constexpr int XSTRIDE = XCB + 16;
+  __shared__ __align__(16) uint8_t x_lds[XBYTES / XCB * XSTRIDE];   // [nq][XSTRIDE]
   __shared__ __align__(16) uint8_t s_lds[kGemvScaleBytes];          // the block's scale rows
   __shared__ float pieces[kGemvPieces];                             // [rows][passes]
 
@@ -326,7 +331,8 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
 #pragma unroll
   for (int q = 0; q < XL; ++q) {
     const uint32_t o = (uint32_t)(tid + q * NT) * 16u;
-    if (o < (uint32_t)XBYTES) *reinterpret_cast<u32x4*>(x_lds + o) = x_bf16 ? bf16x8_to_f16x8(xg[q]) : xg[q];
+    if (o < (uint32_t)XBYTES)
+      *reinterpret_cast<u32x4*>(x_lds + o + o / XCB * 16u) = x_bf16 ? bf16x8_to_f16x8(xg[q]) : xg[q];
   }
 #pragma unroll
   for (int q = 0; q < SL; ++q) {
@@ -361,7 +367,7 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
 #pragma unroll
         for (int k = 0; k < HX / 4; ++k) {
           u32x4 v = u32x4{0u, 0u, 0u, 0u};
-          if (ok) v = *reinterpret_cast<const u32x4*>(x_lds + (uint32_t)q * 32u * D + 16u * k);
+          if (ok) v = *reinterpret_cast<const u32x4*>(x_lds + (uint32_t)q * XSTRIDE + 16u * k);
           xv[j][4 * k + 0] = as_half2(v.x);
           xv[j][4 * k + 1] = as_half2(v.y);
           xv[j][4 * k + 2] = as_half2(v.z);
