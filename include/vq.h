@@ -74,7 +74,12 @@ typedef enum {
  * one tensor per (layer, projection) holding all experts -- paper, Appendix A,
  * on expert modules).
  *
- * Supported geometry: d in {2, 4, 8}, log2_k in {8, 12}, group in {64, 128}.
+ * Supported geometry: d in {2, 4, 8}, log2_k in 4 .. 14 (K = 16 ... 16384;
+ * the paper's builds run from d2/K16 to d4/K16384, section 1 Notation; the
+ * published ones use 8 and 12 bits), group in {64, 128}.  Codebooks of up to
+ * 64 KiB (K * d * 2 bytes) are read from LDS, larger ones (d4/K16384,
+ * d8/K8192, d8/K16384) from device memory, which is slower (paper section
+ * 3.1 on codebooks past threadgroup memory).
  * Shape rules (else VQ_ERR_SHAPE): rows >= 1; cols >= 1; cols % group == 0;
  * group % d == 0; (cols / d) % 32 == 0 (rows hold whole 32-code blocks, so
  * no row needs padding); num_experts >= 1; codebook_per_expert in {0, 1};
@@ -97,7 +102,7 @@ typedef struct vq_tensor {
   int32_t rows;             /* output features per expert                        */
   int32_t cols;             /* input features                                    */
   int32_t d;                /* subvector length: 2, 4 or 8                       */
-  int32_t log2_k;           /* bits per code B: 8 or 12 (K = 256 or 4096)        */
+  int32_t log2_k;           /* bits per code B: 4 .. 14 (K = 2^B)                */
   int32_t group;            /* weights per scale along a row: 64 or 128          */
   int32_t num_experts;      /* E; 1 for a dense tensor                           */
   int32_t codebook_per_expert; /* 0: one codebook for the tensor; 1: one per expert */
