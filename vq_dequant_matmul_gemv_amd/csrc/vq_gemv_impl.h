@@ -439,15 +439,21 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
     if (pass >= passes) { pass -= passes; ++g; }
   };
   // Slot k of the ring holds items k, k + P, k + 2P, ...: unrolled by P so
-  // every slot is a fixed set of registers.  The wave runs its item count
-  // rounded up to P; the extra items read zeros (their loads are out of
-  // range) and store nothing (their rows lie past the block).  With no
-  // branch and no global store in the loop, every wait for a slot's codes
-  // leaves the other slots' loads in flight.
-  for (int u0 = 0; u0 < n_items; u0 += P) {
+  // every slot is a fixed set of registers.  The wave leaves the loop after
+  // its last item (a wave-uniform exit; the loads already issued for slots
+  // past it are out of range and read zeros).  With no other branch and no
+  // global store in the loop, every wait for a slot's codes leaves the other
+  // slots' loads in flight.
+  if (n_items > 0) {
+    for (int u0 = 0;; u0 += P) {
 #pragma unroll
-    for (int k = 0; k < P; ++k) item(ring[k]);
+      for (int k = 0; k < P; ++k) {
+        item(ring[k]);
+        if (u0 + k + 1 >= n_items) goto items_done;
+      }
+    }
   }
+items_done:
 
   {  // y: each row's pass pieces added in pass order (deterministic)
     __syncthreads();
