@@ -160,8 +160,11 @@ typedef struct vq_io {
   const float *route_weights;  /* COMBINE: device [T][top_k] fp32 router weights  */
 } vq_io;
 
-/* uint32 words per row of packed codes: ceil(cols/d/32) * log2_k.  Returns -1
- * for a non-positive cols or an unsupported d / log2_k. */
+/* uint32 words per row of packed codes: ceil(cols/d/32) * log2_k -- each row
+ * holds its codes in row-local blocks of 32 codes packed LSB-first into
+ * log2_k words (model card "Qwen3.5-397B-A17B-VQ-2.4bpw", Methodology, on the
+ * packed index format; paper §2.3 Packing: codes stored at their true bit
+ * width).  Returns -1 for a non-positive cols or an unsupported d / log2_k. */
 int32_t vq_words_per_row(int32_t cols, int32_t d, int32_t log2_k);
 
 /*
@@ -245,7 +248,9 @@ size_t vq_moe_workspace_bytes(int32_t T, int32_t top_k, int32_t num_experts);
 
 /*
  * Routed-expert product, prefill-shaped: same arguments and result as
- * vq_moe_gemv.  On the device, the (token, slot) pairs are counted, scanned
+ * vq_moe_gemv (paper, Appendix A, on expert modules, and §3.4 on the prefill
+ * path; model card "aquaman164/Qwen3.6-35B-A3B-MLX-VQ-2.4bpw", Recipe, on
+ * top-8 routed experts).  On the device, the (token, slot) pairs are counted, scanned
  * and scattered by expert, a grouped MFMA GEMM runs over the flat list of
  * (expert, token tile) work items with gathered x rows, and results are
  * written straight to y[t][s].  No host synchronisation.
