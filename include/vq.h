@@ -249,8 +249,8 @@ size_t vq_moe_workspace_bytes(int32_t T, int32_t top_k, int32_t num_experts);
 /*
  * Routed-expert product, prefill-shaped: same arguments and result as
  * vq_moe_gemv (paper, Appendix A, on expert modules, and §3.4 on the prefill
- * path; model card "aquaman164/Qwen3.6-35B-A3B-MLX-VQ-2.4bpw", Recipe, on
- * top-8 routed experts).  On the device, the (token, slot) pairs are counted, scanned
+ * path; model card "aquaman164/Qwen3.6-35B-A3B-MLX-VQ-2.4bpw", Experimental
+ * MTP section, on its top-8 MoE).  On the device, the (token, slot) pairs are counted, scanned
  * and scattered by expert, a grouped MFMA GEMM runs over the flat list of
  * (expert, token tile) work items with gathered x rows, and results are
  * written straight to y[t][s].  No host synchronisation.
