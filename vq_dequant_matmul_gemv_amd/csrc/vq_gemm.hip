@@ -84,21 +84,51 @@ struct RouteArgs {
 // serialize at L2 (tens of microseconds per call), LDS atomics do not.
 constexpr int kRouteLdsExperts = 8192;
 
+// Pairs a thread of the routing block keeps in registers (id and rank within
+// its expert) between counting and scattering: up to 16 x 1024 pairs the ids
+// are read once and every pair's place comes from its counting atomic, with
+// no second pass of atomics; larger calls take the two-pass path.
+constexpr int kRouteRegPairs = 16;
+
 template <bool kLds>
 __device__ __forceinline__ void route_pairs(const RouteArgs& a, int32_t* counts, int32_t* fill, int32_t* part) {
   const int E = a.num_experts;
-  int32_t* offsets = a.ws + E;
   int32_t* tbase = a.ws + 3 * E;
   int32_t* n_tiles = tbase + E;
   int32_t* pairs = moe_ws_pairs(a.ws, E);
   int32_t* tiles = moe_ws_tiles(a.ws, E, a.npairs);
   const int tid = threadIdx.x, nt = blockDim.x;
+  // one pass (LDS counters, pairs held in registers) or two (counters and
+  // their second use in the workspace, or too many pairs)
+  const bool one_pass = kLds && a.npairs <= kRouteRegPairs * nt;
+  // expert offsets: in LDS (the fill counters are not needed) on the one-pass
+  // path, in the workspace otherwise
+  int32_t* offsets = one_pass ? fill : a.ws + E;
+  int32_t my_e[kRouteRegPairs], my_rank[kRouteRegPairs];
 
   for (int e = tid; e < E; e += nt) { counts[e] = 0; fill[e] = 0; }
   __syncthreads();
-  for (int p = tid; p < a.npairs; p += nt) {
-    const int e = a.ids[p];
-    if (e >= 0 && e < E) atomicAdd(&counts[e], 1);
+  if (one_pass) {
+    // every id load in flight at once (an index past the end reads pair 0,
+    // then is dropped), then the counting atomics
+#pragma unroll
+    for (int k = 0; k < kRouteRegPairs; ++k) {
+      const int p = tid + k * nt;
+      my_e[k] = a.ids[p < a.npairs ? p : 0];
+    }
+#pragma unroll
+    for (int k = 0; k < kRouteRegPairs; ++k) {
+      const int p = tid + k * nt;
+      const int e = my_e[k];
+      const bool ok = p < a.npairs && e >= 0 && e < E;
+      my_e[k] = ok ? e : -1;
+      my_rank[k] = ok ? atomicAdd(&counts[e], 1) : -1;
+    }
+  } else {
+    for (int p = tid; p < a.npairs; p += nt) {
+      const int e = a.ids[p];
+      if (e >= 0 && e < E) atomicAdd(&counts[e], 1);
+    }
   }
   __syncthreads();
   // exclusive scans of counts and of tiles-per-expert: each thread owns a
@@ -145,14 +175,28 @@ __device__ __forceinline__ void route_pairs(const RouteArgs& a, int32_t* counts,
     run_t += nt_e;
   }
   __syncthreads();
-  for (int p = tid; p < a.npairs; p += nt) {
-    const int e = a.ids[p];
-    if (e >= 0 && e < E) {
-      const int pos = offsets[e] + atomicAdd(&fill[e], 1);
-      pairs[pos] = p;
-    } else if (a.y) {
-      uint16_t* yr = static_cast<uint16_t*>(a.y) + (int64_t)p * a.y_row_halves;  // skipped slot: zero row
+  auto skipped = [&](int p) {  // skipped slot: zero its output row
+    if (a.y) {
+      uint16_t* yr = static_cast<uint16_t*>(a.y) + (int64_t)p * a.y_row_halves;
       for (int r = 0; r < a.y_row_halves; ++r) yr[r] = 0;
+    }
+  };
+  if (one_pass) {
+#pragma unroll
+    for (int k = 0; k < kRouteRegPairs; ++k) {
+      const int p = tid + k * nt;
+      if (my_e[k] >= 0) pairs[offsets[my_e[k]] + my_rank[k]] = p;
+      else if (p < a.npairs) skipped(p);
+    }
+  } else {
+    for (int p = tid; p < a.npairs; p += nt) {
+      const int e = a.ids[p];
+      if (e >= 0 && e < E) {
+        const int pos = offsets[e] + atomicAdd(&fill[e], 1);
+        pairs[pos] = p;
+      } else {
+        skipped(p);
+      }
     }
   }
 }
