@@ -343,6 +343,38 @@ def test_moe_gemm_more_experts_than_lds_counters():
     assert row_rel_err(y.reshape(-1, rows), ref.reshape(-1, rows)) <= TOL
 
 
+def test_moe_gemm_routing_beyond_one_pass():
+    """The routing block keeps up to 16 pairs per thread (16 x 1024) in
+    registers and places them in one pass; more pairs take the two-pass path
+    with the same result.  2600 tokens x top-8 = 20800 pairs, skipped and out
+    of range slots among them, and the same call at 2000 tokens (one pass):
+    both match the oracle on a sample of pairs, and the pairs both calls share
+    give the same rows bit for bit."""
+    from vq_dequant_matmul_gemv_amd import binding
+    E, rows, cols, top_k = 64, 64, 128, 8
+    spec, arrs, w = _case(2, 8, 64, rows, cols, ("moe-2pass",), experts=E)
+    ys = {}
+    for T in (2600, 2000):
+        ids = _moe_ids(T, top_k, E, ("moe-2pass",))
+        ids[5, 3] = -1
+        ids[7, 1] = E + 2
+        x = synth.activations((T, cols), "moe-2pass")
+        announce("moe-2pass", T, T * top_k)
+        y = binding.moe_gemm(w, to_dev(x), to_dev(ids)).cpu().numpy()
+        assert np.all(y[5, 3] == 0) and np.all(y[7, 1] == 0)
+        pick = np.random.default_rng(T).choice(T, size=64, replace=False)
+        ref = O.moe_ref(arrs["codes"], arrs["codebook"], arrs["scales"], x[pick], ids[pick], cols=cols, d=2,
+                        log2_k=8, group=64, x_per_slot=False)
+        assert row_rel_err(y[pick].reshape(-1, rows), ref.reshape(-1, rows)) <= TOL
+        ys[T] = (y, ids)
+    # the first 2000 tokens draw the same ids and x in both calls (seeded by key)
+    y_big, ids_big = ys[2600]
+    y_small, ids_small = ys[2000]
+    same = np.all(ids_big[:2000] == ids_small, axis=1)
+    assert same.sum() > 1000
+    assert np.array_equal(y_big[:2000][same], y_small[same])
+
+
 def test_moe_grouped_equals_per_slot_bit_identical_on_exact_inputs():
     """Grouping by expert does not change any row: on exact-arithmetic
     inputs grouped GEMM, per-slot GEMV and the oracle agree bit for bit."""
