@@ -181,11 +181,12 @@ vq_status vq_dequant(const vq_tensor *w, int32_t expert, uint16_t *w_out, void *
  *   x: device [T][cols] fp16 bits, 16-byte aligned;
  *   y: device [T][rows] fp32, 16-byte aligned.
  * T >= 0 (T == 0 enqueues nothing).  Any T is accepted.  The streaming
- * kernel reads every code once per token, the fast path for T = 1 (the fused
- * decode-and-matmul of paper §3.4); above a token count measured per shape
- * (1 for d = 2/4 matrices, 4 for d = 8, 6 for matrices of at most 16M
- * weights) vq_gemv runs the MFMA kernel of vq_gemm instead, with the same
- * result contract.
+ * kernel reads every code once per token, or once per two tokens when a
+ * row's x fits 16 KiB: the fast path for T = 1 and 2 (the fused
+ * decode-and-matmul of paper §3.4; two tokens: a two-token speculative
+ * verify step, 35B card, Experimental MTP); above a token count measured per shape (2 for d = 2/4
+ * matrices, 4 for d = 8, 6 for matrices of at most 16M weights) vq_gemv runs
+ * the MFMA kernel of vq_gemm instead, with the same result contract.
  */
 vq_status vq_gemv(const vq_tensor *w, const uint16_t *x, int32_t T, float *y, void *stream);
 

@@ -216,6 +216,36 @@ def test_gemv_partial_last_rounds():
             assert row_rel_err(y, ref) <= TOL, (rows, cols, T)
 
 
+@pytest.mark.parametrize("d,b,g", [(2, 8, 64), (4, 8, 64), (4, 12, 128), (8, 12, 128)])
+def test_gemv_two_token_slices(d, b, g):
+    """Two tokens per grid slice (rows whose x fits 16 KiB): each code and
+    codebook entry read once for both tokens.  Matrices above 16M weights
+    hand T = 2 to this path; odd token counts (a last slice of one token) go
+    through the same kernel on smaller matrices.  fp32, fp16 and bf16
+    outputs and the SwiGLU step."""
+    import torch
+    from vq_dequant_matmul_gemv_amd import binding
+    rows, cols = 3584, 5120            # 18.4M weights: T = 2 stays on the GEMV
+    spec, arrs, w = _case(d, b, g, rows, cols, ("two-tok", d, b, g))
+    x = synth.activations((2, cols), "two-tok", d, b, g)
+    ref = O.gemv_ref(arrs["codes"][0], arrs["codebook"], arrs["scales"][0], x, cols, d, b, g)
+    announce("gemv two-token", d, b, g)
+    y = binding.gemv(w, to_dev(x)).cpu().numpy()
+    assert row_rel_err(y, ref) <= TOL
+    y16 = binding.gemv(w, to_dev(x), y_dtype=torch.float16).float().cpu().numpy()
+    assert row_rel_err(y16, ref) <= TOL + 2.0 ** -11
+    h = binding.gemv(w, to_dev(x), y_dtype=torch.bfloat16, epilogue="swiglu").float().cpu().numpy()
+    assert row_rel_err(h, O.swiglu_ref(ref)) <= TOL + 2.0 ** -8
+    # odd token counts on a matrix that keeps up to 6 tokens on the GEMV
+    spec, arrs, w = _case(d, b, g, 301, 2048, ("two-tok-odd", d, b, g))
+    for T in (3, 5):
+        x = synth.activations((T, 2048), "two-tok-odd", d, b, g, T)
+        announce("gemv two-token odd", d, b, g, T)
+        y = binding.gemv(w, to_dev(x)).cpu().numpy()
+        ref = O.gemv_ref(arrs["codes"][0], arrs["codebook"], arrs["scales"][0], x, 2048, d, b, g)
+        assert row_rel_err(y, ref) <= TOL, T
+
+
 def test_zero_tokens_is_a_no_op():
     import torch
     from vq_dequant_matmul_gemv_amd import binding

@@ -220,15 +220,17 @@ vq_status vq_dequant(const vq_tensor* w, int32_t expert, uint16_t* w_out, void* 
 }
 
 // Largest token count for which the streaming GEMV beats the MFMA GEMM,
-// measured on MI355X at the benchmark shapes: the GEMV re-reads every code
-// per token (one grid slice per token), the GEMM once per 32- or 128-token
-// tile, split along K to fill the GPU.  Small matrices stay in L2 between
-// token slices, and d = 8 codes are few per weight, so the GEMV keeps a few
-// tokens there; otherwise it wins at T = 1 only.
+// measured on MI355X at the benchmark shapes: the GEMV reads every code once
+// per grid slice (two tokens per slice where a row's x fits 16 KiB, else one),
+// the GEMM once per 32- or 128-token tile, split along K to fill the GPU.
+// Small matrices stay in L2 between token slices, and d = 8 codes are few per
+// weight, so the GEMV keeps a few tokens there; otherwise it wins up to T = 2
+// (17408x5120 and 5120x17408, d = 2 and 4: 15.9-18.6 us against 17.3-21.7 us
+// for the GEMM) and loses from T = 3 on.
 static int gemv_token_limit(const vqmi::TensorView& v) {
   if ((int64_t)v.rows * v.cols <= (int64_t)16 << 20) return 6;
   if (v.d == 8) return 4;
-  return 1;
+  return 2;
 }
 
 static vq_status dense_call(const vq_tensor* w, const vq_io* io, const void* x, int32_t T, void* y,

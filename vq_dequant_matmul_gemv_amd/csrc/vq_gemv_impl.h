@@ -28,9 +28,12 @@
 //  * x sits in VGPRs for a whole pass (x-stationary); the inner loop per code
 //    is one v_perm_b32 (LDS offset), one LDS gather and d/2 v_dot2_f32_f16;
 //    the group scale multiplies each group sum once.
-//  * Several tokens run as one grid slice each (blockIdx.y), re-reading the
-//    codes per token: above a few tokens the MFMA GEMM is the faster kernel
-//    and the C ABI's vq_gemv hands such calls to it.
+//  * Several tokens run as grid slices (blockIdx.y) of TT tokens each: TT = 2
+//    (small-batch decode, e.g. a two-token speculative verify) holds both
+//    tokens' x in VGPRs and reads each code and codebook entry once for both;
+//    otherwise one token per slice, re-reading the codes per token.  Above a
+//    few tokens the MFMA GEMM is the faster kernel and the C ABI's vq_gemv
+//    hands such calls to it.
 //  * Each wave keeps P row groups' loads in flight (P items of C chunks per
 //    lane, about six chunks in all): wide items (d = 2, five chunks per lane)
 //    keep one, since a deeper ring only holds the wave at the issue of loads
@@ -83,8 +86,11 @@ constexpr int kGemvXMaxBytes = 40 * 1024;      // largest x slice in LDS
 constexpr int kGemvScaleBytes = 24 * 1024;     // the block's scale rows (136 rows of 80 groups fit)
 constexpr int kGemvPieces = 4096;              // per-(row, pass) partial sums
 
-// Chunks per lane a pass can hold in VGPRs: x costs 8*d VGPRs per chunk.
-__host__ __device__ constexpr int gemv_max_c(int D) { return D == 2 ? 5 : (D == 4 ? 3 : 1); }
+// Chunks per lane a pass can hold in VGPRs: x costs 8*d VGPRs per chunk and
+// token of the slice.
+__host__ __device__ constexpr int gemv_max_c(int D, int TT = 1) {
+  return TT == 1 ? (D == 2 ? 5 : (D == 4 ? 3 : 1)) : (D == 2 ? 3 : (D == 4 ? 2 : 1));
+}
 
 // Items a wave keeps in flight: about six 16-code chunks per lane in all, so
 // narrow items (few chunks per lane) still put enough bytes on the wire per
@@ -102,9 +108,10 @@ __device__ __forceinline__ float lane_group_sum(float v, int lg) {
   return v;
 }
 
-// XS: the x slice takes XS * 8 KiB of LDS (2 or 5); fewer staging loads for
-// short rows.
-template <int D, int B, int G, int C, int XS, bool MOE>
+// XS: the x slice takes XS * 8 KiB of LDS per token (2 or 5); fewer staging
+// loads for short rows.  TT: tokens per grid slice (1, or 2 for dense calls
+// with XS = 2).
+template <int D, int B, int G, int C, int XS, bool MOE, int TT>
 //
 // The arguments a block needs before its first loads come first, as scalars:
 // with kernel-argument preloading (the build passes
@@ -125,7 +132,8 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
   constexpr int HX = 8 * D;                              // half2 of x per chunk
   constexpr int NW = kGemvWaves;
   constexpr int NT = kGemvThreads;
-  static_assert(C <= gemv_max_c(D), "tile does not fit the VGPR budget");
+  static_assert(C <= gemv_max_c(D, TT), "tile does not fit the VGPR budget");
+  static_assert(TT == 1 || (!MOE && XS == 2), "two-token slices: dense calls with short x slices");
 
   __shared__ __align__(16) uint8_t cb_lds[LY::kBytes];
   constexpr int XBYTES = XS * 8192;                                 // x bytes staged at most
@@ -134,9 +142,10 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
   // 32 D-byte stride would put 8 to 16 of them on the same banks.
   constexpr int XCB = 32 * D;
   constexpr int XSTRIDE = XCB + 16;
-  __shared__ __align__(16) uint8_t x_lds[XBYTES / XCB * XSTRIDE];   // [nq][XSTRIDE]
+  constexpr int XTOK = XBYTES / XCB * XSTRIDE;                      // LDS bytes of one token's x
+  __shared__ __align__(16) uint8_t x_lds[TT * XTOK];                // [TT][nq][XSTRIDE]
   __shared__ __align__(16) uint8_t s_lds[kGemvScaleBytes];          // the block's scale rows
-  __shared__ float pieces[kGemvPieces];                             // [rows][passes]
+  __shared__ float pieces[kGemvPieces];                             // [TT][rows][passes]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -184,20 +193,26 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
     cb += (int64_t)e * a.cb_estride;
     xb = xs + (int64_t)(a.x_per_slot ? pair : pair / a.top_k) * cols;
   } else {
-    xb = xs + (int64_t)blockIdx.y * cols;  // one token per grid slice
-    yrow = a.tok0 + blockIdx.y;
+    xb = xs + (int64_t)blockIdx.y * TT * cols;  // TT tokens per grid slice
+    yrow = a.tok0 + (int64_t)blockIdx.y * TT;
   }
+  // tokens of this slice (an odd token count leaves the last slice one short)
+  const int ntok = MOE ? 1 : min(TT, a.T - (int)yrow);
 
   // ---- small loads first: x slice, codebook entries, the block's scales ----
   const int xcols = nq * 16 * D;                        // columns of the slice
   const uint32_t xbytes = (uint32_t)xcols * 2u;
   constexpr int XL = (XBYTES + NT * 16 - 1) / (NT * 16);
-  u32x4 xg[XL];
-  const rsrc_t rx = make_rsrc(xb, (uint64_t)cols * 2);
+  u32x4 xg[TT][XL];
 #pragma unroll
-  for (int q = 0; q < XL; ++q) {
-    const uint32_t o = (uint32_t)(tid + q * NT) * 16u;  // byte in the x slice
-    xg[q] = buf_load_b128(rx, o < xbytes ? (uint32_t)q0 * 32u * D + o : kOutOfRange);
+  for (int t = 0; t < TT; ++t) {
+    // a token past the slice's count gets an empty buffer: its x reads zeros
+    const rsrc_t rx = make_rsrc(xb + (int64_t)t * cols, t < ntok ? (uint64_t)cols * 2 : 0);
+#pragma unroll
+    for (int q = 0; q < XL; ++q) {
+      const uint32_t o = (uint32_t)(tid + q * NT) * 16u;  // byte in the x slice
+      xg[t][q] = buf_load_b128(rx, o < xbytes ? (uint32_t)q0 * 32u * D + o : kOutOfRange);
+    }
   }
   // codebook (replicated layout): lane l < 32 of wave w holds entry 32 w + l
   u32x4 ce = u32x4{0u, 0u, 0u, 0u};
@@ -329,11 +344,14 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
   }
   const bool x_bf16 = a.x_bf16 != 0;
 #pragma unroll
-  for (int q = 0; q < XL; ++q) {
-    const uint32_t o = (uint32_t)(tid + q * NT) * 16u;
-    if (o < (uint32_t)XBYTES)
-      *reinterpret_cast<u32x4*>(x_lds + o + o / XCB * 16u) = x_bf16 ? bf16x8_to_f16x8(xg[q]) : xg[q];
-  }
+  for (int t = 0; t < TT; ++t)
+#pragma unroll
+    for (int q = 0; q < XL; ++q) {
+      const uint32_t o = (uint32_t)(tid + q * NT) * 16u;
+      if (o < (uint32_t)XBYTES)
+        *reinterpret_cast<u32x4*>(x_lds + t * XTOK + o + o / XCB * 16u) =
+            x_bf16 ? bf16x8_to_f16x8(xg[t][q]) : xg[t][q];
+    }
 #pragma unroll
   for (int q = 0; q < SL; ++q) {
     const uint32_t o = (uint32_t)(tid + q * NT) * 16u;
@@ -347,7 +365,7 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
   const uint8_t* cbp;
   if constexpr (LY::kGlobal) cbp = reinterpret_cast<const uint8_t*>(cb);
   else cbp = cb_lds;
-  half2_t xv[C][HX];
+  half2_t xv[TT][C][HX];
   uint32_t lane_sq[C], lane_ok[C];  // per pass: scale byte offset in the row, chunk-valid mask
   uint32_t lane_csh[C];             // per pass: bit offset of each chunk in its first word
   int cur_pass = -1;
@@ -365,21 +383,25 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
         lane_ok[j] = ok ? 0xffffffffu : 0u;
         lane_csh[j] = chunk_shift<B>((uint32_t)(q0 + q));
 #pragma unroll
-        for (int k = 0; k < HX / 4; ++k) {
-          u32x4 v = u32x4{0u, 0u, 0u, 0u};
-          if (ok) v = *reinterpret_cast<const u32x4*>(x_lds + (uint32_t)q * XSTRIDE + 16u * k);
-          xv[j][4 * k + 0] = as_half2(v.x);
-          xv[j][4 * k + 1] = as_half2(v.y);
-          xv[j][4 * k + 2] = as_half2(v.z);
-          xv[j][4 * k + 3] = as_half2(v.w);
-        }
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+          for (int k = 0; k < HX / 4; ++k) {
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (ok) v = *reinterpret_cast<const u32x4*>(x_lds + t * XTOK + (uint32_t)q * XSTRIDE + 16u * k);
+            xv[t][j][4 * k + 0] = as_half2(v.x);
+            xv[t][j][4 * k + 1] = as_half2(v.y);
+            xv[t][j][4 * k + 2] = as_half2(v.z);
+            xv[t][j][4 * k + 3] = as_half2(v.w);
+          }
       }
     }
 
     const int rb = g * R + rsub;                        // row within the block
     const uint32_t srow = s_skew + (uint32_t)rb * (uint32_t)spr * 2u;  // the row's scales in s_lds
     const uint32_t rowok = rb < brows ? 0xffffffffu : 0u;
-    float acc = 0.f;
+    float acc[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) acc[t] = 0.f;
     // The gathers of step t + 1 are issued before the dot products of step
     // t; a step is SB codes of one chunk (16 for d = 2, 8 for d = 4, 4 for
     // d = 8), so the gathered entries in flight take 2 * SB * d / 2 = 32 VGPRs
@@ -409,7 +431,9 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
       }
     };
     issue(0, e[0]);
-    float gs[2] = {0.f, 0.f};  // two chains for ILP, restarted per scale group
+    float gs[TT][2];  // two chains per token for ILP, restarted per scale group
+#pragma unroll
+    for (int t = 0; t < TT; ++t) gs[t][0] = gs[t][1] = 0.f;
 #pragma unroll
     for (int t = 0; t < C * S; ++t) {
       if (t + 1 < C * S) issue(t + 1, e[(t + 1) & 1]);
@@ -419,20 +443,29 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
         const int i = b * SB + ii;
 #pragma unroll
         for (int k = 0; k < D / 2; ++k)
-          gs[(i * (D / 2) + k) & 1] = dot2(e[t & 1][ii].v[k], xv[j][i * (D / 2) + k], gs[(i * (D / 2) + k) & 1]);
+#pragma unroll
+          for (int u = 0; u < TT; ++u)
+            gs[u][(i * (D / 2) + k) & 1] =
+                dot2(e[t & 1][ii].v[k], xv[u][j][i * (D / 2) + k], gs[u][(i * (D / 2) + k) & 1]);
       }
       if (((b + 1) * SB) % CPS == 0) {  // the step ends scale group s2 of chunk j
         const int s2 = (b + 1) * SB / CPS - 1;
         const uint32_t keep = lane_ok[j] & rowok;
         const uint16_t sbits = *reinterpret_cast<const uint16_t*>(s_lds + ((srow + lane_sq[j] + 2u * s2) & keep));
-        const float scale = half_bits_to_float(sbits);
-        const float gsum = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, gs[0] + gs[1]) & keep);
-        acc = __builtin_fmaf(gsum, __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, scale) & keep), acc);
-        gs[0] = gs[1] = 0.f;
+        const float scale = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, half_bits_to_float(sbits)) & keep);
+#pragma unroll
+        for (int u = 0; u < TT; ++u) {
+          const float gsum = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, gs[u][0] + gs[u][1]) & keep);
+          acc[u] = __builtin_fmaf(gsum, scale, acc[u]);
+          gs[u][0] = gs[u][1] = 0.f;
+        }
       }
     }
-    const float v = lane_group_sum(acc, lg);
-    if (li == L - 1 && rb < brows) pieces[rb * passes + pass] = v;
+#pragma unroll
+    for (int u = 0; u < TT; ++u) {
+      const float v = lane_group_sum(acc[u], lg);
+      if (li == L - 1 && rb < brows) pieces[(u * brows + rb) * passes + pass] = v;
+    }
     load_end();
     g += step_g;
     pass += step_p;
@@ -457,26 +490,30 @@ items_done:
 
   {  // y: each row's pass pieces added in pass order (deterministic)
     __syncthreads();
-    auto row_sum = [&](int r) {
-      float v = 0.f;
-      for (int c = 0; c < passes; ++c) v += pieces[r * passes + c];
-      return v;
-    };
-    const int64_t ybase = yrow * yrows;
-    if (a.epi == kEpiSwiglu) {  // rows 2i (gate) and 2i + 1 (up) -> y[i]
-      for (int i = tid; 2 * i < brows; i += NT)
-        store_out(a.y, ybase + (brow0 >> 1) + i, swiglu(row_sum(2 * i), row_sum(2 * i + 1)), a.y_kind);
-    } else if (a.epi == kEpiCombine) {  // y[token] += router weight * row
-      if constexpr (MOE) {
-        const float wgt = a.route_w[blockIdx.y];
-        float* yc = reinterpret_cast<float*>(a.y) + ybase + brow0;
-        for (int r = tid; r < brows; r += NT) atomicAdd(yc + r, wgt * row_sum(r));
+#pragma unroll
+    for (int u = 0; u < TT; ++u) {
+      if (u >= ntok) break;
+      auto row_sum = [&](int r) {
+        float v = 0.f;
+        for (int c = 0; c < passes; ++c) v += pieces[(u * brows + r) * passes + c];
+        return v;
+      };
+      const int64_t ybase = (yrow + u) * yrows;
+      if (a.epi == kEpiSwiglu) {  // rows 2i (gate) and 2i + 1 (up) -> y[i]
+        for (int i = tid; 2 * i < brows; i += NT)
+          store_out(a.y, ybase + (brow0 >> 1) + i, swiglu(row_sum(2 * i), row_sum(2 * i + 1)), a.y_kind);
+      } else if (a.epi == kEpiCombine) {  // y[token] += router weight * row
+        if constexpr (MOE) {
+          const float wgt = a.route_w[blockIdx.y];
+          float* yc = reinterpret_cast<float*>(a.y) + ybase + brow0;
+          for (int r = tid; r < brows; r += NT) atomicAdd(yc + r, wgt * row_sum(r));
+        }
+      } else if (a.accumulate) {  // a column slice after the first (fp32 y)
+        float* yf = reinterpret_cast<float*>(a.y) + ybase + brow0;
+        for (int r = tid; r < brows; r += NT) yf[r] += row_sum(r);
+      } else {
+        for (int r = tid; r < brows; r += NT) store_out(a.y, ybase + brow0 + r, row_sum(r), a.y_kind);
       }
-    } else if (a.accumulate) {  // a column slice after the first (fp32 y)
-      float* yf = reinterpret_cast<float*>(a.y) + ybase + brow0;
-      for (int r = tid; r < brows; r += NT) yf[r] += row_sum(r);
-    } else {
-      for (int r = tid; r < brows; r += NT) store_out(a.y, ybase + brow0 + r, row_sum(r), a.y_kind);
     }
   }
 }
@@ -626,7 +663,7 @@ LaneTiling plan_tiling(int nq, int max_c, int waves, bool cu_bound) {
   return best;
 }
 
-template <int D, int B, int G, int C, int XS, bool MOE>
+template <int D, int B, int G, int C, int XS, bool MOE, int TT>
 hipError_t gemv_launch_c(const GemvArgs& a, dim3 grid, hipStream_t s) {
   const uint16_t* xs = MOE ? a.x : a.x + (int64_t)a.tok0 * a.cols;  // fp16 or bf16: 2 bytes a value
   const int pw = (a.nq + a.passes - 1) / a.passes;
@@ -634,20 +671,20 @@ hipError_t gemv_launch_c(const GemvArgs& a, dim3 grid, hipStream_t s) {
     return hipErrorInvalidValue;
   const uint32_t shape = (uint32_t)a.nq | ((uint32_t)a.lanes_log2 << 12) | ((uint32_t)a.passes << 15) |
                          ((uint32_t)pw << 23);
-  hipLaunchKernelGGL((vq_gemv_kernel<D, B, G, C, XS, MOE>), grid, dim3(kGemvThreads), 0, s, a.codes, a.codebook,
+  hipLaunchKernelGGL((vq_gemv_kernel<D, B, G, C, XS, MOE, TT>), grid, dim3(kGemvThreads), 0, s, a.codes, a.codebook,
                      a.scales, xs, a.rows, a.rows_base, a.rows_extra, a.q0, a.spr, shape, a);
   return hipGetLastError();
 }
 
-template <int D, int B, int G, int XS, bool MOE>
+template <int D, int B, int G, int XS, bool MOE, int TT>
 hipError_t gemv_launch(const GemvArgs& a, int C, dim3 grid, hipStream_t s) {
-  constexpr int MC = gemv_max_c(D);
+  constexpr int MC = gemv_max_c(D, TT);
   switch (C) {
-    case 1: return gemv_launch_c<D, B, G, 1, XS, MOE>(a, grid, s);
-    case 2: if constexpr (MC >= 2) return gemv_launch_c<D, B, G, 2, XS, MOE>(a, grid, s); break;
-    case 3: if constexpr (MC >= 3) return gemv_launch_c<D, B, G, 3, XS, MOE>(a, grid, s); break;
-    case 4: if constexpr (MC >= 4) return gemv_launch_c<D, B, G, 4, XS, MOE>(a, grid, s); break;
-    case 5: if constexpr (MC >= 5) return gemv_launch_c<D, B, G, 5, XS, MOE>(a, grid, s); break;
+    case 1: return gemv_launch_c<D, B, G, 1, XS, MOE, TT>(a, grid, s);
+    case 2: if constexpr (MC >= 2) return gemv_launch_c<D, B, G, 2, XS, MOE, TT>(a, grid, s); break;
+    case 3: if constexpr (MC >= 3) return gemv_launch_c<D, B, G, 3, XS, MOE, TT>(a, grid, s); break;
+    case 4: if constexpr (MC >= 4) return gemv_launch_c<D, B, G, 4, XS, MOE, TT>(a, grid, s); break;
+    case 5: if constexpr (MC >= 5) return gemv_launch_c<D, B, G, 5, XS, MOE, TT>(a, grid, s); break;
     default: break;
   }
   return hipErrorInvalidValue;
@@ -656,23 +693,28 @@ hipError_t gemv_launch(const GemvArgs& a, int C, dim3 grid, hipStream_t s) {
 // Column slices that fit the x slice in LDS run one after another, adding
 // into y; rows are split over about one block per CU (per token slice), or
 // more where a block's scales or row pieces would not fit in LDS.  Dense
-// calls run one grid slice per token (blockIdx.y), routed calls one per
+// calls run one grid slice (blockIdx.y) per token, or per two tokens when
+// there are several and a row's x fits one 16 KiB slice; routed calls one per
 // (token, slot) pair.
 template <int D, int B, int G, bool MOE>
 hipError_t gemv_run(GemvArgs a, int P, int ycount, hipStream_t s) {
-  const int slice_max = kGemvXMaxBytes / (32 * D);
+  const int slice_two = 2 * 8192 / (32 * D);            // chunks of a 16 KiB x slice
+  const bool two = !MOE && ycount >= 2 && P <= slice_two;
+  const int TT = two ? 2 : 1;
+  const int slice_max = two ? slice_two : kGemvXMaxBytes / (32 * D);
   const int n_slices = (P + slice_max - 1) / slice_max;
   const int per_slice = (P + n_slices - 1) / n_slices;
-  const int blocks_fill = std::max(1, num_cus() / std::max(1, ycount));
+  const int ny = (ycount + TT - 1) / TT;                 // grid slices along y
+  const int blocks_fill = std::max(1, num_cus() / std::max(1, ny));
   for (int sl = 0; sl < n_slices; ++sl) {
     a.q0 = sl * per_slice;
     a.nq = std::min(per_slice, P - a.q0);
     a.accumulate = sl > 0;
-    const LaneTiling t = plan_tiling(a.nq, gemv_max_c(D), kGemvWaves, D >= 4);
+    const LaneTiling t = plan_tiling(a.nq, gemv_max_c(D, TT), kGemvWaves, D >= 4);
     a.lanes_log2 = t.lg;
     a.passes = t.passes;
     const int64_t by_scales = std::max<int64_t>(1, (kGemvScaleBytes - 16) / (2 * (int64_t)a.spr));
-    const int64_t by_pieces = std::max<int64_t>(1, kGemvPieces / (int64_t)t.passes);
+    const int64_t by_pieces = std::max<int64_t>(1, kGemvPieces / ((int64_t)t.passes * TT));
     // under SwiGLU a block owns whole (gate, up) row pairs
     const int unit = a.epi == kEpiSwiglu ? 2 : 1;
     const int64_t rows_max = std::max<int64_t>(unit, std::min(by_scales, by_pieces) / unit * unit);
@@ -681,12 +723,18 @@ hipError_t gemv_run(GemvArgs a, int P, int ycount, hipStream_t s) {
     a.rows_base = (int)(units / blocks) * unit;
     a.rows_extra = (int)(units - units / blocks * blocks) | (unit == 2 ? 1 << 30 : 0);
     const int XS = (int64_t)a.nq * 32 * D <= 2 * 8192 ? 2 : 5;
-    // dense: at most 65535 token slices per launch
-    for (int y0 = 0; y0 < ycount; y0 += 65535) {
-      const int yc = std::min(65535, ycount - y0);
-      if (!MOE) a.tok0 = y0;
-      hipError_t e = XS == 2 ? gemv_launch<D, B, G, 2, MOE>(a, t.C, dim3((unsigned)blocks, (unsigned)yc), s)
-                             : gemv_launch<D, B, G, 5, MOE>(a, t.C, dim3((unsigned)blocks, (unsigned)yc), s);
+    // at most 65535 grid slices per launch
+    for (int y0 = 0; y0 < ny; y0 += 65535) {
+      const int yc = std::min(65535, ny - y0);
+      if (!MOE) a.tok0 = y0 * TT;
+      const dim3 grid((unsigned)blocks, (unsigned)yc);
+      hipError_t e;
+      if constexpr (!MOE) {
+        if (two) e = gemv_launch<D, B, G, 2, MOE, 2>(a, t.C, grid, s);
+        else e = XS == 2 ? gemv_launch<D, B, G, 2, MOE, 1>(a, t.C, grid, s) : gemv_launch<D, B, G, 5, MOE, 1>(a, t.C, grid, s);
+      } else {
+        e = XS == 2 ? gemv_launch<D, B, G, 2, MOE, 1>(a, t.C, grid, s) : gemv_launch<D, B, G, 5, MOE, 1>(a, t.C, grid, s);
+      }
       if (e != hipSuccess) return e;
       if (MOE) break;
     }
