@@ -87,9 +87,10 @@ constexpr int kGemvScaleBytes = 24 * 1024;     // the block's scale rows (136 ro
 constexpr int kGemvPieces = 4096;              // per-(row, pass) partial sums
 
 // Chunks per lane a pass can hold in VGPRs: x costs 8*d VGPRs per chunk and
-// token of the slice.
-__host__ __device__ constexpr int gemv_max_c(int D, int TT = 1) {
-  return TT == 1 ? (D == 2 ? 5 : (D == 4 ? 3 : 1)) : (D == 2 ? 3 : (D == 4 ? 2 : 1));
+// token of the slice (d = 4 two-token slices of 13- and 14-bit codes hold
+// one: with two, their wider code chunks spill registers).
+__host__ __device__ constexpr int gemv_max_c(int D, int B, int TT) {
+  return TT == 1 ? (D == 2 ? 5 : (D == 4 ? 3 : 1)) : (D == 2 ? 3 : (D == 4 ? (B > 12 ? 1 : 2) : 1));
 }
 
 // Items a wave keeps in flight: about six 16-code chunks per lane in all, so
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
   constexpr int HX = 8 * D;                              // half2 of x per chunk
   constexpr int NW = kGemvWaves;
   constexpr int NT = kGemvThreads;
-  static_assert(C <= gemv_max_c(D, TT), "tile does not fit the VGPR budget");
+  static_assert(C <= gemv_max_c(D, B, TT), "tile does not fit the VGPR budget");
   static_assert(TT == 1 || (!MOE && XS == 2), "two-token slices: dense calls with short x slices");
 
   __shared__ __align__(16) uint8_t cb_lds[LY::kBytes];
@@ -678,7 +679,7 @@ hipError_t gemv_launch_c(const GemvArgs& a, dim3 grid, hipStream_t s) {
 
 template <int D, int B, int G, int XS, bool MOE, int TT>
 hipError_t gemv_launch(const GemvArgs& a, int C, dim3 grid, hipStream_t s) {
-  constexpr int MC = gemv_max_c(D, TT);
+  constexpr int MC = gemv_max_c(D, B, TT);
   switch (C) {
     case 1: return gemv_launch_c<D, B, G, 1, XS, MOE, TT>(a, grid, s);
     case 2: if constexpr (MC >= 2) return gemv_launch_c<D, B, G, 2, XS, MOE, TT>(a, grid, s); break;
@@ -710,7 +711,7 @@ hipError_t gemv_run(GemvArgs a, int P, int ycount, hipStream_t s) {
     a.q0 = sl * per_slice;
     a.nq = std::min(per_slice, P - a.q0);
     a.accumulate = sl > 0;
-    const LaneTiling t = plan_tiling(a.nq, gemv_max_c(D, TT), kGemvWaves, D >= 4);
+    const LaneTiling t = plan_tiling(a.nq, gemv_max_c(D, B, TT), kGemvWaves, D >= 4);
     a.lanes_log2 = t.lg;
     a.passes = t.passes;
     const int64_t by_scales = std::max<int64_t>(1, (kGemvScaleBytes - 16) / (2 * (int64_t)a.spr));
