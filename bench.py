@@ -423,7 +423,8 @@ def configs_report(only=""):
         dense("gemv_1024", "w", W["gemv_1024"]["tensors"]["w"], [1], [], ("gemv_1024", "w"))
     wl = "dense_mlp_5120x17408_d2k256"
     for n in ("gate", "up", "down") if keep(wl) else ():
-        dense(wl, n, W[wl]["tensors"][n], [1], [2048], (wl, n))
+        # T = 2: a two-token verify step; both kernels timed for the crossover
+        dense(wl, n, W[wl]["tensors"][n], [1, 2], [2, 2048], (wl, n))
     if keep(wl):
         stacked_pair(wl, "gate+up (two-expert stack, ids {0,1})", W[wl]["tensors"]["gate"],
                      ((wl, "gate"), (wl, "up")))
@@ -440,7 +441,7 @@ def configs_report(only=""):
                    (wl, tier, idx))
     wl = "sweep_17408x5120_d4k256"
     for n in ("A", "B") if keep(wl) else ():
-        Ts = W[wl]["tokens"]
+        Ts = sorted(set(W[wl]["tokens"]) | {2})
         dense(wl, n, W[wl]["tensors"][n], Ts, Ts, (wl, n))
     if keep(wl):
         dequant_row(wl, "A", W[wl]["tensors"]["A"], (wl, "A"))

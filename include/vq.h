@@ -251,18 +251,24 @@ size_t vq_moe_workspace_bytes(int32_t T, int32_t top_k, int32_t num_experts);
  * Routed-expert product, prefill-shaped: same arguments and result as
  * vq_moe_gemv (paper, Appendix A, on expert modules, and §3.4 on the prefill
  * path; model card "aquaman164/Qwen3.6-35B-A3B-MLX-VQ-2.4bpw", Experimental
- * MTP section, on its top-8 MoE).  On the device, the (token, slot) pairs are counted, scanned
- * and scattered by expert, a grouped MFMA GEMM runs over the flat list of
- * (expert, token tile) work items with gathered x rows, and results are
- * written straight to y[t][s].  No host synchronisation.
+ * MTP section, on its top-8 MoE).  On the device, the (token, slot) pairs are
+ * counted, scanned and scattered by expert, a grouped MFMA GEMM runs over the
+ * flat list of (expert, token tile) work items with gathered x rows, and
+ * results are written straight to y[t][s].  No host synchronisation.  Token
+ * tiles hold 32 pairs, or 128 for an expert's whole 128s (and a remainder
+ * above 64) when the call is large enough to fill the GPU twice over; the two
+ * kinds group the columns of the k-steps differently, so a row's fp32 value
+ * can differ in the last bits between calls that tile its expert differently
+ * (within the stated tolerance; each call is deterministic).
  *   workspace: device, >= vq_moe_workspace_bytes(T, top_k, num_experts)
  *   bytes, 16-byte aligned, owned by the caller; contents on entry are
  *   ignored and on return are undefined.  Concurrent calls need separate
  *   workspaces.
  * The stacked gate/up layouts described for vq_moe_gemv apply here too
  * (workspace sized for the doubled top_k and expert count): each output row
- * depends only on its expert and x row, so the results are bit for bit those
- * of separate calls.
+ * depends only on its expert, its x row and its tile kind, so the results are
+ * bit for bit those of separate calls, unless only the stacked call (twice
+ * the pairs) is large enough for 128-pair tiles.
  */
 vq_status vq_moe_gemm(const vq_tensor *w, const uint16_t *x, int32_t x_per_slot,
                       const int32_t *expert_ids, int32_t T, int32_t top_k, float *y,

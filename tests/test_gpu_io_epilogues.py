@@ -13,7 +13,7 @@ import pytest
 
 from oracle import vq_oracle as O
 from vq_dequant_matmul_gemv_amd import synth
-from tests.helpers import TOL, announce, row_rel_err, to_dev, upload
+from tests.helpers import TOL, announce, hot_expert_ids, row_rel_err, to_dev, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -190,6 +190,39 @@ def test_combine_routed(fn, d, b, g, x_per_slot):
         getattr(binding, fn)(w, to_dev(x), to_dev(ids), x_per_slot=x_per_slot, y=y, epilogue="combine",
                              route_weights=to_dev(rw))
         assert row_rel_err(y.cpu().numpy(), ref) <= TOL, T
+
+
+def test_routed_gemm_output_steps_over_mixed_tile_kinds():
+    """The routed GEMM's output steps where the routing lists 128-token tiles
+    for hot experts, 32-token tiles and row halves (1024 tokens x top-8,
+    992-row experts): SwiGLU of interleaved gate/up rows into bf16 h, then
+    the combine of per-slot h through a down tensor of 992 rows."""
+    import torch
+    from vq_dequant_matmul_gemv_amd import binding
+    E, top_k, T, I, cols = 32, 8, 1024, 496, 256
+    spec, arrs, w = _gate_up(I, cols, 4, 8, 64, ("mix-swiglu",), experts=E)
+    ids = hot_expert_ids(T, top_k, E, ("mix-epi",))
+    x = synth.activations((T, cols), "mix-swiglu")
+    announce("moe_gemm mixed tiles swiglu")
+    h = binding.moe_gemm(w, to_dev(x), to_dev(ids), y_dtype=torch.bfloat16, epilogue="swiglu")
+    yref = O.moe_ref(arrs["codes"], arrs["codebook"], arrs["scales"], x, ids, cols=cols, d=4, log2_k=8, group=64,
+                     x_per_slot=False)
+    hh = _host(h)
+    assert np.all(hh[900, 7] == 0) and np.all(hh[901, 6] == 0)
+    assert row_rel_err(hh.reshape(-1, I), O.swiglu_ref(yref).reshape(-1, I)) <= OUT_TOL["bf16"]
+    # down: 992 rows over the bf16 h of each slot, router-weighted combine
+    dspec = synth.Spec(rows=992, cols=I + 16, d=4, log2_k=8, group=64, experts=E)
+    darrs = synth.tensor(dspec, "mix-down")
+    dw = upload(darrs, dspec)
+    hx = np.zeros((T, top_k, I + 16), dtype=np.float16)
+    hx[:, :, :I] = np.asarray(hh, dtype=np.float16)
+    rw = synth.router_weights(T, top_k, "mix-down")
+    y = torch.full((T, 992), float("nan"), device="cuda")
+    announce("moe_gemm mixed tiles combine")
+    binding.moe_gemm(dw, to_dev(hx), to_dev(ids), x_per_slot=True, y=y, epilogue="combine", route_weights=to_dev(rw))
+    dref = O.moe_ref(darrs["codes"], darrs["codebook"], darrs["scales"], hx, ids, cols=I + 16, d=4, log2_k=8,
+                     group=64, x_per_slot=True)
+    assert row_rel_err(y.cpu().numpy(), O.moe_combine_ref(dref, rw, ids, E)) <= TOL
 
 
 def test_bf16_profile_routed_gate_up_swiglu_then_down_combine():

@@ -9,7 +9,7 @@ import pytest
 
 from oracle import vq_oracle as O
 from vq_dequant_matmul_gemv_amd import synth
-from tests.helpers import TOL, announce, row_rel_err, to_dev, upload
+from tests.helpers import hot_expert_ids, TOL, announce, row_rel_err, to_dev, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -382,13 +382,16 @@ def test_moe_gemm_routing_beyond_one_pass():
     give the same rows bit for bit."""
     from vq_dequant_matmul_gemv_amd import binding
     E, rows, cols, top_k = 64, 64, 128, 8
-    spec, arrs, w = _case(2, 8, 64, rows, cols, ("moe-2pass",), experts=E)
+    # exact-arithmetic inputs: a row's value does not depend on which tile
+    # kind (32 or 128 tokens, whose k-steps group the columns differently)
+    # the routing put its pair in, so shared pairs must agree bit for bit
+    spec, arrs, w = _case(2, 8, 64, rows, cols, ("moe-2pass",), exact=True, experts=E)
     ys = {}
     for T in (2600, 2000):
         ids = _moe_ids(T, top_k, E, ("moe-2pass",))
         ids[5, 3] = -1
         ids[7, 1] = E + 2
-        x = synth.activations((T, cols), "moe-2pass")
+        x = synth.activations((T, cols), "moe-2pass", exact=True)
         announce("moe-2pass", T, T * top_k)
         y = binding.moe_gemm(w, to_dev(x), to_dev(ids)).cpu().numpy()
         assert np.all(y[5, 3] == 0) and np.all(y[7, 1] == 0)
@@ -403,6 +406,44 @@ def test_moe_gemm_routing_beyond_one_pass():
     same = np.all(ids_big[:2000] == ids_small, axis=1)
     assert same.sum() > 1000
     assert np.array_equal(y_big[:2000][same], y_small[same])
+
+
+@pytest.mark.parametrize("d,b,g", [(2, 8, 64), (4, 8, 64), (4, 12, 128), (8, 12, 128)])
+def test_moe_gemm_mixed_tile_kinds(d, b, g):
+    """1024 tokens x top-8 over 992-row experts: enough 32-token units to
+    fill the GPU twice, so hot experts get 128-token tiles (listed first)
+    and the rest 32-token ones, and a last round at most half full runs as
+    256-row halves.  Every output row against the oracle; skipped and
+    out-of-range slots are zero rows."""
+    from vq_dequant_matmul_gemv_amd import binding
+    E, rows, cols, top_k, T = 32, 992, 512, 8, 1024
+    spec, arrs, w = _case(d, b, g, rows, cols, ("moe-mix", d, b, g), experts=E)
+    ids = hot_expert_ids(T, top_k, E, ("moe-mix", d, b, g))
+    x = synth.activations((T, cols), "moe-mix", d, b, g)
+    announce("moe-mix", d, b, g, rows, cols)
+    y = binding.moe_gemm(w, to_dev(x), to_dev(ids)).cpu().numpy()
+    ref = O.moe_ref(arrs["codes"], arrs["codebook"], arrs["scales"], x, ids, cols=cols, d=d, log2_k=b,
+                    group=g, x_per_slot=False)
+    assert np.all(y[900, 7] == 0) and np.all(y[901, 6] == 0)
+    assert row_rel_err(y.reshape(-1, rows), ref.reshape(-1, rows)) <= TOL
+
+
+def test_moe_gemm_mixed_tiles_place_rows_exactly():
+    """The same routing on exact-arithmetic inputs: the grouped GEMM over
+    mixed tile kinds and halves, the per-slot GEMV and the oracle agree bit
+    for bit, so every pair's row lands where it belongs."""
+    from vq_dequant_matmul_gemv_amd import binding
+    E, rows, cols, top_k, T = 32, 992, 256, 8, 1024
+    spec, arrs, w = _case(4, 8, 64, rows, cols, ("moe-mix-exact",), exact=True, experts=E)
+    ids = hot_expert_ids(T, top_k, E, ("moe-mix-exact",))
+    x = synth.activations((T, cols), "moe-mix-exact", exact=True)
+    announce("moe-mix-exact")
+    a = binding.moe_gemm(w, to_dev(x), to_dev(ids)).cpu().numpy()
+    bgv = binding.moe_gemv(w, to_dev(x), to_dev(ids)).cpu().numpy()
+    ref = O.moe_ref(arrs["codes"], arrs["codebook"], arrs["scales"], x, ids, cols=cols, d=4, log2_k=8, group=64,
+                    x_per_slot=False)
+    assert np.array_equal(a, bgv)
+    assert np.array_equal(a.astype(np.float64), ref)
 
 
 def test_moe_grouped_equals_per_slot_bit_identical_on_exact_inputs():

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void vq_zero_kernel(uint32_t* p, int64_t n) {
 // routing: group (token, slot) pairs by expert and emit the token-tile list.
 // One block; pairs and experts are walked in strides of the block size.
 // Workspace layout (int32): counts[E] | offsets[E] | fill[E] | tile_base[E] |
-// n_tiles[1] | pad to 4 | pairs[npairs] | tiles[max_tiles][3]
+// n_tiles[1] | n_wide[1] | pad to 4 | pairs[npairs] | tiles[max_tiles][3]
 // ---------------------------------------------------------------------------
 
 struct RouteArgs {
@@ -75,8 +75,18 @@ struct RouteArgs {
   int32_t* ws;
   void* y;            // skipped slots' output rows are zeroed (nullptr: none to zero)
   int y_row_halves;   // 16-bit words per output row
-  int npairs, num_experts, rows, tile_tokens, max_tiles;
+  int npairs, num_experts;
+  int wide;           // list 128-pair tiles for hot experts
 };
+
+// An expert's tiles: with wide tiles, one per whole kMoeWideTokens pairs and
+// one for a remainder above kMoeWideMin; a smaller remainder (or every pair,
+// without wide tiles) in tiles of kMoeTileTokens.
+__device__ __forceinline__ void expert_tiles(int c, bool wide, int& nw, int& nt) {
+  const int r = wide ? c % kMoeWideTokens : c;
+  nw = wide ? c / kMoeWideTokens + (r > kMoeWideMin ? 1 : 0) : 0;
+  nt = (wide && r > kMoeWideMin) ? 0 : (r + kMoeTileTokens - 1) / kMoeTileTokens;
+}
 
 // Experts whose counters fit in LDS (two int32 per expert); more experts use
 // the workspace copies.  Counters in LDS matter: with skewed routing hundreds
@@ -94,7 +104,9 @@ template <bool kLds>
 __device__ __forceinline__ void route_pairs(const RouteArgs& a, int32_t* counts, int32_t* fill, int32_t* part) {
   const int E = a.num_experts;
   int32_t* tbase = a.ws + 3 * E;
-  int32_t* n_tiles = tbase + E;
+  int32_t* n_tiles = moe_ws_n_tiles(a.ws, E);
+  int32_t* n_wide = moe_ws_n_wide(a.ws, E);
+  const bool wide = a.wide != 0;
   int32_t* pairs = moe_ws_pairs(a.ws, E);
   int32_t* tiles = moe_ws_tiles(a.ws, E, a.npairs);
   const int tid = threadIdx.x, nt = blockDim.x;
@@ -131,47 +143,69 @@ __device__ __forceinline__ void route_pairs(const RouteArgs& a, int32_t* counts,
     }
   }
   __syncthreads();
-  // exclusive scans of counts and of tiles-per-expert: each thread owns a
-  // contiguous run of experts
+  // exclusive scans of the pair counts, the wide tiles and the 32-pair tiles
+  // per expert: each thread owns a contiguous run of experts
   const int per = (E + nt - 1) / nt;
   const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
-  int sc = 0, st = 0;
-  for (int e = e0; e < e1; ++e) { sc += counts[e]; st += (counts[e] + a.tile_tokens - 1) / a.tile_tokens; }
-  // Both scans at once: inclusive within each wave by shuffles, then over
-  // the (at most 16) wave totals by the first wave; two barriers in all.
-  const int lane = tid & 63, wid = tid >> 6, nw = nt >> 6;
-  int ic = sc, it = st;
-  for (int off = 1; off < 64; off <<= 1) {
-    const int c = __shfl_up(ic, off, 64), t = __shfl_up(it, off, 64);
-    if (lane >= off) { ic += c; it += t; }
+  int sc = 0, sw = 0, st = 0;
+  for (int e = e0; e < e1; ++e) {
+    int nw_e, nt_e;
+    expert_tiles(counts[e], wide, nw_e, nt_e);
+    sc += counts[e];
+    sw += nw_e;
+    st += nt_e;
   }
-  if (lane == 63) { part[wid] = ic; part[32 + wid] = it; }
+  // The three scans at once: inclusive within each wave by shuffles, then
+  // over the (at most 16) wave totals by the first wave; two barriers in all.
+  const int lane = tid & 63, wid = tid >> 6, nw = nt >> 6;
+  int ic = sc, iw = sw, it = st;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int c = __shfl_up(ic, off, 64), w = __shfl_up(iw, off, 64), t = __shfl_up(it, off, 64);
+    if (lane >= off) { ic += c; iw += w; it += t; }
+  }
+  if (lane == 63) { part[wid] = ic; part[32 + wid] = iw; part[64 + wid] = it; }
   __syncthreads();
   if (wid == 0) {
-    const int wc = lane < nw ? part[lane] : 0, wt = lane < nw ? part[32 + lane] : 0;
-    int jc = wc, jt = wt;
+    const int wc = lane < nw ? part[lane] : 0, ww = lane < nw ? part[32 + lane] : 0;
+    const int wt = lane < nw ? part[64 + lane] : 0;
+    int jc = wc, jw = ww, jt = wt;
     for (int off = 1; off < 32; off <<= 1) {
-      const int c = __shfl_up(jc, off, 64), t = __shfl_up(jt, off, 64);
-      if (lane >= off) { jc += c; jt += t; }
+      const int c = __shfl_up(jc, off, 64), w = __shfl_up(jw, off, 64), t = __shfl_up(jt, off, 64);
+      if (lane >= off) { jc += c; jw += w; jt += t; }
     }
-    if (lane < nw) { part[64 + lane] = jc - wc; part[96 + lane] = jt - wt; }  // exclusive per wave
-    if (lane == nw - 1) *n_tiles = jt;
+    if (lane < nw) { part[96 + lane] = jc - wc; part[128 + lane] = jw - ww; part[160 + lane] = jt - wt; }
+    if (lane == nw - 1) {
+      part[192] = jw;  // wide tiles in all: the 32-pair tiles follow them
+      *n_tiles = jw + jt;
+      *n_wide = jw;
+    }
   }
   __syncthreads();
-  int run_c = part[64 + wid] + ic - sc;
-  int run_t = part[96 + wid] + it - st;
+  const int total_w = part[192];
+  int run_c = part[96 + wid] + ic - sc;
+  int run_w = part[128 + wid] + iw - sw;
+  int run_t = total_w + part[160 + wid] + it - st;
   for (int e = e0; e < e1; ++e) {
     offsets[e] = run_c;
-    tbase[e] = run_t;
     const int c = counts[e];
-    const int nt_e = (c + a.tile_tokens - 1) / a.tile_tokens;
+    int nw_e, nt_e;
+    expert_tiles(c, wide, nw_e, nt_e);
+    tbase[e] = nw_e > 0 ? run_w : run_t;
+    for (int k = 0; k < nw_e; ++k) {
+      int32_t* t = tiles + 3 * (run_w + k);
+      t[0] = e;
+      t[1] = run_c + k * kMoeWideTokens;
+      t[2] = min(kMoeWideTokens, c - k * kMoeWideTokens);
+    }
+    const int c0 = nw_e * kMoeWideTokens;  // pairs the wide tiles took
     for (int k = 0; k < nt_e; ++k) {
       int32_t* t = tiles + 3 * (run_t + k);
       t[0] = e;
-      t[1] = run_c + k * a.tile_tokens;
-      t[2] = min(a.tile_tokens, c - k * a.tile_tokens);
+      t[1] = run_c + c0 + k * kMoeTileTokens;
+      t[2] = min(kMoeTileTokens, c - c0 - k * kMoeTileTokens);
     }
     run_c += c;
+    run_w += nw_e;
     run_t += nt_e;
   }
   __syncthreads();
@@ -286,31 +320,32 @@ hipError_t launch_gemm(const TensorView& w, const IoSpec& io, const void* x, int
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_moe_gemm(const TensorView& w, const IoSpec& io, const void* x, int x_per_slot,
-                           const int32_t* ids, int T, int top_k, void* y, void* ws, hipStream_t s) {
-  const int npairs = T * top_k;
-  const int E = w.num_experts;
-  int32_t* wsi = static_cast<int32_t*>(ws);
+hipError_t launch_route(const int32_t* ids, int npairs, int num_experts, int32_t* ws, void* y_skip, int y_row_halves,
+                        bool wide, hipStream_t s) {
   RouteArgs r{};
   r.ids = ids;
-  r.ws = wsi;
-  r.y = io.epi == kEpiCombine ? nullptr : y;   // combine: skipped slots add nothing
-  r.y_row_halves = (io.epi == kEpiSwiglu ? w.rows / 2 : w.rows) * (io.y_kind == kOutF32 ? 2 : 1);
+  r.ws = ws;
+  r.y = y_skip;
+  r.y_row_halves = y_row_halves;
   r.npairs = npairs;
-  r.num_experts = E;
-  r.rows = w.rows;
-  r.tile_tokens = kMoeTileTokens;
-  r.max_tiles = moe_max_tiles(npairs, E);
+  r.num_experts = num_experts;
+  r.wide = wide ? 1 : 0;
   hipLaunchKernelGGL(vq_route_kernel, dim3(1), dim3(1024), 0, s, r);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+// Zero y for the combine step, then (in the code width's unit) route and run
+// the grouped GEMM.
+hipError_t launch_moe_gemm(const TensorView& w, const IoSpec& io, const void* x, int x_per_slot,
+                           const int32_t* ids, int T, int top_k, void* y, void* ws, hipStream_t s) {
+  int32_t* wsi = static_cast<int32_t*>(ws);
   if (io.epi == kEpiCombine) {  // the slots add into y: zero it first
-    e = launch_zero(y, (size_t)T * w.rows * sizeof(float), s);
+    hipError_t e = launch_zero(y, (size_t)T * w.rows * sizeof(float), s);
     if (e != hipSuccess) return e;
   }
   switch (w.log2_k) {
 #define X(B) \
-  case B: return moe_gemm_b##B(w, io, x, x_per_slot, T, top_k, y, wsi, s);
+  case B: return moe_gemm_b##B(w, io, x, x_per_slot, ids, T, top_k, y, wsi, s);
     VQMI_BITS(X)
 #undef X
     default: break;

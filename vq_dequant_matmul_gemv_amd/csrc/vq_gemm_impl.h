@@ -151,6 +151,11 @@ struct GemmArgs {
   int top_k, x_per_slot;
   int x_rows;             // routed: rows of x (T or T*top_k)
   int n_row_tiles, n_tok_tiles;
+  // routed: a unit is (tile, row tile); n_wide of the tiles (listed first)
+  // hold 128 tokens, the rest 32.  moe_slots blocks are resident at once,
+  // one per CU (0: the variant runs no row halves).
+  const int32_t* n_wide;  // device scalar
+  int moe_slots;
   // dense grid: blocks [0, n_full) each own a whole tile; the blocks after them
   // each own one of rem_split K slices of a remaining tile and add into y
   // (zeroed beforehand) atomically.
@@ -208,465 +213,117 @@ __device__ __forceinline__ uint32_t pick16(u32x4 v, int pos) {
 constexpr bool kGemmPhaseOffset = true;
 constexpr int kGemmCluster = 4;
 
-template <int D, int B, int G, class SH, bool MOE, bool WIDE>
+// LDS bytes of a tile shape's two x stages [2][tokens][row bytes + 16].
+__host__ __device__ constexpr int gemm_xbuf_bytes(int D, bool wide, int tokens) {
+  return 2 * tokens * (2 * gemm_cg(D, wide) * 2 + 16);
+}
+
+// Dense GEMM: one tile (or one K slice of one) per block.
+template <int D, int B, int G, class SH, bool WIDE>
 __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
-  using L = CodebookLayout<D, B>;
-  constexpr int CG = gemm_cg(D, WIDE);    // columns per lane half per super-step
-  constexpr int S = CG / 8;               // k-steps of 16 (8 per half) per super-step
-  constexpr int NCL = CG / D;             // codes per lane per super-step
-  constexpr int SS = 2 * CG;              // columns per super-step
-  constexpr int MB = SH::kMB;
-  constexpr int NB = SH::kNB;
-  constexpr int WN = SH::kTokens;
-  constexpr int XROW = SS * 2 + 16;       // LDS bytes per token row (padded)
-  constexpr int SEGS = SS / 8;            // 16-byte segments per token row
-  constexpr int NT = SH::kThreads;
-  constexpr int XLD = (WN * SEGS + NT - 1) / NT;  // x segments per thread per super-step
-  constexpr int CPA = 8 / D;              // codebook entries per A fragment (8 columns)
-
-  // Static LDS: codebook, then the two x tiles [2][WN][XROW].
-  __shared__ __align__(16) uint8_t cb_lds[L::kBytes];
-  __shared__ __align__(16) uint8_t xbuf[2 * WN * XROW];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int l32 = lane & 31;
-  const int h = lane >> 5;
-
-  // ---- which tile ----
-  int rt, expert = 0, first = 0, count;
-  int tok_base = 0;
-  int kslice = 0, nslices = 1;  // this block's share of the tile's K range
-  if constexpr (MOE) {
-    const int tix = blockIdx.x;
-    if (tix >= *a.n_tiles) return;
-    expert = a.tiles[3 * tix + 0];
-    first = a.tiles[3 * tix + 1];
-    count = a.tiles[3 * tix + 2];
-    rt = blockIdx.y;
+  __shared__ __align__(16) uint8_t cb_lds[CodebookLayout<D, B>::kBytes];
+  __shared__ __align__(16) uint8_t xbuf[gemm_xbuf_bytes(D, WIDE, SH::kTokens)];
+  const int bid = blockIdx.x;
+  int tile, kslice = 0, nslices = 1;
+  if (bid < a.n_full) {
+    // XCD-aware order: blocks land on XCD (bid % 8) round-robin; give each
+    // XCD a contiguous range of tiles so concurrently running blocks share
+    // x and W slices in that XCD's L2.
+    const int N = a.n_full;
+    const int q = N / 8, r8 = N % 8, xcd = bid % 8, j = bid / 8;
+    tile = xcd * q + min(xcd, r8) + j;
   } else {
-    const int bid = blockIdx.x;
-    int tile;
-    if (bid < a.n_full) {
-      // XCD-aware order: blocks land on XCD (bid % 8) round-robin; give each
-      // XCD a contiguous range of tiles so concurrently running blocks share
-      // x and W slices in that XCD's L2.
-      const int N = a.n_full;
-      const int q = N / 8, r8 = N % 8, xcd = bid % 8, j = bid / 8;
-      tile = xcd * q + min(xcd, r8) + j;
-    } else {
-      const int u = bid - a.n_full;
-      tile = a.n_full + u / a.rem_split;
-      kslice = u % a.rem_split;
-      nslices = a.rem_split;
-    }
-    int tt;
-    gemm_tile_coords(tile, a.n_row_tiles, a.n_tok_tiles, rt, tt);
-    tok_base = tt * WN;
-    count = min(WN, a.T - tok_base);
+    const int u = bid - a.n_full;
+    tile = a.n_full + u / a.rem_split;
+    kslice = u % a.rem_split;
+    nslices = a.rem_split;
   }
+  int rt, tt;
+  gemm_tile_coords(tile, a.n_row_tiles, a.n_tok_tiles, rt, tt);
+  const int tok_base = tt * SH::kTokens;
+  const int count = min(SH::kTokens, a.T - tok_base);
+  using TS = SH;
+  constexpr bool MOE = false, TW = WIDE;
+  constexpr int expert = 0, first = 0;
+#include "vq_gemm_tile.inc"
+}
 
-  const uint32_t* codes = a.codes + (int64_t)expert * a.code_estride;
-  const uint16_t* scales = a.scales + (int64_t)expert * a.scale_estride;
-  const uint16_t* cb = a.codebook + (int64_t)expert * a.cb_estride;
-  // codebook entries: staged in LDS, or read from device memory (large codebooks)
-  const uint8_t* cbp;
-  if constexpr (L::kGlobal) cbp = reinterpret_cast<const uint8_t*>(cb);
-  else cbp = cb_lds;
+// Whether the routed kernel runs a short last round as row halves: only
+// where its LDS (codebook stage and x stages) keeps a second block off the
+// CU (more than half of the CU's 160 KiB).  Where two blocks share a CU, a
+// short last round already runs beside the round before it.
+template <int D, int B, bool WIDE, bool MIX>
+__host__ __device__ constexpr bool moe_halves() {
+  const int xb = gemm_xbuf_bytes(D, WIDE, kMoeTileTokens);
+  const int xbw = MIX ? gemm_xbuf_bytes(D, false, kMoeWideTokens) : 0;
+  return CodebookLayout<D, B>::kBytes + (xb > xbw ? xb : xbw) > 80 * 1024;
+}
 
-  // K range (super-steps) of this block.
-  const int nks_all = (a.cols + SS - 1) / SS;
-  int ks_begin = 0, ks_end = nks_all;
-  if constexpr (!MOE) {
-    ks_begin = (int)((int64_t)nks_all * kslice / nslices);
-    ks_end = (int)((int64_t)nks_all * (kslice + 1) / nslices);
-  }
-
-  // All streaming loads are branch-free buffer loads with 32-bit offsets:
-  // tokens past the tile's count, rows past the end and super-steps past
-  // ks_end get an out-of-range offset and read zeros.
-
-  // ---- x: XLD segments of 16 bytes per thread per super-step ----
-  rsrc_t rx;
-  if constexpr (MOE) {
-    rx = make_rsrc(a.x, (uint64_t)a.x_rows * a.cols * 2);
+// Routed (grouped) GEMM over the routing kernel's tile list, one unit (tile,
+// row tile of SH::kRows) per block, in list order: the 128-token tiles of hot
+// experts (MIX only; the routing kernel lists them first, so they start in
+// the first round), then the 32-token tiles.  The list's length is known only
+// here, on the device: when the last round of units (in 32-token-tile time,
+// a 128-token tile counting two) would fill at most half the resident
+// blocks, its units run as two halves of SH::kRows / 2 rows each, finishing
+// in about half the time.  Blocks past the units exit.
+template <int D, int B, int G, class SH, bool WIDE, bool MIX>
+__global__ __launch_bounds__(SH::kThreads, 1) void vq_moe_gemm_kernel(GemmArgs a) {
+  using SW = GemmShape<SH::kWaves, SH::kMB, 4>;               // 128-token tiles
+  using SHALF = GemmShape<SH::kWaves, SH::kMB / 2, SH::kNB>;  // half units
+  static_assert(SH::kNB == 1 && SH::kMB % 2 == 0, "32-token tiles with whole row halves");
+  constexpr int XB = gemm_xbuf_bytes(D, WIDE, SH::kTokens);
+  constexpr int XBW = MIX ? gemm_xbuf_bytes(D, false, SW::kTokens) : 0;
+  constexpr int XBYTES = XB > XBW ? XB : XBW;
+  static_assert(moe_halves<D, B, WIDE, MIX>() == (CodebookLayout<D, B>::kBytes + XBYTES > 80 * 1024),
+                "row halves exactly where a block's LDS keeps a second block off its CU");
+  __shared__ __align__(16) uint8_t cb_lds[CodebookLayout<D, B>::kBytes];
+  __shared__ __align__(16) uint8_t xbuf[XBYTES];
+  const int nrt = a.n_row_tiles;
+  const int n_wide = MIX ? *a.n_wide : 0;
+  const int n_units = *a.n_tiles * nrt;
+  const int wide_units = n_wide * nrt;
+  const int thin_units = n_units - wide_units;
+  const int rem = a.moe_slots > 0 ? (2 * wide_units + thin_units) % a.moe_slots : 0;
+  const int split = 2 * rem <= a.moe_slots ? min(rem, thin_units) : 0;
+  const int whole = n_units - split;
+  const int b = blockIdx.x;
+  int u, hsel = -1;
+  if (b < whole) {
+    u = b;
+  } else if (b < whole + 2 * split) {
+    u = whole + ((b - whole) >> 1);
+    hsel = (b - whole) & 1;
   } else {
-    rx = make_rsrc(a.x + (int64_t)tok_base * a.cols, (uint64_t)count * a.cols * 2);
+    return;
   }
-  uint32_t xoff[XLD];
-  int xdst[XLD];
-#pragma unroll
-  for (int i = 0; i < XLD; ++i) {
-    const int gs = tid + i * NT;
-    const int tok = gs / SEGS;
-    const int seg = gs % SEGS;
-    xdst[i] = gs < WN * SEGS ? tok * XROW + seg * 16 : -1;
-    uint32_t row;
-    if constexpr (MOE) {
-      const int pair = tok < count ? a.pairs[first + tok] : 0;
-      row = (uint32_t)(a.x_per_slot ? pair : pair / a.top_k);
-    } else {
-      row = (uint32_t)tok;
+  const int tix = u / nrt;
+  const int urt = u - tix * nrt;
+  const int expert = a.tiles[3 * tix + 0];
+  const int first = a.tiles[3 * tix + 1];
+  const int count = a.tiles[3 * tix + 2];
+  constexpr bool MOE = true;
+  constexpr int tok_base = 0, kslice = 0, nslices = 1;
+  if (MIX && tix < n_wide) {
+    if constexpr (MIX) {
+      using TS = SW;
+      constexpr bool TW = false;
+      const int rt = urt;
+#include "vq_gemm_tile.inc"
     }
-    xoff[i] = (gs < WN * SEGS && tok < count) ? row * (uint32_t)a.cols * 2u + (uint32_t)seg * 16u : kOutOfRange;
-  }
-
-  // ---- A: this wave's 32*MB rows, lane row l32 of each m-block ----
-  const int row_base = rt * SH::kRows + wave * 32 * MB;
-  const rsrc_t rc = make_rsrc(codes, (uint64_t)a.rows * a.wr * 4);
-  const rsrc_t rs = make_rsrc(scales, (uint64_t)a.rows * a.spr * 2);
-  uint32_t coff[MB], soff[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const uint32_t r = (uint32_t)(row_base + mb * 32 + l32);  // past the end: reads zeros
-    coff[mb] = r * (uint32_t)a.wr * 4u;
-    soff[mb] = r * (uint32_t)a.spr * 2u;
-  }
-
-  auto load_x = [&](int ks, u32x4 (&xr)[XLD]) {
-    const bool live = ks < ks_end;
-#pragma unroll
-    for (int i = 0; i < XLD; ++i) xr[i] = buf_load_b128(rx, live ? xoff[i] + (uint32_t)ks * SS * 2u : kOutOfRange);
-  };
-  const bool x_bf16 = a.x_bf16 != 0;  // bf16 x: converted to fp16 on its way into LDS
-  auto store_x = [&](int buf, const u32x4 (&xr)[XLD]) {
-#pragma unroll
-    for (int i = 0; i < XLD; ++i)
-      if (xdst[i] >= 0)
-        *reinterpret_cast<u32x4*>(xbuf + buf * (WN * XROW) + xdst[i]) = x_bf16 ? bf16x8_to_f16x8(xr[i]) : xr[i];
-  };
-  // Scales come in 16-byte windows of 8 groups per row (one load per lane
-  // per 8 groups instead of one per super-step; a row's scales are used a
-  // few bytes per super-step, so per-step loads would fetch a cache line per
-  // row for 2 bytes).  The window of the next group range is fetched one
-  // super-step before it is needed.  Rows whose scale runs are not 16-byte
-  // aligned fill the window with 2-byte loads.  Every group of a super-step
-  // lies in one window for both lane halves (8 groups span >= 512 columns).
-  const bool sw_aligned = (a.spr & 7) == 0;
-  u32x4 swc[MB], swp[MB];
-  auto load_window = [&](int w, u32x4 (&dst)[MB]) {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const uint32_t off = soff[mb] + (uint32_t)w * 16u;
-      if (sw_aligned) {
-        dst[mb] = buf_load_b128(rs, off);
-      } else {
-        uint32_t v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          v[q] = (uint32_t)buf_load_b16(rs, off + 4u * q) | ((uint32_t)buf_load_b16(rs, off + 4u * q + 2u) << 16);
-        dst[mb] = u32x4{v[0], v[1], v[2], v[3]};
-      }
-    }
-  };
-  auto window_of = [&](int ks) { return (ks * SS / G) >> 3; };
-  auto load_codes = [&](int ks, LaneCodes<NCL, B> (&cc)[MB], uint16_t (&sc)[MB]) {
-    const bool ok = ks < ks_end;
-    const uint32_t bit = (uint32_t)(ks * 2 * NCL + h * NCL) * B;  // the lane's first code, in bits of the row
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) load_lane_codes<NCL, B>(cc[mb], rc, ok ? coff[mb] : kOutOfRange, bit);
-    const int w = window_of(ks);
-    if (ks == ks_begin) {
-      load_window(w, swc);
-    } else if (w != window_of(ks - 1)) {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) swc[mb] = swp[mb];
-    }
-    if (window_of(ks + 1) != w) load_window(w + 1, swp);
-    const int pos = ((ks * SS + h * CG) / G) & 7;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) sc[mb] = (uint16_t)pick16(swc[mb], pos);
-  };
-
-  const uint32_t lane_off = lane_copy_offset<D, B>(lane);
-  float16_t acc[MB][NB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
-
-  // One super-step: dequantize the A fragments of each m-block straight into
-  // registers and run the MFMAs against the x tile in LDS buffer `buf`.  The
-  // codebook gathers of k-step s + 1 are issued before the arithmetic of
-  // k-step s, so their LDS latency overlaps the MFMAs.  Every super-step is
-  // whole: the API requires cols % (32 d) == 0 and SS divides 32 d (the wide
-  // d = 2 variant runs only when cols % 128 == 0).
-  auto compute = [&](int buf, const LaneCodes<NCL, B> (&cc_in)[MB], const uint16_t (&sc)[MB]) {
-    LaneCodes<NCL, B> cc[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      cc[mb] = cc_in[mb];
-      align_lane_codes<NCL, B>(cc[mb]);  // widths whose runs are not word aligned
-    }
-    const uint8_t* xb = xbuf + buf * (WN * XROW);
-    half2_t s2[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) s2[mb] = as_half2((uint32_t)sc[mb] * 0x10001u);
-    Entry<D> e[2][MB][CPA];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int c = 0; c < CPA; ++c) e[0][mb][c] = lane_gather<D, B, NCL>(cbp, cc[mb], c, lane_off);
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      if (s + 1 < S) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int c = 0; c < CPA; ++c)
-            e[(s + 1) & 1][mb][c] = lane_gather<D, B, NCL>(cbp, cc[mb], (s + 1) * CPA + c, lane_off);
-      }
-      half8_t bf[NB];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        bf[nb] = *reinterpret_cast<const half8_t*>(xb + (nb * 32 + l32) * XROW + (h * CG + 8 * s) * 2);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        half2_t w[4];
-#pragma unroll
-        for (int c = 0; c < CPA; ++c)
-#pragma unroll
-          for (int j = 0; j < D / 2; ++j) w[c * (D / 2) + j] = e[s & 1][mb][c].v[j] * s2[mb];
-        const half8_t af = half8_t{w[0].x, w[0].y, w[1].x, w[1].y, w[2].x, w[2].y, w[3].x, w[3].y};
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(bf[nb], af, acc[mb][nb]);
-      }
-    }
-  };
-
-  // Ping-pong over two register sets (A, B) and two LDS x buffers (0, 1):
-  // the loads for super-step ks + 1 are issued before super-step ks is
-  // computed.  No register copies and no exit in the middle of the loop body
-  // (the second half is skipped by a uniform branch on an odd count), so the
-  // accumulators stay in place and the prefetch stays in flight.
-  u32x4 xr[XLD];
-  LaneCodes<NCL, B> ccA[MB], ccB[MB];
-  uint16_t scA[MB], scB[MB];
-
-  load_x(ks_begin, xr);
-  load_codes(ks_begin, ccA, scA);
-  stage_codebook<D, B>(cb_lds, cb, tid, NT);
-  store_x(0, xr);
-  __syncthreads();
-
-  if constexpr (kGemmPhaseOffset && NB >= 4 && (D == 2 || (D == 4 && B == 8) || D == 8) && LaneCodes<NCL, B>::kAligned &&
-                !L::kGlobal) {
-    // Phase-offset schedule for the 128-token tiles.  A super-step runs as
-    // clusters of KC k-steps, each split into a dequant phase (codebook
-    // gathers and fp16 multiplies for the cluster's W fragments, kept in
-    // registers) and an MFMA phase (x fragments from LDS, KC * MB * NB
-    // MFMAs), separated by block barriers.  The upper half of the waves
-    // enters one phase late, so on every SIMD (waves w and w + 4 share one)
-    // one wave runs its MFMAs while the other dequantizes.  Every wave passes
-    // the same number of barriers: the late half one extra at the start, the
-    // early half one at the end.  The MFMA phase runs at raised wave
-    // priority, so the SIMD's issue slots go to the MFMAs first.  Not used
-    // for d = 4 with 12-bit codes, where a cluster's fragments spill
-    // registers.
-    constexpr int KC = kGemmCluster < S ? kGemmCluster : S;
-    static_assert(S % KC == 0, "clusters tile the super-step");
-    const bool late = wave >= SH::kWaves / 2;
-    auto phase_sync = [&]() {
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    // x of the next super-step is stored at the end of this super-step's
-    // last MFMA phase, behind a barrier that waits for it: the last reads of
-    // that buffer (the super-step before) end at least two barriers earlier,
-    // and the first reads of the new x (the next super-step's first MFMA
-    // phase) come at least one barrier later for both halves.
-    // The next super-step's x stage travels in NCLU parts, one per cluster:
-    // part p is loaded at the start of cluster p's dequant phase and written
-    // to LDS at the end of its MFMA phase (the buffer's last reads end before
-    // the first part is written, and the barrier ending the super-step waits
-    // for every part's stores), so only one part occupies registers.
-    constexpr int NCLU = S / KC;
-    static_assert(XLD % NCLU == 0, "x segments split evenly over the clusters");
-    constexpr int XP = XLD / NCLU;
-    auto load_xp = [&](int ks, int p, u32x4 (&q)[XP]) {
-      const bool live = ks < ks_end;
-#pragma unroll
-      for (int i = 0; i < XP; ++i)
-        q[i] = buf_load_b128(rx, live ? xoff[p * XP + i] + (uint32_t)ks * SS * 2u : kOutOfRange);
-    };
-    auto store_xp = [&](int buf, int p, const u32x4 (&q)[XP]) {
-#pragma unroll
-      for (int i = 0; i < XP; ++i)
-        if (xdst[p * XP + i] >= 0)
-          *reinterpret_cast<u32x4*>(xbuf + buf * (WN * XROW) + xdst[p * XP + i]) =
-              x_bf16 ? bf16x8_to_f16x8(q[i]) : q[i];
-    };
-    auto super_step = [&](int ks, int buf, const LaneCodes<NCL, B> (&cc)[MB], const uint16_t (&sc)[MB],
-                          LaneCodes<NCL, B> (&ccn)[MB], uint16_t (&scn)[MB]) {
-      u32x4 xq[XP];
-      load_xp(ks + 1, 0, xq);
-      load_codes(ks + 1, ccn, scn);
-      const uint8_t* xb = xbuf + buf * (WN * XROW);
-      half2_t s2[MB];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) s2[mb] = as_half2((uint32_t)sc[mb] * 0x10001u);
-#pragma unroll
-      for (int s0 = 0; s0 < S; s0 += KC) {
-        if (s0 > 0) load_xp(ks + 1, s0 / KC, xq);
-        half8_t af[KC][MB];
-        Entry<D> e[KC][MB][CPA];
-#pragma unroll
-        for (int k = 0; k < KC; ++k)
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int c = 0; c < CPA; ++c)
-              e[k][mb][c] = lane_gather<D, B, NCL>(cbp, cc[mb], (s0 + k) * CPA + c, lane_off);
-#pragma unroll
-        for (int k = 0; k < KC; ++k)
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            half2_t w[4];
-#pragma unroll
-            for (int c = 0; c < CPA; ++c)
-#pragma unroll
-              for (int j = 0; j < D / 2; ++j) w[c * (D / 2) + j] = e[k][mb][c].v[j] * s2[mb];
-            af[k][mb] = half8_t{w[0].x, w[0].y, w[1].x, w[1].y, w[2].x, w[2].y, w[3].x, w[3].y};
-          }
-        phase_sync();
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int k = 0; k < KC; ++k) {
-          half8_t bf[NB];
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            bf[nb] = *reinterpret_cast<const half8_t*>(xb + (nb * 32 + l32) * XROW + (h * CG + 8 * (s0 + k)) * 2);
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(bf[nb], af[k][mb], acc[mb][nb]);
-        }
-        __builtin_amdgcn_s_setprio(0);
-        store_xp(buf ^ 1, s0 / KC, xq);
-        if (s0 + KC == S) {
-          __builtin_amdgcn_sched_barrier(0);
-          lds_barrier();
-          __builtin_amdgcn_sched_barrier(0);
-        } else {
-          phase_sync();
-        }
-      }
-    };
-    if (late) phase_sync();
-    for (int ks = ks_begin; ks < ks_end; ks += 2) {
-      super_step(ks, 0, ccA, scA, ccB, scB);
-      if (ks + 1 < ks_end) super_step(ks + 1, 1, ccB, scB, ccA, scA);
-    }
-    if (!late) phase_sync();
-  } else
-  for (int ks = ks_begin; ks < ks_end; ks += 2) {
-    load_x(ks + 1, xr);
-    load_codes(ks + 1, ccB, scB);
-    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
-    compute(0, ccA, scA);
-    store_x(1, xr);
-    __syncthreads();
-    load_x(ks + 2, xr);
-    load_codes(ks + 2, ccA, scA);
-    __builtin_amdgcn_sched_barrier(0);
-    if (ks + 1 < ks_end) compute(1, ccB, scB);
-    store_x(0, xr);
-    __syncthreads();
-  }
-
-  // ---- epilogue: x is the MFMA's A operand and W its B operand, so lane
-  // (l32, h) holds W row row_base + 32*mb + l32 for tokens 32*nb + 8*(i/4) +
-  // 4*h + (i%4): for each i a half-wave covers 32 consecutive y elements of
-  // one token (128 contiguous bytes), for stores and atomics alike.
-  // Output step.  Lane (l32, h) holds W row row_base + 32*mb + l32 for tokens
-  // 32*nb + 8*(i/4) + 4*h + (i%4).  Each output kind has a loop nest of its
-  // own (block-uniform branch outside the loops), so every nest unrolls and
-  // the accumulators stay in registers.
-  const int row = row_base + l32;  // + 32 * mb
-  auto out_row = [&](int tok) {
-    if constexpr (MOE) return a.pairs[first + tok];
-    else return tok_base + tok;
-  };
-  if (a.epi == kEpiNone && a.y_kind == kOutF32) {
-    // plain fp32: for each i a half-wave covers 32 consecutive y elements of
-    // one token (128 contiguous bytes), for stores and atomics alike
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int tok = nb * 32 + 8 * (i / 4) + 4 * h + (i % 4);
-        if (tok >= count) continue;
-        float* yrow = reinterpret_cast<float*>(a.y) + (int64_t)out_row(tok) * a.rows;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int r = row + 32 * mb;
-          if (r < a.rows) {
-            if (nslices > 1) atomicAdd(yrow + r, acc[mb][nb][i]);  // block-uniform branch
-            else yrow[r] = acc[mb][nb][i];
-          }
-        }
-      }
-    }
-  } else if (a.epi == kEpiSwiglu) {
-    // rows 2i (gate, even lane) and 2i + 1 (up, the odd neighbour, fetched by
-    // a DPP swap; both lanes of a pair hold the same tokens) -> y[.][i]
-    const int y_kind = a.y_kind, half_rows = a.rows >> 1;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int tok = nb * 32 + 8 * (i / 4) + 4 * h + (i % 4);
-        if (tok >= count) continue;
-        const int64_t ybase = (int64_t)out_row(tok) * half_rows;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int r = row + 32 * mb;
-          const float up = dpp_mov<0xB1>(acc[mb][nb][i]);  // quad_perm [1,0,3,2]
-          if ((l32 & 1) == 0 && r < a.rows) store_out(a.y, ybase + (r >> 1), swiglu(acc[mb][nb][i], up), y_kind);
-        }
-      }
-    }
-  } else if (a.epi == kEpiCombine) {
-    // routed only: y[token] += router weight x row
-    if constexpr (MOE) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int tok = nb * 32 + 8 * (i / 4) + 4 * h + (i % 4);
-          if (tok >= count) continue;
-          const int pair = out_row(tok);
-          const float wgt = a.route_w[pair];
-          float* yrow = reinterpret_cast<float*>(a.y) + (int64_t)(pair / a.top_k) * a.rows;
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            const int r = row + 32 * mb;
-            if (r < a.rows) atomicAdd(yrow + r, wgt * acc[mb][nb][i]);
-          }
-        }
-      }
+  } else if (hsel >= 0) {
+    if constexpr (moe_halves<D, B, WIDE, MIX>()) {
+      using TS = SHALF;
+      constexpr bool TW = WIDE;
+      const int rt = 2 * urt + hsel;
+      if (rt * TS::kRows >= a.rows) return;
+#include "vq_gemm_tile.inc"
     }
   } else {
-    // fp16 / bf16 y (such tiles are never split along K)
-    const int y_kind = a.y_kind;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int tok = nb * 32 + 8 * (i / 4) + 4 * h + (i % 4);
-        if (tok >= count) continue;
-        const int64_t ybase = (int64_t)out_row(tok) * a.rows;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int r = row + 32 * mb;
-          if (r < a.rows) store_out(a.y, ybase + r, acc[mb][nb][i], y_kind);
-        }
-      }
-    }
+    using TS = SH;
+    constexpr bool TW = WIDE;
+    const int rt = urt;
+#include "vq_gemm_tile.inc"
   }
 }
 
@@ -704,7 +361,8 @@ using GemmSmallT = GemmShape<8, 2, 1>;  // 512 rows x 32 tokens, two waves per S
 using GemmLargeT = GemmShape<8, 2, 4>;  // 512 rows x 128 tokens
 using GemmMoe = GemmShape<8, 2, 1>;     // 512 rows x 32 tokens: routed experts mostly get a
                                         // few tokens, so thin tiles waste the least MFMA work
-static_assert(GemmMoe::kTokens == kMoeTileTokens, "routing tiles match the grouped GEMM's token tile");
+static_assert(GemmMoe::kTokens == kMoeTileTokens && 4 * GemmMoe::kTokens == kMoeWideTokens,
+              "routing tiles match the grouped GEMM's token tiles");
 
 // d = 2 thin tiles (32 tokens) take 128-column super-steps when the columns
 // allow: half the barriers and x stages per column, 6-10 % faster there; the
@@ -712,15 +370,15 @@ static_assert(GemmMoe::kTokens == kMoeTileTokens, "routing tiles match the group
 template <int D, class SH>
 bool gemm_wide(int cols) { return D == 2 && SH::kTokens <= 32 && cols % 128 == 0; }
 
-template <int D, int B, int G, class SH, bool MOE>
+template <int D, int B, int G, class SH>
 hipError_t gemm_launch(const GemmArgs& a, dim3 grid, hipStream_t s) {
   if constexpr (D == 2 && SH::kTokens <= 32) {
     if (gemm_wide<D, SH>(a.cols)) {
-      hipLaunchKernelGGL((vq_gemm_kernel<D, B, G, SH, MOE, true>), grid, dim3(SH::kThreads), 0, s, a);
+      hipLaunchKernelGGL((vq_gemm_kernel<D, B, G, SH, true>), grid, dim3(SH::kThreads), 0, s, a);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((vq_gemm_kernel<D, B, G, SH, MOE, false>), grid, dim3(SH::kThreads), 0, s, a);
+  hipLaunchKernelGGL((vq_gemm_kernel<D, B, G, SH, false>), grid, dim3(SH::kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -802,7 +460,7 @@ hipError_t gemm_dense(GemmArgs a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return gemm_launch<D, B, G, SH, false>(a, dim3((unsigned)(full + rem * split)), s);
+  return gemm_launch<D, B, G, SH>(a, dim3((unsigned)(full + rem * split)), s);
 }
 
 template <int D, int B, int G>
@@ -813,23 +471,49 @@ hipError_t gemm_geom(const TensorView& w, const IoSpec& io, const void* x, int T
   return gemm_dense<D, B, G, GemmLargeT>(a, s);
 }
 
-// The grouped GEMM over the tile list the routing kernel left in the
-// workspace.
+// The routed kernel variant (32-token tiles with 128-column super-steps for
+// d = 2; MIX: 128-token tiles too), launched over max_units whole units plus
+// room for the halves of a last round where the variant runs them.
+template <int D, int B, int G, bool WIDE, bool MIX>
+hipError_t moe_launch(GemmArgs a, int max_units, hipStream_t s) {
+  a.moe_slots = moe_halves<D, B, WIDE, MIX>() ? num_cus() : 0;
+  hipLaunchKernelGGL((vq_moe_gemm_kernel<D, B, G, GemmMoe, WIDE, MIX>), dim3((unsigned)(max_units + a.moe_slots / 2)),
+                     dim3(GemmMoe::kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+// Route the pairs, then the grouped GEMM over the tile list the routing
+// kernel left in the workspace.  128-token tiles for hot experts pay when
+// the 32-token units alone would take at least kMoeWideRounds rounds of the
+// GPU even if every expert's pairs filled whole tiles: a 128-token tile
+// takes about twice a 32-token one, so in shorter runs it would outlast
+// the rest of the schedule.
+constexpr int kMoeWideRounds = 2;
+
 template <int D, int B, int G>
-hipError_t moe_gemm_geom(const TensorView& w, const IoSpec& io, const void* x, int x_per_slot, int T, int top_k,
-                         void* y, int32_t* ws, hipStream_t s) {
+hipError_t moe_gemm_geom(const TensorView& w, const IoSpec& io, const void* x, int x_per_slot, const int32_t* ids,
+                         int T, int top_k, void* y, int32_t* ws, hipStream_t s) {
   const int npairs = T * top_k;
   const int E = w.num_experts;
   GemmArgs a = base_args(w, io, x, y, G, D, B);
   a.tiles = moe_ws_tiles(ws, E, npairs);
   a.n_tiles = moe_ws_n_tiles(ws, E);
+  a.n_wide = moe_ws_n_wide(ws, E);
   a.pairs = moe_ws_pairs(ws, E);
   a.top_k = top_k;
   a.x_per_slot = x_per_slot;
   a.x_rows = x_per_slot ? npairs : T;
   a.n_row_tiles = (a.rows + GemmMoe::kRows - 1) / GemmMoe::kRows;
-  dim3 grid(moe_max_tiles(npairs, E), a.n_row_tiles);
-  return gemm_launch<D, B, G, GemmMoe, true>(a, grid, s);
+  const int64_t min_units = (int64_t)((npairs + kMoeTileTokens - 1) / kMoeTileTokens) * a.n_row_tiles;
+  const bool mix = min_units >= (int64_t)kMoeWideRounds * num_cus();
+  void* y_skip = io.epi == kEpiCombine ? nullptr : y;  // combine: skipped slots add nothing
+  const int y_row_halves = (io.epi == kEpiSwiglu ? w.rows / 2 : w.rows) * (io.y_kind == kOutF32 ? 2 : 1);
+  hipError_t e = launch_route(ids, npairs, E, ws, y_skip, y_row_halves, mix, s);
+  if (e != hipSuccess) return e;
+  const int max_units = moe_max_tiles(npairs, E) * a.n_row_tiles;
+  const bool wide = gemm_wide<D, GemmMoe>(a.cols);
+  if (mix) return wide ? moe_launch<D, B, G, true, true>(a, max_units, s) : moe_launch<D, B, G, false, true>(a, max_units, s);
+  return wide ? moe_launch<D, B, G, true, false>(a, max_units, s) : moe_launch<D, B, G, false, false>(a, max_units, s);
 }
 
 }  // namespace
@@ -845,10 +529,10 @@ hipError_t gemm_bits(const TensorView& w, const IoSpec& io, const void* x, int T
 }
 
 template <int B>
-hipError_t moe_gemm_bits(const TensorView& w, const IoSpec& io, const void* x, int x_per_slot, int T, int top_k,
-                         void* y, int32_t* ws, hipStream_t s) {
+hipError_t moe_gemm_bits(const TensorView& w, const IoSpec& io, const void* x, int x_per_slot, const int32_t* ids,
+                         int T, int top_k, void* y, int32_t* ws, hipStream_t s) {
 #define X(D, G) \
-  if (w.d == D && w.group == G) return moe_gemm_geom<D, B, G>(w, io, x, x_per_slot, T, top_k, y, ws, s);
+  if (w.d == D && w.group == G) return moe_gemm_geom<D, B, G>(w, io, x, x_per_slot, ids, T, top_k, y, ws, s);
   X(2, 64) X(2, 128) X(4, 64) X(4, 128) X(8, 64) X(8, 128)
 #undef X
   return hipErrorInvalidValue;
@@ -859,9 +543,9 @@ hipError_t moe_gemm_bits(const TensorView& w, const IoSpec& io, const void* x, i
   hipError_t gemm_b##B(const TensorView& w, const IoSpec& io, const void* x, int T, void* y, hipStream_t s) { \
     return gemm_bits<B>(w, io, x, T, y, s);                                                                  \
   }                                                                                                          \
-  hipError_t moe_gemm_b##B(const TensorView& w, const IoSpec& io, const void* x, int x_per_slot, int T,     \
-                           int top_k, void* y, int32_t* ws, hipStream_t s) {                                \
-    return moe_gemm_bits<B>(w, io, x, x_per_slot, T, top_k, y, ws, s);                                       \
+  hipError_t moe_gemm_b##B(const TensorView& w, const IoSpec& io, const void* x, int x_per_slot,           \
+                           const int32_t* ids, int T, int top_k, void* y, int32_t* ws, hipStream_t s) {     \
+    return moe_gemm_bits<B>(w, io, x, x_per_slot, ids, T, top_k, y, ws, s);                                  \
   }
 
 }  // namespace vqmi

@@ -39,8 +39,8 @@ constexpr int kMaxBits = 14;
                        const int32_t* ids, int top_k, int x_per_slot, hipStream_t s);                        \
   hipError_t dequant_b##B(const TensorView& w, int expert, uint16_t* out, hipStream_t s);                   \
   hipError_t gemm_b##B(const TensorView& w, const IoSpec& io, const void* x, int T, void* y, hipStream_t s); \
-  hipError_t moe_gemm_b##B(const TensorView& w, const IoSpec& io, const void* x, int x_per_slot, int T,     \
-                           int top_k, void* y, int32_t* ws, hipStream_t s);
+  hipError_t moe_gemm_b##B(const TensorView& w, const IoSpec& io, const void* x, int x_per_slot,           \
+                           const int32_t* ids, int T, int top_k, void* y, int32_t* ws, hipStream_t s);
 VQMI_BITS(VQMI_DECLARE_WIDTH)
 #undef VQMI_DECLARE_WIDTH
 
@@ -58,16 +58,23 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
 size_t moe_workspace_bytes(int T, int top_k, int num_experts);
 
-// Routed GEMM: (token, slot) pairs go in tiles of this many per expert.
+// Routed GEMM: (token, slot) pairs go in tiles of this many per expert; with
+// wide tiles on, also in tiles of kMoeWideTokens: one per whole 128 pairs of
+// an expert and one for a remainder above kMoeWideMin (a smaller remainder
+// takes 32-pair tiles).
 constexpr int kMoeTileTokens = 32;
+constexpr int kMoeWideTokens = 128;
+constexpr int kMoeWideMin = 64;
 
 // Routing workspace (int32): counts[E] | offsets[E] | fill[E] | tile_base[E] |
-// n_tiles | pad to 4 | pairs[npairs] | tiles[max_tiles][3] (expert, first
-// pair, count).  At most ceil(npairs / tile) + E tiles.
+// n_tiles | n_wide | pad to 4 | pairs[npairs] | tiles[max_tiles][3] (expert,
+// first pair, count; the n_wide wide tiles first).  At most ceil(npairs /
+// 32) + E tiles (an expert's wide tiles never outnumber its 32-pair tiles).
 __host__ __device__ inline int moe_max_tiles(int npairs, int E) {
   return (npairs + kMoeTileTokens - 1) / kMoeTileTokens + E;
 }
 __host__ __device__ inline int32_t* moe_ws_n_tiles(int32_t* ws, int E) { return ws + 4 * E; }
+__host__ __device__ inline int32_t* moe_ws_n_wide(int32_t* ws, int E) { return ws + 4 * E + 1; }
 __host__ __device__ inline int32_t* moe_ws_pairs(int32_t* ws, int E) { return ws + ((4 * E + 1 + 3) & ~3); }
 __host__ __device__ inline int32_t* moe_ws_tiles(int32_t* ws, int E, int npairs) {
   return moe_ws_pairs(ws, E) + ((npairs + 3) & ~3);
@@ -77,6 +84,12 @@ __host__ __device__ inline int32_t* moe_ws_tiles(int32_t* ws, int E, int npairs)
 // address on the current device (looked up once per device).
 constexpr size_t kStaticScratchBytes = (size_t)4 << 20;
 hipError_t static_scratch(void** out);
+// The routing pass (vq_gemm.hip): group the pairs of `ids` by expert into
+// the workspace and write the tile list (wide: 128-pair tiles for hot
+// experts); skipped slots' output rows (y_row_halves 16-bit words each) are
+// zeroed unless y_skip is null.
+hipError_t launch_route(const int32_t* ids, int npairs, int num_experts, int32_t* ws, void* y_skip, int y_row_halves,
+                        bool wide, hipStream_t s);
 hipError_t launch_moe_gemm(const TensorView& w, const IoSpec& io, const void* x, int x_per_slot,
                            const int32_t* ids, int T, int top_k, void* y, void* ws, hipStream_t s);
 
