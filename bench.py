@@ -787,12 +787,12 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "vq_moe_gemv over the gate+up stack (T=1, ids {0,1})",
                      "achieved": round(gu_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic("vq_gemv_kernel<2, 8, 64, 5, 2, true>", GATE_TAG),
+                     "traffic": measured_traffic("vq_gemv_kernel<2, 8, 64, 5, 2, true,", GATE_TAG),
                      "algorithmic_bytes": gu_bytes},
         "roofline_single_tensor": {"bound": "hbm", "kernel": "vq_gemv (gate, T=1)",
                                    "achieved": round(gate_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                    "frac": round(gate_gbps / HBM_PEAK_GBPS, 4),
-                                   "traffic": measured_traffic("vq_gemv_kernel<2, 8, 64, 5, 2, false>", GATE_TAG),
+                                   "traffic": measured_traffic("vq_gemv_kernel<2, 8, 64, 5, 2, false,", GATE_TAG),
                                    "algorithmic_bytes": dec_bytes["gate"]},
         "roofline_prefill": {"bound": "mfma", "kernel": "vq_gemm (gate, T=2048)",
                              "achieved": round(gate_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,

@@ -1,0 +1,89 @@
+"""GPU parity of the matrix-core GEMV: dense vq_gemv calls of two or more
+tokens on matrices with at least one 16-row group per CU and rows short
+enough for its passes (d = 2: 5120 columns, d = 4: 6144, d = 8: 4096).
+
+The codebook entries go straight into the MFMA B operand and the x of four
+chunk positions into a block-diagonal A operand, so every output needs the
+right entry, the right x columns and the right scale group; each case is
+checked against the CPU oracle on every output.  Rows past a whole number of
+16-row groups, pass widths with idle chunk slots, token counts that leave a
+partial four-token slice, bf16 / fp16 inputs and outputs and the SwiGLU step
+are covered."""
+import numpy as np
+import pytest
+
+from oracle import vq_oracle as O
+from vq_dequant_matmul_gemv_amd import synth
+from tests.helpers import TOL, announce, row_rel_err, to_dev, upload
+
+pytestmark = pytest.mark.gpu
+
+GEOMS = [(d, b, g) for d in (2, 4, 8) for b in (8, 12) for g in (64, 128)]
+ROWS = 4096 + 37          # 16 rows per CU on 256 CUs, and a ragged last group
+
+
+def _case(d, b, g, rows, cols, key):
+    spec = synth.Spec(rows=rows, cols=cols, d=d, log2_k=b, group=g)
+    arrs = synth.tensor(spec, *key)
+    return spec, arrs, upload(arrs, spec)
+
+
+def _ref(arrs, spec, x):
+    return O.gemv_ref(arrs["codes"][0], arrs["codebook"], arrs["scales"][0], x, spec.cols, spec.d,
+                      spec.log2_k, spec.group)
+
+
+@pytest.mark.parametrize("d,b,g", GEOMS)
+def test_mf_gemv_all_geometries(d, b, g):
+    from vq_dequant_matmul_gemv_amd import binding
+    spec, arrs, w = _case(d, b, g, ROWS, 2048, ("mf", d, b, g))
+    for T in (2, 3, 4):
+        x = synth.activations((T, spec.cols), "mf", d, b, g, T)
+        announce("mf-gemv", d, b, g, T)
+        y = binding.gemv(w, to_dev(x)).cpu().numpy()
+        assert row_rel_err(y, _ref(arrs, spec, x)) <= TOL, T
+
+
+@pytest.mark.parametrize("rows,cols,d,b,g,Ts", [
+    (ROWS, 5120, 2, 8, 64, (2, 4)),        # 160 chunks: 8 passes of 20 on 4 lanes x 5
+    (ROWS, 6144, 4, 8, 64, (2, 4)),        # 96 chunks: 8 passes of 12 on 4 lanes x 3
+    (ROWS, 5120, 4, 12, 128, (3,)),        # 80 chunks: 8 passes of 10, two idle slots
+    (4096, 4096, 8, 12, 128, (2, 5, 8)),   # 32 chunks: 8 passes of 4; 16M weights keep 8 tokens
+    (4608, 1088, 2, 8, 64, (4, 7)),        # 34 chunks: 2 passes of 17 on 4 lanes x 5
+])
+def test_mf_gemv_widths_passes_and_slices(rows, cols, d, b, g, Ts):
+    from vq_dequant_matmul_gemv_amd import binding
+    spec, arrs, w = _case(d, b, g, rows, cols, ("mf-wide", rows, cols, d, b, g))
+    for T in Ts:
+        x = synth.activations((T, cols), "mf-wide", rows, cols, T)
+        announce("mf-gemv-wide", rows, cols, d, b, g, T)
+        y = binding.gemv(w, to_dev(x)).cpu().numpy()
+        assert row_rel_err(y, _ref(arrs, spec, x)) <= TOL, T
+
+
+@pytest.mark.parametrize("d,b,g", [(2, 8, 64), (4, 8, 64), (8, 12, 128)])
+def test_mf_gemv_io_types_and_swiglu(d, b, g):
+    """bf16 x, fp16 / bf16 y and the SwiGLU step over row pairs (2i, 2i + 1)."""
+    import torch
+    from vq_dequant_matmul_gemv_amd import binding
+    rows, cols, T = ROWS + 1, 2048, 3
+    spec, arrs, w = _case(d, b, g, rows, cols, ("mf-io", d, b, g))
+    xb = synth.activations_bf16((T, cols), "mf-io", d, b, g)
+    ref = O.gemv_ref(arrs["codes"][0], arrs["codebook"], arrs["scales"][0], O.bf16_to_f64(xb), cols, d, b, g)
+    announce("mf-gemv-io", d, b, g)
+    xd = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+    y16 = binding.gemv(w, xd, y_dtype=torch.float16).float().cpu().numpy()
+    assert row_rel_err(y16, ref) <= TOL + 2.0 ** -11
+    h = binding.gemv(w, xd, y_dtype=torch.bfloat16, epilogue="swiglu").float().cpu().numpy()
+    assert row_rel_err(h, O.swiglu_ref(ref)) <= TOL + 2.0 ** -8
+
+
+def test_mf_gemv_repeat_runs_bit_identical():
+    """No atomics: two runs give the same bits."""
+    from vq_dequant_matmul_gemv_amd import binding
+    spec, arrs, w = _case(4, 8, 64, ROWS, 2048, ("mf-rep",))
+    x = to_dev(synth.activations((4, 2048), "mf-rep"))
+    announce("mf-gemv-repeat")
+    a = binding.gemv(w, x).cpu().numpy()
+    b = binding.gemv(w, x).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))

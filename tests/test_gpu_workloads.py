@@ -69,7 +69,7 @@ def test_dense_mlp_trio(name, fn, T):
 
 
 @pytest.mark.parametrize("name", ["A", "B"])
-@pytest.mark.parametrize("fn,T", [("gemv", 1), ("gemv", 4), ("gemv", 16), ("gemm", 16),
+@pytest.mark.parametrize("fn,T", [("gemv", 1), ("gemv", 2), ("gemv", 3), ("gemv", 4), ("gemv", 16), ("gemm", 16),
                                   ("gemm", 256), ("gemm", 4096)])
 def test_sweep_17408x5120_d4k256(name, fn, T):
     _dense_case("sweep_17408x5120_d4k256", name, fn, T)

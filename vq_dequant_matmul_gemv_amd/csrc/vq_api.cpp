@@ -221,14 +221,20 @@ vq_status vq_dequant(const vq_tensor* w, int32_t expert, uint16_t* w_out, void* 
 
 // Largest token count for which the streaming GEMV beats the MFMA GEMM,
 // measured on MI355X at the benchmark shapes: the GEMV reads every code once
-// per grid slice (two tokens per slice where a row's x fits 16 KiB, else one),
-// the GEMM once per 32- or 128-token tile, split along K to fill the GPU.
-// Small matrices stay in L2 between token slices, and d = 8 codes are few per
-// weight, so the GEMV keeps a few tokens there; otherwise it wins up to T = 2
-// (17408x5120 and 5120x17408, d = 2 and 4: 15.9-18.6 us against 17.3-21.7 us
-// for the GEMM) and loses from T = 3 on.
+// per grid slice, the GEMM once per 32- or 128-token tile, split along K to
+// fill the GPU.  Where the matrix-core GEMV takes the call (four tokens per
+// slice) it wins up to T = 4 (17408x5120 d = 4: 11.6-12.7 us at T = 2-4
+// against 17.7-17.9 us for the GEMM; d = 2: 15.1-15.8 against 17.1-22.3 us)
+// and loses from T = 5 on (two slices read the codes twice), except on
+// matrices that stay in L2 between slices (4096x4096 d = 8, T = 8: 9.6 against
+// 15.3 us).  Otherwise small matrices and d = 8 keep a few tokens on the
+// scalar GEMV, and the rest wins up to T = 2 (two tokens per slice;
+// 17408x5120 and 5120x17408, d = 2 and 4: 15.9-18.6 us against 17.3-21.7 us
+// for the GEMM).
 static int gemv_token_limit(const vqmi::TensorView& v) {
-  if ((int64_t)v.rows * v.cols <= (int64_t)16 << 20) return 6;
+  const bool small = (int64_t)v.rows * v.cols <= (int64_t)16 << 20;
+  if (vqmi::gemv_mf_takes(v.rows, v.cols, v.d, 2, vqmi::device_cus())) return small ? 8 : 4;
+  if (small) return 6;
   if (v.d == 8) return 4;
   return 2;
 }

@@ -21,6 +21,17 @@ hipError_t launch_gemv(const TensorView& w, const IoSpec& io, const void* x, int
   return hipErrorInvalidValue;
 }
 
+int device_cus() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+  }
+  return n;
+}
+
 hipError_t launch_dequant(const TensorView& w, int expert, uint16_t* out, hipStream_t s) {
   switch (w.log2_k) {
 #define X(B) \

@@ -34,6 +34,18 @@
 //    otherwise one token per slice, re-reading the codes per token.  Above a
 //    few tokens the MFMA GEMM is the faster kernel and the C ABI's vq_gemv
 //    hands such calls to it.
+//  * Matrix-core variant (MF) for dense calls of 2 to 4 tokens (up to 8 on
+//    matrices that stay in L2): the dot products move from the VALU to
+//    v_mfma_f32_16x16x32_f16.  Lane l serves row l % 16 of a 16-row group at
+//    chunk position l / 16 (4 lanes per row, C chunks each); the gathered
+//    codebook entries are the B operand as they arrive (no VALU work on
+//    them), and the A operand holds x block-diagonally: A row 4t + p carries
+//    token t's x for chunk position p only, so one MFMA returns, per token,
+//    the four chunk positions' partial sums in four separate registers.  Each
+//    is one scale group's sum (a chunk lies inside one group, or a group
+//    inside it), so the scale multiplies it once, as in the scalar kernel.
+//    Per code: one v_perm_b32 and one gather; the per-token dot products
+//    cost nothing extra up to four tokens.
 //  * Each wave keeps P row groups' loads in flight (P items of C chunks per
 //    lane, about six chunks in all): wide items (d = 2, five chunks per lane)
 //    keep one, since a deeper ring only holds the wave at the issue of loads
@@ -98,6 +110,18 @@ __host__ __device__ constexpr int gemv_max_c(int D, int B, int TT) {
 // memory round trip.
 __host__ __device__ constexpr int gemv_ring(int C) { return C >= 4 ? 1 : (C == 3 ? 2 : (C == 2 ? 3 : 4)); }
 
+// Matrix-core variant (MF): tokens per grid slice and chunks per lane.  The
+// x of a pass sits in the MFMA A operand, 4 * d VGPRs per chunk, like the
+// scalar kernel's x-stationary registers.
+constexpr int kGemvMfTokens = 4;
+__host__ __device__ constexpr int gemv_mf_max_c(int D) { return D == 2 ? 5 : (D == 4 ? 3 : 1); }
+// x bytes per token a block stages (the longest rows MF takes: 8 passes of 4 * C chunks)
+__host__ __device__ constexpr int gemv_mf_x_bytes(int D) { return 8 * 4 * gemv_mf_max_c(D) * 32 * D; }
+#ifndef VQMI_MF_RING_EXTRA
+#define VQMI_MF_RING_EXTRA 0
+#endif
+__host__ __device__ constexpr int gemv_mf_ring(int C) { return gemv_ring(C) + VQMI_MF_RING_EXTRA; }
+
 // Sum of v over aligned groups of L = 1 << lg lanes; valid in the group's last lane.
 __device__ __forceinline__ float lane_group_sum(float v, int lg) {
   v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
@@ -112,7 +136,7 @@ __device__ __forceinline__ float lane_group_sum(float v, int lg) {
 // XS: the x slice takes XS * 8 KiB of LDS per token (2 or 5); fewer staging
 // loads for short rows.  TT: tokens per grid slice (1, or 2 for dense calls
 // with XS = 2).
-template <int D, int B, int G, int C, int XS, bool MOE, int TT>
+template <int D, int B, int G, int C, int XS, bool MOE, int TT, bool MF>
 //
 // The arguments a block needs before its first loads come first, as scalars:
 // with kernel-argument preloading (the build passes
@@ -133,18 +157,19 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
   constexpr int HX = 8 * D;                              // half2 of x per chunk
   constexpr int NW = kGemvWaves;
   constexpr int NT = kGemvThreads;
-  static_assert(C <= gemv_max_c(D, B, TT), "tile does not fit the VGPR budget");
-  static_assert(TT == 1 || (!MOE && XS == 2), "two-token slices: dense calls with short x slices");
+  static_assert(C <= (MF ? gemv_mf_max_c(D) : gemv_max_c(D, B, TT)), "tile does not fit the VGPR budget");
+  static_assert(MF ? TT == kGemvMfTokens : (TT == 1 || (!MOE && XS == 2)),
+                "two-token slices: dense calls with short x slices");
 
   __shared__ __align__(16) uint8_t cb_lds[LY::kBytes];
-  constexpr int XBYTES = XS * 8192;                                 // x bytes staged at most
+  constexpr int XBYTES = MF ? gemv_mf_x_bytes(D) : XS * 8192;       // x bytes staged at most, per token
   // In LDS each chunk's 32 D bytes of x are followed by 16 bytes of padding:
   // the lanes of a row read consecutive chunks' x at once, and unpadded the
   // 32 D-byte stride would put 8 to 16 of them on the same banks.
   constexpr int XCB = 32 * D;
   constexpr int XSTRIDE = XCB + 16;
   constexpr int XTOK = XBYTES / XCB * XSTRIDE;                      // LDS bytes of one token's x
-  __shared__ __align__(16) uint8_t x_lds[TT * XTOK];                // [TT][nq][XSTRIDE]
+  __shared__ __align__(16) uint8_t x_lds[TT * XTOK + (MF ? 16 : 0)];  // [TT][nq][XSTRIDE] (+ MF: 16 zero bytes)
   __shared__ __align__(16) uint8_t s_lds[kGemvScaleBytes];          // the block's scale rows
   __shared__ float pieces[kGemvPieces];                             // [TT][rows][passes]
 
@@ -157,10 +182,12 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
   const int PW = (int)(shape >> 23);       // chunks per pass; the last pass may hold fewer
   const int cols = spr * G;
   const int wr = cols / (32 * D) * B;     // code words per row
+  // MF: lane l serves row l % 16 of a 16-row group at chunk position l / 16
+  // (the B-operand layout of v_mfma_f32_16x16x32_f16); L = 4, lg = 2.
   const int L = 1 << lg;
-  const int R = 64 >> lg;                 // rows per group
-  const int rsub = lane >> lg;            // this lane's row within the group
-  const int li = lane & (L - 1);          // this lane's position within the row
+  const int R = MF ? 16 : 64 >> lg;                  // rows per group
+  const int rsub = MF ? (lane & 15) : lane >> lg;    // this lane's row within the group
+  const int li = MF ? (lane >> 4) : lane & (L - 1);  // this lane's position within the row
 
   // ---- this block's rows ----
   const int bid = blockIdx.x;
@@ -207,6 +234,7 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
   u32x4 xg[TT][XL];
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
+    if (MF && t >= ntok) break;  // MF: four token slots; only the slice's tokens are staged
     // a token past the slice's count gets an empty buffer: its x reads zeros
     const rsrc_t rx = make_rsrc(xb + (int64_t)t * cols, t < ntok ? (uint64_t)cols * 2 : 0);
 #pragma unroll
@@ -260,7 +288,7 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
   const int total_items = ngroups * passes;
   const int step_g = NW / passes, step_p = NW - step_g * passes;  // f += NW
   const int n_items = total_items > wave ? (total_items - wave + NW - 1) / NW : 0;
-  constexpr int P = gemv_ring(C);
+  constexpr int P = MF ? gemv_mf_ring(C) : gemv_ring(C);
   Chunk<B> ring[P][C];                                  // codes of the items in flight
   int l_item = 0;                                       // next item to load
   int l_pass = wave % passes, l_g = wave / passes;  // its pass and group
@@ -345,7 +373,8 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
   }
   const bool x_bf16 = a.x_bf16 != 0;
 #pragma unroll
-  for (int t = 0; t < TT; ++t)
+  for (int t = 0; t < TT; ++t) {
+    if (MF && t >= ntok) break;
 #pragma unroll
     for (int q = 0; q < XL; ++q) {
       const uint32_t o = (uint32_t)(tid + q * NT) * 16u;
@@ -353,6 +382,8 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
         *reinterpret_cast<u32x4*>(x_lds + t * XTOK + o + o / XCB * 16u) =
             x_bf16 ? bf16x8_to_f16x8(xg[t][q]) : xg[t][q];
     }
+  }
+  if (MF && tid == 0) *reinterpret_cast<u32x4*>(x_lds + TT * XTOK) = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
   for (int q = 0; q < SL; ++q) {
     const uint32_t o = (uint32_t)(tid + q * NT) * 16u;
@@ -367,105 +398,196 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
   if constexpr (LY::kGlobal) cbp = reinterpret_cast<const uint8_t*>(cb);
   else cbp = cb_lds;
   half2_t xv[TT][C][HX];
+  // MF: the x of a pass in the MFMA A operand.  A row m of the 16 x 32 A tile
+  // is (token m / 4, chunk position m % 4); lane (m, p) holds its 8 columns of
+  // k-slot group p, and only the lanes with p == m % 4 hold x (the rest read
+  // the zero slot), so each MFMA adds the four chunk positions' products into
+  // four separate output rows instead of summing them.
+  constexpr int KS = MF ? 2 * D : 1;  // k-steps (8 fp16 of A and B each) per chunk
+  u32x4 xa[MF ? C : 1][KS];
+  auto load_xa = [&](int pass) {
+    const int m = lane & 15, tk = m >> 2;
+    const bool mine = (m & 3) == (lane >> 4) && tk < ntok;
+    const int lim = min(PW, nq - pass * PW);
+#pragma unroll
+    for (int j = 0; j < (MF ? C : 1); ++j) {
+      const int qp = j * 4 + (lane >> 4);
+      const uint32_t src = (mine && qp < lim) ? (uint32_t)(tk * XTOK + (pass * PW + qp) * XSTRIDE)
+                                              : (uint32_t)(TT * XTOK);
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2)
+        xa[j][s2] = *reinterpret_cast<const u32x4*>(x_lds + src + (src == (uint32_t)(TT * XTOK) ? 0u : 16u * s2));
+    }
+  };
   uint32_t lane_sq[C], lane_ok[C];  // per pass: scale byte offset in the row, chunk-valid mask
   uint32_t lane_csh[C];             // per pass: bit offset of each chunk in its first word
   int cur_pass = -1;
   int pass = wave % passes, g = wave / passes;
+  uint32_t mf_sq[MF ? C : 1][4], mf_ok[MF ? C : 1][4];  // MF, per pass: scale byte offset in the row, chunk-valid mask
   auto item = [&](Chunk<B> (&rs)[C]) {
-    if (pass != cur_pass) {  // x of this pass into VGPRs (zeros past the slice)
-      cur_pass = pass;
-      const int lim = min(PW, nq - pass * PW);
+    if constexpr (MF) {
+      if (pass != cur_pass) {
+        load_xa(pass);
+        cur_pass = pass;
+        const int lim = min(PW, nq - pass * PW);
 #pragma unroll
-      for (int j = 0; j < C; ++j) {
-        const int qp = j * L + li;
-        const int q = pass * PW + qp;
-        const bool ok = qp < lim;
-        lane_sq[j] = ((uint32_t)(q0 + q) * 16u * D) / G * 2u;
-        lane_ok[j] = ok ? 0xffffffffu : 0u;
-        lane_csh[j] = chunk_shift<B>((uint32_t)(q0 + q));
+        for (int j = 0; j < C; ++j) {
 #pragma unroll
-        for (int t = 0; t < TT; ++t)
-#pragma unroll
-          for (int k = 0; k < HX / 4; ++k) {
-            u32x4 v = u32x4{0u, 0u, 0u, 0u};
-            if (ok) v = *reinterpret_cast<const u32x4*>(x_lds + t * XTOK + (uint32_t)q * XSTRIDE + 16u * k);
-            xv[t][j][4 * k + 0] = as_half2(v.x);
-            xv[t][j][4 * k + 1] = as_half2(v.y);
-            xv[t][j][4 * k + 2] = as_half2(v.z);
-            xv[t][j][4 * k + 3] = as_half2(v.w);
+          for (int i = 0; i < 4; ++i) {
+            const int qp = j * 4 + i;
+            mf_sq[j][i] = ((uint32_t)(q0 + pass * PW + qp) * 16u * D) / G * 2u;
+            mf_ok[j][i] = qp < lim ? 0xffffffffu : 0u;
           }
-      }
-    }
-
-    const int rb = g * R + rsub;                        // row within the block
-    const uint32_t srow = s_skew + (uint32_t)rb * (uint32_t)spr * 2u;  // the row's scales in s_lds
-    const uint32_t rowok = rb < brows ? 0xffffffffu : 0u;
-    float acc[TT];
-#pragma unroll
-    for (int t = 0; t < TT; ++t) acc[t] = 0.f;
-    // The gathers of step t + 1 are issued before the dot products of step
-    // t; a step is SB codes of one chunk (16 for d = 2, 8 for d = 4, 4 for
-    // d = 8), so the gathered entries in flight take 2 * SB * d / 2 = 32 VGPRs
-    // whatever d, and wide x-stationary tiles (5 chunks per lane) fit for d = 4
-    // too.  Everything is computed unconditionally; a chunk past the slice or
-    // a row past the block is dropped with a bit mask (a select would let the
-    // compiler branch around the gathers).
-    constexpr int S = (D == 2) ? 1 : (D == 4 ? 2 : 4);  // steps per chunk
-    constexpr int SB = 16 / S;                          // codes per step
-    static_assert(CPS % SB == 0, "a step lies inside one scale group");
-    //
-    // This slot's next item (u + P) is loaded chunk by chunk: once the last
-    // gather of chunk j is issued, the chunk's code registers are free and its
-    // load for the next item goes out at once.  The wave so keeps C chunk
-    // loads in flight, no more than loading whole items after the compute,
-    // but they leave during the compute rather than after it.
-    const NextLoad nl = load_begin();
-    Entry<D> e[2][SB];
-    auto issue = [&](int t, Entry<D> (&dst)[SB]) {
-      if (t % S == 0) align_chunk<B>(rs[t / S], lane_csh[t / S]);  // odd widths: shift the words into place
-#pragma unroll
-      for (int i = 0; i < SB; ++i) dst[i] = gather<D, B>(cbp, rs[t / S], (t % S) * SB + i, lane_off);
-      if (t % S == S - 1) {  // kept in place: the scheduler would sink it below later waits
-        __builtin_amdgcn_sched_barrier(0);
-        load_chunk(rs[t / S], t / S, nl);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    issue(0, e[0]);
-    float gs[TT][2];  // two chains per token for ILP, restarted per scale group
-#pragma unroll
-    for (int t = 0; t < TT; ++t) gs[t][0] = gs[t][1] = 0.f;
-#pragma unroll
-    for (int t = 0; t < C * S; ++t) {
-      if (t + 1 < C * S) issue(t + 1, e[(t + 1) & 1]);
-      const int j = t / S, b = t % S;
-#pragma unroll
-      for (int ii = 0; ii < SB; ++ii) {
-        const int i = b * SB + ii;
-#pragma unroll
-        for (int k = 0; k < D / 2; ++k)
-#pragma unroll
-          for (int u = 0; u < TT; ++u)
-            gs[u][(i * (D / 2) + k) & 1] =
-                dot2(e[t & 1][ii].v[k], xv[u][j][i * (D / 2) + k], gs[u][(i * (D / 2) + k) & 1]);
-      }
-      if (((b + 1) * SB) % CPS == 0) {  // the step ends scale group s2 of chunk j
-        const int s2 = (b + 1) * SB / CPS - 1;
-        const uint32_t keep = lane_ok[j] & rowok;
-        const uint16_t sbits = *reinterpret_cast<const uint16_t*>(s_lds + ((srow + lane_sq[j] + 2u * s2) & keep));
-        const float scale = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, half_bits_to_float(sbits)) & keep);
-#pragma unroll
-        for (int u = 0; u < TT; ++u) {
-          const float gsum = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, gs[u][0] + gs[u][1]) & keep);
-          acc[u] = __builtin_fmaf(gsum, scale, acc[u]);
-          gs[u][0] = gs[u][1] = 0.f;
+          lane_csh[j] = chunk_shift<B>((uint32_t)(q0 + pass * PW + j * 4 + li));
         }
       }
-    }
+      const int rb = g * 16 + rsub;                       // this lane's row within the block
+      const uint32_t srow = s_skew + (uint32_t)rb * (uint32_t)spr * 2u;
+      const uint32_t rowok = rb < brows ? 0xffffffffu : 0u;
+      constexpr int CPK = 8 / D;                          // codes per k-step
+      constexpr int FK = (G / 8 < KS) ? G / 8 : KS;       // k-steps per scale fold: a group or a chunk
+      const NextLoad nl = load_begin();
+      // B operand of k-step t: the entries of codes (t % KS) * CPK ... of
+      // chunk t / KS, gathered straight into the operand registers.  Once the
+      // last gather of a chunk is issued its code registers are free and the
+      // chunk of this slot's next item is requested.
+      auto issue = [&](int t) -> half8_t {
+        const int j = t / KS, s2 = t % KS;
+        if (s2 == 0) align_chunk<B>(rs[j], lane_csh[j]);
+        uint32_t w[4];
 #pragma unroll
-    for (int u = 0; u < TT; ++u) {
-      const float v = lane_group_sum(acc[u], lg);
-      if (li == L - 1 && rb < brows) pieces[(u * brows + rb) * passes + pass] = v;
+        for (int c = 0; c < CPK; ++c) {
+          const Entry<D> e = gather<D, B>(cbp, rs[j], s2 * CPK + c, lane_off);
+#pragma unroll
+          for (int k = 0; k < D / 2; ++k) w[c * (D / 2) + k] = as_u32(e.v[k]);
+        }
+        if (s2 == KS - 1) {
+          __builtin_amdgcn_sched_barrier(0);
+          load_chunk(rs[j], j, nl);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        return __builtin_bit_cast(half8_t, u32x4{w[0], w[1], w[2], w[3]});
+      };
+      float acc = 0.f;
+      half8_t bq[2];
+      bq[0] = issue(0);
+      // two accumulator chains (even and odd k-steps) per scale fold
+      float4_t dacc[2] = {float4_t{0.f, 0.f, 0.f, 0.f}, float4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int t = 0; t < C * KS; ++t) {
+        if (t + 1 < C * KS) bq[(t + 1) & 1] = issue(t + 1);
+        const int j = t / KS, s2 = t % KS;
+        const float4_t cin = (s2 % FK < 2) ? float4_t{0.f, 0.f, 0.f, 0.f} : dacc[s2 & 1];
+        dacc[s2 & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, xa[j][s2]), bq[t & 1], cin, 0, 0, 0);
+        if ((s2 + 1) % FK == 0) {  // dacc[i]: token lane / 16, row rsub, chunk position i, one scale group
+          const uint32_t f2 = 2u * (uint32_t)(s2 / FK);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t keep = mf_ok[j][i] & rowok;
+            const uint16_t sbits = *reinterpret_cast<const uint16_t*>(s_lds + ((srow + mf_sq[j][i] + f2) & keep));
+            const float scale = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, half_bits_to_float(sbits)) & keep);
+            acc = __builtin_fmaf(dacc[0][i] + dacc[1][i], scale, acc);
+          }
+        }
+      }
+      const int tk = lane >> 4;
+      if (tk < ntok && rb < brows) pieces[(tk * brows + rb) * passes + pass] = acc;
+    } else {
+      if (pass != cur_pass) {  // x of this pass into VGPRs (zeros past the slice)
+        cur_pass = pass;
+        const int lim = min(PW, nq - pass * PW);
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+          const int qp = j * L + li;
+          const int q = pass * PW + qp;
+          const bool ok = qp < lim;
+          lane_sq[j] = ((uint32_t)(q0 + q) * 16u * D) / G * 2u;
+          lane_ok[j] = ok ? 0xffffffffu : 0u;
+          lane_csh[j] = chunk_shift<B>((uint32_t)(q0 + q));
+#pragma unroll
+          for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int k = 0; k < HX / 4; ++k) {
+              u32x4 v = u32x4{0u, 0u, 0u, 0u};
+              if (ok) v = *reinterpret_cast<const u32x4*>(x_lds + t * XTOK + (uint32_t)q * XSTRIDE + 16u * k);
+              xv[t][j][4 * k + 0] = as_half2(v.x);
+              xv[t][j][4 * k + 1] = as_half2(v.y);
+              xv[t][j][4 * k + 2] = as_half2(v.z);
+              xv[t][j][4 * k + 3] = as_half2(v.w);
+            }
+        }
+      }
+
+      const int rb = g * R + rsub;                        // row within the block
+      const uint32_t srow = s_skew + (uint32_t)rb * (uint32_t)spr * 2u;  // the row's scales in s_lds
+      const uint32_t rowok = rb < brows ? 0xffffffffu : 0u;
+      float acc[TT];
+#pragma unroll
+      for (int t = 0; t < TT; ++t) acc[t] = 0.f;
+      // The gathers of step t + 1 are issued before the dot products of step
+      // t; a step is SB codes of one chunk (16 for d = 2, 8 for d = 4, 4 for
+      // d = 8), so the gathered entries in flight take 2 * SB * d / 2 = 32 VGPRs
+      // whatever d, and wide x-stationary tiles (5 chunks per lane) fit for d = 4
+      // too.  Everything is computed unconditionally; a chunk past the slice or
+      // a row past the block is dropped with a bit mask (a select would let the
+      // compiler branch around the gathers).
+      constexpr int S = (D == 2) ? 1 : (D == 4 ? 2 : 4);  // steps per chunk
+      constexpr int SB = 16 / S;                          // codes per step
+      static_assert(CPS % SB == 0, "a step lies inside one scale group");
+      //
+      // This slot's next item (u + P) is loaded chunk by chunk: once the last
+      // gather of chunk j is issued, the chunk's code registers are free and its
+      // load for the next item goes out at once.  The wave so keeps C chunk
+      // loads in flight, no more than loading whole items after the compute,
+      // but they leave during the compute rather than after it.
+      const NextLoad nl = load_begin();
+      Entry<D> e[2][SB];
+      auto issue = [&](int t, Entry<D> (&dst)[SB]) {
+        if (t % S == 0) align_chunk<B>(rs[t / S], lane_csh[t / S]);  // odd widths: shift the words into place
+#pragma unroll
+        for (int i = 0; i < SB; ++i) dst[i] = gather<D, B>(cbp, rs[t / S], (t % S) * SB + i, lane_off);
+        if (t % S == S - 1) {  // kept in place: the scheduler would sink it below later waits
+          __builtin_amdgcn_sched_barrier(0);
+          load_chunk(rs[t / S], t / S, nl);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      issue(0, e[0]);
+      float gs[TT][2];  // two chains per token for ILP, restarted per scale group
+#pragma unroll
+      for (int t = 0; t < TT; ++t) gs[t][0] = gs[t][1] = 0.f;
+#pragma unroll
+      for (int t = 0; t < C * S; ++t) {
+        if (t + 1 < C * S) issue(t + 1, e[(t + 1) & 1]);
+        const int j = t / S, b = t % S;
+#pragma unroll
+        for (int ii = 0; ii < SB; ++ii) {
+          const int i = b * SB + ii;
+#pragma unroll
+          for (int k = 0; k < D / 2; ++k)
+#pragma unroll
+            for (int u = 0; u < TT; ++u)
+              gs[u][(i * (D / 2) + k) & 1] =
+                  dot2(e[t & 1][ii].v[k], xv[u][j][i * (D / 2) + k], gs[u][(i * (D / 2) + k) & 1]);
+        }
+        if (((b + 1) * SB) % CPS == 0) {  // the step ends scale group s2 of chunk j
+          const int s2 = (b + 1) * SB / CPS - 1;
+          const uint32_t keep = lane_ok[j] & rowok;
+          const uint16_t sbits = *reinterpret_cast<const uint16_t*>(s_lds + ((srow + lane_sq[j] + 2u * s2) & keep));
+          const float scale = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, half_bits_to_float(sbits)) & keep);
+#pragma unroll
+          for (int u = 0; u < TT; ++u) {
+            const float gsum = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, gs[u][0] + gs[u][1]) & keep);
+            acc[u] = __builtin_fmaf(gsum, scale, acc[u]);
+            gs[u][0] = gs[u][1] = 0.f;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < TT; ++u) {
+        const float v = lane_group_sum(acc[u], lg);
+        if (li == L - 1 && rb < brows) pieces[(u * brows + rb) * passes + pass] = v;
+      }
     }
     load_end();
     g += step_g;
@@ -664,7 +786,7 @@ LaneTiling plan_tiling(int nq, int max_c, int waves, bool cu_bound) {
   return best;
 }
 
-template <int D, int B, int G, int C, int XS, bool MOE, int TT>
+template <int D, int B, int G, int C, int XS, bool MOE, int TT, bool MF>
 hipError_t gemv_launch_c(const GemvArgs& a, dim3 grid, hipStream_t s) {
   const uint16_t* xs = MOE ? a.x : a.x + (int64_t)a.tok0 * a.cols;  // fp16 or bf16: 2 bytes a value
   const int pw = (a.nq + a.passes - 1) / a.passes;
@@ -672,20 +794,20 @@ hipError_t gemv_launch_c(const GemvArgs& a, dim3 grid, hipStream_t s) {
     return hipErrorInvalidValue;
   const uint32_t shape = (uint32_t)a.nq | ((uint32_t)a.lanes_log2 << 12) | ((uint32_t)a.passes << 15) |
                          ((uint32_t)pw << 23);
-  hipLaunchKernelGGL((vq_gemv_kernel<D, B, G, C, XS, MOE, TT>), grid, dim3(kGemvThreads), 0, s, a.codes, a.codebook,
+  hipLaunchKernelGGL((vq_gemv_kernel<D, B, G, C, XS, MOE, TT, MF>), grid, dim3(kGemvThreads), 0, s, a.codes, a.codebook,
                      a.scales, xs, a.rows, a.rows_base, a.rows_extra, a.q0, a.spr, shape, a);
   return hipGetLastError();
 }
 
-template <int D, int B, int G, int XS, bool MOE, int TT>
+template <int D, int B, int G, int XS, bool MOE, int TT, bool MF = false>
 hipError_t gemv_launch(const GemvArgs& a, int C, dim3 grid, hipStream_t s) {
-  constexpr int MC = gemv_max_c(D, B, TT);
+  constexpr int MC = MF ? gemv_mf_max_c(D) : gemv_max_c(D, B, TT);
   switch (C) {
-    case 1: return gemv_launch_c<D, B, G, 1, XS, MOE, TT>(a, grid, s);
-    case 2: if constexpr (MC >= 2) return gemv_launch_c<D, B, G, 2, XS, MOE, TT>(a, grid, s); break;
-    case 3: if constexpr (MC >= 3) return gemv_launch_c<D, B, G, 3, XS, MOE, TT>(a, grid, s); break;
-    case 4: if constexpr (MC >= 4) return gemv_launch_c<D, B, G, 4, XS, MOE, TT>(a, grid, s); break;
-    case 5: if constexpr (MC >= 5) return gemv_launch_c<D, B, G, 5, XS, MOE, TT>(a, grid, s); break;
+    case 1: return gemv_launch_c<D, B, G, 1, XS, MOE, TT, MF>(a, grid, s);
+    case 2: if constexpr (MC >= 2) return gemv_launch_c<D, B, G, 2, XS, MOE, TT, MF>(a, grid, s); break;
+    case 3: if constexpr (MC >= 3) return gemv_launch_c<D, B, G, 3, XS, MOE, TT, MF>(a, grid, s); break;
+    case 4: if constexpr (MC >= 4) return gemv_launch_c<D, B, G, 4, XS, MOE, TT, MF>(a, grid, s); break;
+    case 5: if constexpr (MC >= 5) return gemv_launch_c<D, B, G, 5, XS, MOE, TT, MF>(a, grid, s); break;
     default: break;
   }
   return hipErrorInvalidValue;
@@ -697,8 +819,53 @@ hipError_t gemv_launch(const GemvArgs& a, int C, dim3 grid, hipStream_t s) {
 // calls run one grid slice (blockIdx.y) per token, or per two tokens when
 // there are several and a row's x fits one 16 KiB slice; routed calls one per
 // (token, slot) pair.
+// Matrix-core GEMV (MF): whole rows in at most kGemvWaves passes of up to
+// 4 * C chunks (L = 4 lanes per row, 16 rows per group), up to four tokens per
+// grid slice, for dense calls of two or more tokens (gemv_mf_takes).  Returns
+// false when the call is not one it takes.
+template <int D, int B, int G, bool MOE>
+bool gemv_run_mf(GemvArgs a, int P, int ycount, hipStream_t s, hipError_t* err) {
+  if constexpr (MOE) {
+    return false;
+  } else {
+    if (!gemv_mf_takes(a.rows, a.cols, D, ycount, num_cus())) return false;
+    constexpr int MC = gemv_mf_max_c(D);
+    int passes = 1;
+    while (passes <= kGemvWaves && (P + passes - 1) / passes > 4 * MC) passes *= 2;
+    if (passes > kGemvWaves) return false;
+    const int pw = (P + passes - 1) / passes;
+    const int C = (pw + 3) / 4;
+    a.q0 = 0;
+    a.nq = P;
+    a.accumulate = 0;
+    a.lanes_log2 = 2;
+    a.passes = passes;
+    const int ny = (ycount + kGemvMfTokens - 1) / kGemvMfTokens;
+    const int blocks_fill = std::max(1, num_cus() / std::max(1, ny));
+    const int64_t by_scales = std::max<int64_t>(1, (kGemvScaleBytes - 16) / (2 * (int64_t)a.spr));
+    const int64_t by_pieces = std::max<int64_t>(1, kGemvPieces / ((int64_t)passes * kGemvMfTokens));
+    const int unit = a.epi == kEpiSwiglu ? 2 : 1;
+    const int64_t rows_max = std::max<int64_t>(unit, std::min(by_scales, by_pieces) / unit * unit);
+    const int64_t units = a.rows / unit;
+    const int64_t blocks = std::min<int64_t>(units, std::max<int64_t>(blocks_fill, (a.rows + rows_max - 1) / rows_max));
+    a.rows_base = (int)(units / blocks) * unit;
+    a.rows_extra = (int)(units - units / blocks * blocks) | (unit == 2 ? 1 << 30 : 0);
+    for (int y0 = 0; y0 < ny; y0 += 65535) {
+      const int yc = std::min(65535, ny - y0);
+      a.tok0 = y0 * kGemvMfTokens;
+      *err = gemv_launch<D, B, G, 2, false, kGemvMfTokens, true>(a, C, dim3((unsigned)blocks, (unsigned)yc), s);
+      if (*err != hipSuccess) break;
+    }
+    return true;
+  }
+}
+
 template <int D, int B, int G, bool MOE>
 hipError_t gemv_run(GemvArgs a, int P, int ycount, hipStream_t s) {
+  {
+    hipError_t e = hipSuccess;
+    if (gemv_run_mf<D, B, G, MOE>(a, P, ycount, s, &e)) return e;
+  }
   const int slice_two = 2 * 8192 / (32 * D);            // chunks of a 16 KiB x slice
   const bool two = !MOE && ycount >= 2 && P <= slice_two;
   const int TT = two ? 2 : 1;

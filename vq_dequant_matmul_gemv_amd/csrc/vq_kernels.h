@@ -52,6 +52,16 @@ hipError_t launch_gemv(const TensorView& w, const IoSpec& io, const void* x, int
 
 hipError_t launch_gemm(const TensorView& w, const IoSpec& io, const void* x, int T, void* y, hipStream_t s);
 
+// The matrix-core GEMV (vq_gemv_impl.h, MF) takes dense calls of two or more
+// tokens whose rows fit its passes (d = 2: 5120 columns, d = 4: 6144, d = 8:
+// 4096) and whose rows give every CU at least one 16-row group.
+__host__ __device__ inline int gemv_mf_max_cols(int d) { return d == 2 ? 5120 : (d == 4 ? 6144 : 4096); }
+inline bool gemv_mf_takes(int rows, int cols, int d, int T, int cus) {
+  return T >= 2 && cols <= gemv_mf_max_cols(d) && rows >= 16 * cus;
+}
+// Compute units of the current device (cached on first use).
+int device_cus();
+
 // Zero `bytes` (a multiple of 4) at p, on the stream, with a kernel (so it can
 // sit in a captured graph).
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
