@@ -94,8 +94,9 @@ def copy_probe():
 
 def _pmc_value(fname, counter, kernel_prefix, grid=None):
     """Average per-dispatch value of `counter` for the first kernel whose
-    name starts with kernel_prefix (and whose grid is `grid`, when given),
-    from a profsum pmc summary."""
+    name starts with kernel_prefix -- a plain prefix, or a compiled regular
+    expression matched at the start of the line -- (and whose grid is `grid`,
+    when given), from a profsum pmc summary."""
     path = os.path.join(PROFILES, fname)
     if not os.path.exists(path):
         return None, None
@@ -104,7 +105,9 @@ def _pmc_value(fname, counter, kernel_prefix, grid=None):
         for line in fh:
             if line.startswith("kernel source digest:"):
                 digest = line.split(":", 1)[1].strip()
-            if line.startswith(kernel_prefix) and (grid is None or f" grid={grid} " in line):
+            hit = (kernel_prefix.match(line) is not None) if hasattr(kernel_prefix, "match") \
+                else line.startswith(kernel_prefix)
+            if hit and (grid is None or f" grid={grid} " in line):
                 for part in line.split():
                     if part.startswith(counter + "="):
                         return float(part.split("=", 1)[1]), digest
@@ -134,10 +137,12 @@ SWEEP_REPLICAS = 16                                   # 16 x 25 MB per matrix: e
 
 def sweep_rooflines(profile_only=None):
     """Config-4 kernels on one GPU: W_A [17408][5120] and W_B [5120][17408],
-    d=4 K=256 g=64, the GEMV at T = 1 (HBM-bound) and the GEMM at T = 4096
+    d=4 K=256 g=64, vq_gemv at T = 1 and T = 4 (HBM-bound; at T = 4 the
+    matrix-core GEMV on A, the MFMA GEMM on B) and the GEMM at T = 4096
     (MFMA-bound).  Per-launch durations from bursts of back-to-back launches
     in one graph (16 GEMVs / 4 GEMMs, rotating over weight replicas), timed
     with events on the launch stream, median of 5 bursts."""
+    import re
     import torch
     from vq_dequant_matmul_gemv_amd import binding, synth
     dev = torch.device("cuda", 0)
@@ -150,21 +155,24 @@ def sweep_rooflines(profile_only=None):
                                           spec.cols, spec.d, spec.log2_k, spec.group)
                          for _ in range(SWEEP_REPLICAS - 1)]
         x1 = torch.from_numpy(synth.activations((1, spec.cols), SWEEP, name, "x", 1)).to(dev)
+        x4 = torch.from_numpy(synth.activations((4, spec.cols), SWEEP, name, "x", 4)).to(dev)
+        y4 = torch.empty((4, spec.rows), dtype=torch.float32, device=dev)
         xT = torch.from_numpy(synth.activations((4096, spec.cols), SWEEP, name, "x", 4096)).to(dev)
         y1 = torch.empty((1, spec.rows), dtype=torch.float32, device=dev)
         yT = torch.empty((4096, spec.rows), dtype=torch.float32, device=dev)
         gemv = [lambda w=reps[i % SWEEP_REPLICAS]: binding.gemv(w, x1, y1) for i in range(16)]
+        gemv4 = [lambda w=reps[i % SWEEP_REPLICAS]: binding.gemv(w, x4, y4) for i in range(16)]
         gemm = [lambda w=reps[i % SWEEP_REPLICAS]: binding.gemm(w, xT, yT) for i in range(4)]
         if profile_only:
-            for c in gemv[:4] + gemm[:2]:
+            for c in gemv[:4] + gemv4[:4] + gemm[:2]:
                 c()
             torch.cuda.synchronize()
             continue
-        for c in gemv + gemm:   # warm
+        for c in gemv + gemv4 + gemm:   # warm
             c()
         torch.cuda.synchronize()
         res = {}
-        for key, calls in (("gemv_T1", gemv), ("gemm_T4096", gemm)):
+        for key, calls in (("gemv_T1", gemv), ("gemv_T4", gemv4), ("gemm_T4096", gemm)):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for c in calls:
@@ -181,23 +189,32 @@ def sweep_rooflines(profile_only=None):
             res[key] = sorted(times)[2]
             del g
         nb = tensor_bytes(spec, 1)
+        nb4 = tensor_bytes(spec, 4)
         flops = 2.0 * 4096 * spec.rows * spec.cols
         gbps = nb / res["gemv_T1"] / 1e9
+        gbps4 = nb4 / res["gemv_T4"] / 1e9
         tflops = flops / res["gemm_T4096"] / 1e12
         out[f"{name}_{spec.rows}x{spec.cols}"] = {
             "gemv_T1": {"bound": "hbm", "us": round(res["gemv_T1"] * 1e6, 2), "achieved": round(gbps, 2),
                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                         "algorithmic_bytes": nb,
-                        "traffic": measured_traffic("vq_gemv_kernel<4, 8, 64", SWEEP_TAG + "_" + name)},
+                        "traffic": measured_traffic(re.compile(r"vq_gemv_kernel<4, 8, 64, \d+, \d+, false, 1, false>"),
+                                                    SWEEP_TAG + "_" + name)},
+            "gemv_T4": {"bound": "hbm", "us": round(res["gemv_T4"] * 1e6, 2), "achieved": round(gbps4, 2),
+                        "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps4 / HBM_PEAK_GBPS, 4),
+                        "algorithmic_bytes": nb4,
+                        "traffic": measured_traffic(re.compile(r"vq_gemv_kernel<4, 8, 64, \d+, \d+, false, 4, true>"),
+                                                    SWEEP_TAG + "_" + name)},
             "gemm_T4096": {"bound": "mfma", "us": round(res["gemm_T4096"] * 1e6, 2), "achieved": round(tflops, 2),
                            "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
                            "algorithmic_bytes": tensor_bytes(spec, 4096),
-                           "traffic": measured_traffic("vq_gemm_kernel<4, 8, 64", SWEEP_TAG + "_" + name)}}
-        del reps, base, xT, yT
+                           "traffic": measured_traffic("vq_gemm_kernel<4, 8, 64, GemmShape<8, 2, 4>",
+                                                       SWEEP_TAG + "_" + name)}}
+        del reps, base, xT, yT, x4, y4
         torch.cuda.empty_cache()
     if profile_only:
-        print(f"profile-sweep {profile_only}: 4 GEMVs (T=1) and 2 GEMMs (T=4096)", flush=True)
+        print(f"profile-sweep {profile_only}: 4 GEMVs (T=1), 4 GEMVs (T=4) and 2 GEMMs (T=4096)", flush=True)
     return out
 
 
@@ -423,8 +440,9 @@ def configs_report(only=""):
         dense("gemv_1024", "w", W["gemv_1024"]["tensors"]["w"], [1], [], ("gemv_1024", "w"))
     wl = "dense_mlp_5120x17408_d2k256"
     for n in ("gate", "up", "down") if keep(wl) else ():
-        # T = 2: a two-token verify step; both kernels timed for the crossover
-        dense(wl, n, W[wl]["tensors"][n], [1, 2], [2, 2048], (wl, n))
+        # T = 2: a two-token verify step, T = 4 a four-token one; both kernels
+        # timed for the crossover
+        dense(wl, n, W[wl]["tensors"][n], [1, 2, 4], [2, 4, 2048], (wl, n))
     if keep(wl):
         stacked_pair(wl, "gate+up (two-expert stack, ids {0,1})", W[wl]["tensors"]["gate"],
                      ((wl, "gate"), (wl, "up")))
@@ -441,7 +459,7 @@ def configs_report(only=""):
                    (wl, tier, idx))
     wl = "sweep_17408x5120_d4k256"
     for n in ("A", "B") if keep(wl) else ():
-        Ts = sorted(set(W[wl]["tokens"]) | {2})
+        Ts = sorted(set(W[wl]["tokens"]) | {2, 3})
         dense(wl, n, W[wl]["tensors"][n], Ts, Ts, (wl, n))
     if keep(wl):
         dequant_row(wl, "A", W[wl]["tensors"]["A"], (wl, "A"))
