@@ -1,6 +1,7 @@
 """GPU parity of the matrix-core GEMV: dense vq_gemv calls of two or more
-tokens on matrices with at least one 16-row group per CU and rows short
-enough for its passes (d = 2: 5120 columns, d = 4: 6144, d = 8: 4096).
+tokens on matrices with at least one 16-row group per CU; rows longer than
+one block's passes (d = 2: 5120 columns, d = 4: 6144, d = 8: 4096) run as
+column slices added into y.
 
 The codebook entries go straight into the MFMA B operand and the x of four
 chunk positions into a block-diagonal A operand, so every output needs the
@@ -61,6 +62,24 @@ def test_mf_gemv_widths_passes_and_slices(rows, cols, d, b, g, Ts):
         assert row_rel_err(y, _ref(arrs, spec, x)) <= TOL, T
 
 
+@pytest.mark.parametrize("rows,cols,d,b,g,Ts", [
+    (ROWS, 17408, 4, 8, 64, (2, 4)),       # 272 chunks: 3 column slices of 91, 90, 91
+    (ROWS, 10240, 2, 12, 128, (3,)),       # 320 chunks: 2 slices of 160
+    (4096, 8192, 8, 8, 64, (4, 7)),        # 64 chunks: 2 slices of 32; 32M weights, 2 token slices at T = 7
+])
+def test_mf_gemv_long_rows_in_column_slices(rows, cols, d, b, g, Ts):
+    """Rows longer than one block's passes: column slices side by side in
+    one launch, each staging its own x and scale groups (slices starting
+    inside a scale group included), added into a zeroed y."""
+    from vq_dequant_matmul_gemv_amd import binding
+    spec, arrs, w = _case(d, b, g, rows, cols, ("mf-long", rows, cols, d, b, g))
+    for T in Ts:
+        x = synth.activations((T, cols), "mf-long", rows, cols, T)
+        announce("mf-gemv-long", rows, cols, d, b, g, T)
+        y = binding.gemv(w, to_dev(x)).cpu().numpy()
+        assert row_rel_err(y, _ref(arrs, spec, x)) <= TOL, T
+
+
 @pytest.mark.parametrize("d,b,g", [(2, 8, 64), (4, 8, 64), (8, 12, 128)])
 def test_mf_gemv_io_types_and_swiglu(d, b, g):
     """bf16 x, fp16 / bf16 y and the SwiGLU step over row pairs (2i, 2i + 1)."""
@@ -79,7 +98,7 @@ def test_mf_gemv_io_types_and_swiglu(d, b, g):
 
 
 def test_mf_gemv_repeat_runs_bit_identical():
-    """No atomics: two runs give the same bits."""
+    """Rows in one slice: no atomics, two runs give the same bits."""
     from vq_dequant_matmul_gemv_amd import binding
     spec, arrs, w = _case(4, 8, 64, ROWS, 2048, ("mf-rep",))
     x = to_dev(synth.activations((4, 2048), "mf-rep"))

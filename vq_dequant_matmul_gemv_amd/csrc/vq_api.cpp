@@ -231,9 +231,10 @@ vq_status vq_dequant(const vq_tensor* w, int32_t expert, uint16_t* w_out, void* 
 // scalar GEMV, and the rest wins up to T = 2 (two tokens per slice;
 // 17408x5120 and 5120x17408, d = 2 and 4: 15.9-18.6 us against 17.3-21.7 us
 // for the GEMM).
-static int gemv_token_limit(const vqmi::TensorView& v) {
+static int gemv_token_limit(const vqmi::TensorView& v, const vqmi::IoSpec& io) {
   const bool small = (int64_t)v.rows * v.cols <= (int64_t)16 << 20;
-  if (vqmi::gemv_mf_takes(v.rows, v.cols, v.d, 2, vqmi::device_cus())) return small ? 8 : 4;
+  const bool plain_out = io.epi == vqmi::kEpiNone && io.y_kind == vqmi::kOutF32;
+  if (vqmi::gemv_mf_takes(v.rows, v.cols, v.d, 2, vqmi::device_cus(), plain_out)) return small ? 8 : 4;
   if (small) return 6;
   if (v.d == 8) return 4;
   return 2;
@@ -256,7 +257,7 @@ static vq_status dense_call(const vq_tensor* w, const vq_io* io, const void* x, 
   if (T == 0) return VQ_OK;
   st = check_xy(x, y, "y");
   if (st != VQ_OK) return st;
-  if (!gemv || T > gemv_token_limit(v))  // above the crossover the MFMA kernel is faster
+  if (!gemv || T > gemv_token_limit(v, ios))  // above the crossover the MFMA kernel is faster
     return hip_status(vqmi::launch_gemm(v, ios, x, T, y, (hipStream_t)stream),
                       gemv ? "vq_gemv (MFMA path) launch" : "vq_gemm launch");
   return hip_status(vqmi::launch_gemv(v, ios, x, T, y, nullptr, 0, 0, (hipStream_t)stream), "vq_gemv launch");

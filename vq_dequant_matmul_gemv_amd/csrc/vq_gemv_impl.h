@@ -79,6 +79,7 @@ struct GemvArgs {
   int rows, cols, wr, spr;
   int rows_base, rows_extra;  // block b owns rows_base (+1 if b < rows_extra) rows
   int q0, nq;             // column slice of this launch, in 16-code chunks
+  int p_total;            // MF: chunks per row (blockIdx.z slices of nq chunks each cover them)
   int lanes_log2;         // L = 1 << lanes_log2 lanes per row (2..5)
   int passes;             // ceil(nq / (L * C))
   int accumulate;         // add into y (column slices after the first)
@@ -150,7 +151,7 @@ template <int D, int B, int G, int C, int XS, bool MOE, int TT, bool MF>
 __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
     const uint32_t* __restrict__ codes_in, const uint16_t* __restrict__ cb_in,
     const uint16_t* __restrict__ scales_in, const uint16_t* __restrict__ xs, int rows, int rows_base,
-    int rows_extra, int q0, int spr, uint32_t shape, GemvArgs a) {
+    int rows_extra, int q0_arg, int spr, uint32_t shape, GemvArgs a) {
   using LY = CodebookLayout<D, B>;
   constexpr int NSC = (16 * D > G) ? (16 * D / G) : 1;  // scales per chunk
   constexpr int CPS = 16 / NSC;                          // codes per scale in a chunk
@@ -176,7 +177,11 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nq = (int)(shape & 0xfffu);
+  // MF: blockIdx.z is a column slice of nq chunks (added atomically into y
+  // when there are several)
+  const int nq_s = (int)(shape & 0xfffu);
+  const int q0 = q0_arg + (MF ? (int)blockIdx.z * nq_s : 0);
+  const int nq = MF ? min(nq_s, a.p_total - q0) : nq_s;
   const int lg = (int)((shape >> 12) & 0x7u);
   const int passes = (int)((shape >> 15) & 0xffu);
   const int PW = (int)(shape >> 23);       // chunks per pass; the last pass may hold fewer
@@ -255,25 +260,48 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
     }
   }
   // scale rows [brow0, brow0 + brows), read as 16-byte pieces from a 16-byte
-  // boundary at or below the first scale
+  // boundary at or below the first scale.  MF: only the groups of the
+  // block's column slice, [sg0, sg0 + sgn) of each row, in LDS rows of spp
+  // pieces (each read from the 16-byte boundary at or below the row's first
+  // scale of the slice).
   const uint64_t s_first = (uint64_t)brow0 * spr * 2u;
   const uint32_t s_skew = (uint32_t)(s_first & 15u);
   const uint32_t s_span = (uint32_t)brows * (uint32_t)spr * 2u + s_skew;
   const uint32_t s_avail = (uint32_t)((uint64_t)rows * spr * 2u - (s_first - s_skew));  // to the tensor's end
-  const rsrc_t rsb = make_rsrc(reinterpret_cast<const uint8_t*>(scales) + (s_first - s_skew), s_avail);
+  const uint32_t sg0 = MF ? (uint32_t)(q0 * 16 * D) / G : 0u;
+  const uint32_t spp = MF ? (((uint32_t)((q0 + nq) * 16 * D - 1) / G + 1u - sg0) * 2u + 30u) / 16u : 0u;
+  const uint32_t s_total = (uint32_t)((uint64_t)rows * spr * 2u);  // bytes of this expert's scales
+  const rsrc_t rsb = MF ? make_rsrc(scales, s_total)
+                        : make_rsrc(reinterpret_cast<const uint8_t*>(scales) + (s_first - s_skew), s_avail);
   constexpr int SL = (kGemvScaleBytes + NT * 16 - 1) / (NT * 16);
   u32x4 sg[SL];
 #pragma unroll
   for (int q = 0; q < SL; ++q) {
-    const uint32_t o = (uint32_t)(tid + q * NT) * 16u;
-    sg[q] = buf_load_b128(rsb, (o < s_span && o + 16u <= s_avail) ? o : kOutOfRange);
-    if (o < s_span && o + 16u > s_avail) {  // the tensor ends inside this piece: 2-byte loads
+    uint32_t o, lim;
+    bool live;
+    if constexpr (MF) {
+      const uint32_t i = (uint32_t)(tid + q * NT);
+      const uint32_t r = i / spp, k = i - r * spp;
+      live = r < (uint32_t)brows && i * 16u < (uint32_t)kGemvScaleBytes;
+      o = ((((uint32_t)(brow0 + (int)r) * (uint32_t)spr + sg0) * 2u) & ~15u) + 16u * k;
+      lim = s_total;
+    } else {
+      o = (uint32_t)(tid + q * NT) * 16u;
+      live = o < s_span;
+      lim = s_avail;
+    }
+    sg[q] = buf_load_b128(rsb, (live && o + 16u <= lim) ? o : kOutOfRange);
+    if (live && o + 16u > lim) {  // the tensor ends inside this piece: 2-byte loads
       uint32_t h[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) h[k] = buf_load_b16(rsb, o + 2u * k < s_avail ? o + 2u * k : kOutOfRange);
+      for (int k = 0; k < 8; ++k) h[k] = buf_load_b16(rsb, o + 2u * k < lim ? o + 2u * k : kOutOfRange);
       sg[q] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
     }
   }
+  // MF: byte offset in s_lds of row rb's first staged scale
+  auto mf_srow = [&](int rb) -> uint32_t {
+    return (uint32_t)rb * spp * 16u + ((((uint32_t)(brow0 + rb) * (uint32_t)spr + sg0) * 2u) & 15u);
+  };
 
   // Every wave's small loads enter the CU's in-order memory queue ahead of
   // any wave's code loads (a plain s_barrier: it waits for no load).
@@ -435,14 +463,14 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int qp = j * 4 + i;
-            mf_sq[j][i] = ((uint32_t)(q0 + pass * PW + qp) * 16u * D) / G * 2u;
+            mf_sq[j][i] = (((uint32_t)(q0 + pass * PW + qp) * 16u * D) / G - sg0) * 2u;
             mf_ok[j][i] = qp < lim ? 0xffffffffu : 0u;
           }
           lane_csh[j] = chunk_shift<B>((uint32_t)(q0 + pass * PW + j * 4 + li));
         }
       }
       const int rb = g * 16 + rsub;                       // this lane's row within the block
-      const uint32_t srow = s_skew + (uint32_t)rb * (uint32_t)spr * 2u;
+      const uint32_t srow = mf_srow(rb);
       const uint32_t rowok = rb < brows ? 0xffffffffu : 0u;
       constexpr int CPK = 8 / D;                          // codes per k-step
       constexpr int FK = (G / 8 < KS) ? G / 8 : KS;       // k-steps per scale fold: a group or a chunk
@@ -631,6 +659,9 @@ items_done:
           float* yc = reinterpret_cast<float*>(a.y) + ybase + brow0;
           for (int r = tid; r < brows; r += NT) atomicAdd(yc + r, wgt * row_sum(r));
         }
+      } else if (MF && gridDim.z > 1) {  // one of several column slices in this launch (fp32 y, zeroed)
+        float* yf = reinterpret_cast<float*>(a.y) + ybase + brow0;
+        for (int r = tid; r < brows; r += NT) atomicAdd(yf + r, row_sum(r));
       } else if (a.accumulate) {  // a column slice after the first (fp32 y)
         float* yf = reinterpret_cast<float*>(a.y) + ybase + brow0;
         for (int r = tid; r < brows; r += NT) yf[r] += row_sum(r);
@@ -819,30 +850,38 @@ hipError_t gemv_launch(const GemvArgs& a, int C, dim3 grid, hipStream_t s) {
 // calls run one grid slice (blockIdx.y) per token, or per two tokens when
 // there are several and a row's x fits one 16 KiB slice; routed calls one per
 // (token, slot) pair.
-// Matrix-core GEMV (MF): whole rows in at most kGemvWaves passes of up to
-// 4 * C chunks (L = 4 lanes per row, 16 rows per group), up to four tokens per
-// grid slice, for dense calls of two or more tokens (gemv_mf_takes).  Returns
-// false when the call is not one it takes.
+// Matrix-core GEMV (MF): rows in at most kGemvWaves passes of up to 4 * C
+// chunks (L = 4 lanes per row, 16 rows per group), up to four tokens per grid
+// slice, for dense calls of two or more tokens (gemv_mf_takes).  Longer rows
+// are split into column slices run side by side (blockIdx.z), each staging
+// only its own x and scales, their sums added atomically into a zeroed fp32 y.
+// Returns false when the call is not one it takes.
 template <int D, int B, int G, bool MOE>
 bool gemv_run_mf(GemvArgs a, int P, int ycount, hipStream_t s, hipError_t* err) {
   if constexpr (MOE) {
     return false;
   } else {
-    if (!gemv_mf_takes(a.rows, a.cols, D, ycount, num_cus())) return false;
+    const bool plain_out = a.epi == kEpiNone && a.y_kind == kOutF32;
+    if (!gemv_mf_takes(a.rows, a.cols, D, ycount, num_cus(), plain_out)) return false;
     constexpr int MC = gemv_mf_max_c(D);
+    const int n_sl = (P + kGemvWaves * 4 * MC - 1) / (kGemvWaves * 4 * MC);
+    const int per = (P + n_sl - 1) / n_sl;                // chunks per column slice
     int passes = 1;
-    while (passes <= kGemvWaves && (P + passes - 1) / passes > 4 * MC) passes *= 2;
-    if (passes > kGemvWaves) return false;
-    const int pw = (P + passes - 1) / passes;
+    while ((per + passes - 1) / passes > 4 * MC) passes *= 2;
+    const int pw = (per + passes - 1) / passes;
     const int C = (pw + 3) / 4;
     a.q0 = 0;
-    a.nq = P;
+    a.nq = per;
+    a.p_total = P;
     a.accumulate = 0;
     a.lanes_log2 = 2;
     a.passes = passes;
     const int ny = (ycount + kGemvMfTokens - 1) / kGemvMfTokens;
-    const int blocks_fill = std::max(1, num_cus() / std::max(1, ny));
-    const int64_t by_scales = std::max<int64_t>(1, (kGemvScaleBytes - 16) / (2 * (int64_t)a.spr));
+    const int blocks_fill = std::max(1, num_cus() / std::max(1, ny * n_sl));
+    // a block stages the scale groups of its slice, up to two partial ones included
+    const int64_t groups = ((int64_t)per * 16 * D + G - 1) / G + 1;
+    const int64_t spp = (groups * 2 + 30) / 16;
+    const int64_t by_scales = std::max<int64_t>(1, kGemvScaleBytes / (16 * spp));
     const int64_t by_pieces = std::max<int64_t>(1, kGemvPieces / ((int64_t)passes * kGemvMfTokens));
     const int unit = a.epi == kEpiSwiglu ? 2 : 1;
     const int64_t rows_max = std::max<int64_t>(unit, std::min(by_scales, by_pieces) / unit * unit);
@@ -850,10 +889,14 @@ bool gemv_run_mf(GemvArgs a, int P, int ycount, hipStream_t s, hipError_t* err) 
     const int64_t blocks = std::min<int64_t>(units, std::max<int64_t>(blocks_fill, (a.rows + rows_max - 1) / rows_max));
     a.rows_base = (int)(units / blocks) * unit;
     a.rows_extra = (int)(units - units / blocks * blocks) | (unit == 2 ? 1 << 30 : 0);
+    if (n_sl > 1) {  // the slices add into y
+      *err = launch_zero(a.y, (size_t)ycount * a.rows * sizeof(float), s);
+      if (*err != hipSuccess) return true;
+    }
     for (int y0 = 0; y0 < ny; y0 += 65535) {
       const int yc = std::min(65535, ny - y0);
       a.tok0 = y0 * kGemvMfTokens;
-      *err = gemv_launch<D, B, G, 2, false, kGemvMfTokens, true>(a, C, dim3((unsigned)blocks, (unsigned)yc), s);
+      *err = gemv_launch<D, B, G, 2, false, kGemvMfTokens, true>(a, C, dim3((unsigned)blocks, (unsigned)yc, (unsigned)n_sl), s);
       if (*err != hipSuccess) break;
     }
     return true;

@@ -53,11 +53,13 @@ hipError_t launch_gemv(const TensorView& w, const IoSpec& io, const void* x, int
 hipError_t launch_gemm(const TensorView& w, const IoSpec& io, const void* x, int T, void* y, hipStream_t s);
 
 // The matrix-core GEMV (vq_gemv_impl.h, MF) takes dense calls of two or more
-// tokens whose rows fit its passes (d = 2: 5120 columns, d = 4: 6144, d = 8:
-// 4096) and whose rows give every CU at least one 16-row group.
+// tokens whose rows give every CU at least one 16-row group.  Rows longer
+// than its passes hold in one block (d = 2: 5120 columns, d = 4: 6144, d = 8:
+// 4096) run as column slices added into y, so they need a plain fp32 output
+// (plain_out: fp32 y and no fused output step).
 __host__ __device__ inline int gemv_mf_max_cols(int d) { return d == 2 ? 5120 : (d == 4 ? 6144 : 4096); }
-inline bool gemv_mf_takes(int rows, int cols, int d, int T, int cus) {
-  return T >= 2 && cols <= gemv_mf_max_cols(d) && rows >= 16 * cus;
+inline bool gemv_mf_takes(int rows, int cols, int d, int T, int cus, bool plain_out) {
+  return T >= 2 && rows >= 16 * cus && (cols <= gemv_mf_max_cols(d) || plain_out);
 }
 // Compute units of the current device (cached on first use).
 int device_cus();
