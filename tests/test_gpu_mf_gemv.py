@@ -1,7 +1,7 @@
 """GPU parity of the matrix-core GEMV: dense vq_gemv calls of two or more
 tokens on matrices with at least one 16-row group per CU; rows longer than
 one block's passes (d = 2: 5120 columns, d = 4: 6144, d = 8: 4096) run as
-column slices added into y.
+column slices added into y, and five to sixteen tokens in its 16-token mode.
 
 The codebook entries go straight into the MFMA B operand and the x of four
 chunk positions into a block-diagonal A operand, so every output needs the
@@ -65,6 +65,7 @@ def test_mf_gemv_widths_passes_and_slices(rows, cols, d, b, g, Ts):
 @pytest.mark.parametrize("rows,cols,d,b,g,Ts", [
     (ROWS, 17408, 4, 8, 64, (2, 4)),       # 272 chunks: 3 column slices of 91, 90, 91
     (ROWS, 10240, 2, 12, 128, (3,)),       # 320 chunks: 2 slices of 160
+    (ROWS, 5184, 2, 8, 64, (2,)),          # 162 chunks: 2 slices of 81, the second from inside a scale group
     (4096, 8192, 8, 8, 64, (4, 7)),        # 64 chunks: 2 slices of 32; 32M weights, 2 token slices at T = 7
 ])
 def test_mf_gemv_long_rows_in_column_slices(rows, cols, d, b, g, Ts):
@@ -78,6 +79,44 @@ def test_mf_gemv_long_rows_in_column_slices(rows, cols, d, b, g, Ts):
         announce("mf-gemv-long", rows, cols, d, b, g, T)
         y = binding.gemv(w, to_dev(x)).cpu().numpy()
         assert row_rel_err(y, _ref(arrs, spec, x)) <= TOL, T
+
+
+@pytest.mark.parametrize("rows,cols,d,b,g,Ts", [
+    (ROWS, 2048, 4, 8, 64, (5, 16, 21)),    # 32 chunks: 3 slices of 11, 11, 10; T = 21 in two token slices
+    (ROWS, 2048, 2, 12, 128, (9,)),          # 64 chunks: 4 slices of 16
+    (ROWS, 1024, 8, 8, 64, (16,)),           # 8 chunks: 2 slices of 4, two scale groups per chunk
+    (ROWS, 10240, 2, 8, 64, (12,)),          # 320 chunks: 16 slices of 20
+    (4096, 4096, 4, 12, 128, (6, 13)),       # 64 chunks: 6 slices of 11 (the last 9), 128-weight groups
+])
+def test_mf_gemv_sixteen_token_mode(rows, cols, d, b, g, Ts):
+    """Five to sixteen tokens per grid slice: one pass per column slice, x of
+    all the slice's tokens staged once per block, the entries dequantized
+    (times their scale, fp16) into the B operand, every item's sums added
+    into y."""
+    from vq_dequant_matmul_gemv_amd import binding
+    spec, arrs, w = _case(d, b, g, rows, cols, ("mf16", rows, cols, d, b, g))
+    for T in Ts:
+        x = synth.activations((T, cols), "mf16", rows, cols, T)
+        announce("mf-gemv-16", rows, cols, d, b, g, T)
+        y = binding.gemv(w, to_dev(x)).cpu().numpy()
+        assert row_rel_err(y, _ref(arrs, spec, x)) <= TOL, T
+
+
+def test_mf_gemv_sixteen_token_mode_bf16_in_and_other_outputs():
+    """bf16 x in the 16-token mode; an fp16 output (the items cannot add into
+    it) keeps such calls on the other kernels."""
+    import torch
+    from vq_dequant_matmul_gemv_amd import binding
+    d, b, g, rows, cols, T = 4, 8, 64, ROWS, 2048, 9
+    spec, arrs, w = _case(d, b, g, rows, cols, ("mf16-io",))
+    xb = synth.activations_bf16((T, cols), "mf16-io")
+    ref = O.gemv_ref(arrs["codes"][0], arrs["codebook"], arrs["scales"][0], O.bf16_to_f64(xb), cols, d, b, g)
+    xd = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+    announce("mf-gemv-16-io")
+    y = binding.gemv(w, xd).cpu().numpy()
+    assert row_rel_err(y, ref) <= TOL
+    y16 = binding.gemv(w, xd, y_dtype=torch.float16).float().cpu().numpy()
+    assert row_rel_err(y16, ref) <= TOL + 2.0 ** -11
 
 
 @pytest.mark.parametrize("d,b,g", [(2, 8, 64), (4, 8, 64), (8, 12, 128)])

@@ -34,9 +34,8 @@
 //    otherwise one token per slice, re-reading the codes per token.  Above a
 //    few tokens the MFMA GEMM is the faster kernel and the C ABI's vq_gemv
 //    hands such calls to it.
-//  * Matrix-core variant (MF) for dense calls of 2 to 4 tokens (up to 8 on
-//    matrices that stay in L2): the dot products move from the VALU to
-//    v_mfma_f32_16x16x32_f16.  Lane l serves row l % 16 of a 16-row group at
+//  * Matrix-core variant (MF) for dense calls of 2 to 16 tokens: the dot
+//    products move from the VALU to v_mfma_f32_16x16x32_f16.  Lane l serves row l % 16 of a 16-row group at
 //    chunk position l / 16 (4 lanes per row, C chunks each); the gathered
 //    codebook entries are the B operand as they arrive (no VALU work on
 //    them), and the A operand holds x block-diagonally: A row 4t + p carries
@@ -45,7 +44,11 @@
 //    is one scale group's sum (a chunk lies inside one group, or a group
 //    inside it), so the scale multiplies it once, as in the scalar kernel.
 //    Per code: one v_perm_b32 and one gather; the per-token dot products
-//    cost nothing extra up to four tokens.
+//    cost nothing extra up to four tokens.  From five tokens on, the 16-token
+//    mode: A row m is token m, the gathered entries are multiplied by their
+//    group scale (v_pk_mul_f16: the dequantized weights, bit for bit) into
+//    the B operand, and each column slice is one pass, so the block stages
+//    the 16 tokens' x once and every item's sums add into y.
 //  * Each wave keeps P row groups' loads in flight (P items of C chunks per
 //    lane, about six chunks in all): wide items (d = 2, five chunks per lane)
 //    keep one, since a deeper ring only holds the wave at the issue of loads
@@ -98,6 +101,9 @@ constexpr int kGemvThreads = 64 * kGemvWaves;
 constexpr int kGemvXMaxBytes = 40 * 1024;      // largest x slice in LDS
 constexpr int kGemvScaleBytes = 24 * 1024;     // the block's scale rows (136 rows of 80 groups fit)
 constexpr int kGemvPieces = 4096;              // per-(row, pass) partial sums
+// The 16-token mode of the matrix-core variant needs no pieces: its scale
+// stage takes their LDS too.
+constexpr int kGemvMfWideScaleBytes = kGemvScaleBytes + 4 * kGemvPieces;
 
 // Chunks per lane a pass can hold in VGPRs: x costs 8*d VGPRs per chunk and
 // token of the slice (d = 4 two-token slices of 13- and 14-bit codes hold
@@ -115,6 +121,10 @@ __host__ __device__ constexpr int gemv_ring(int C) { return C >= 4 ? 1 : (C == 3
 // x of a pass sits in the MFMA A operand, 4 * d VGPRs per chunk, like the
 // scalar kernel's x-stationary registers.
 constexpr int kGemvMfTokens = 4;
+// Its 16-token mode (TT = 16): one pass per column slice, x of 16 tokens in
+// the A operand, the entries dequantized (times their group scale, one fp16
+// rounding) into the B operand, each item's sums added into y.
+constexpr int kGemvMfWideTokens = 16;
 __host__ __device__ constexpr int gemv_mf_max_c(int D) { return D == 2 ? 5 : (D == 4 ? 3 : 1); }
 // x bytes per token a block stages (the longest rows MF takes: 8 passes of 4 * C chunks)
 __host__ __device__ constexpr int gemv_mf_x_bytes(int D) { return 8 * 4 * gemv_mf_max_c(D) * 32 * D; }
@@ -158,12 +168,16 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
   constexpr int HX = 8 * D;                              // half2 of x per chunk
   constexpr int NW = kGemvWaves;
   constexpr int NT = kGemvThreads;
-  static_assert(C <= (MF ? gemv_mf_max_c(D) : gemv_max_c(D, B, TT)), "tile does not fit the VGPR budget");
-  static_assert(MF ? TT == kGemvMfTokens : (TT == 1 || (!MOE && XS == 2)),
+  constexpr bool WIDE = MF && TT == kGemvMfWideTokens;  // the 16-token mode
+  constexpr int TTU = TT > 4 ? 1 : TT;                  // unroll of the per-token loops
+  static_assert(C <= (MF ? gemv_mf_max_c(D) : gemv_max_c(D, B, TT)),
+                "tile does not fit the VGPR budget");
+  static_assert(MF ? (TT == kGemvMfTokens || TT == kGemvMfWideTokens) : (TT == 1 || (!MOE && XS == 2)),
                 "two-token slices: dense calls with short x slices");
 
   __shared__ __align__(16) uint8_t cb_lds[LY::kBytes];
-  constexpr int XBYTES = MF ? gemv_mf_x_bytes(D) : XS * 8192;       // x bytes staged at most, per token
+  // x bytes staged at most, per token (16-token mode: one pass, 4 * C chunks)
+  constexpr int XBYTES = WIDE ? 4 * gemv_mf_max_c(D) * 32 * D : (MF ? gemv_mf_x_bytes(D) : XS * 8192);
   // In LDS each chunk's 32 D bytes of x are followed by 16 bytes of padding:
   // the lanes of a row read consecutive chunks' x at once, and unpadded the
   // 32 D-byte stride would put 8 to 16 of them on the same banks.
@@ -171,8 +185,9 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
   constexpr int XSTRIDE = XCB + 16;
   constexpr int XTOK = XBYTES / XCB * XSTRIDE;                      // LDS bytes of one token's x
   __shared__ __align__(16) uint8_t x_lds[TT * XTOK + (MF ? 16 : 0)];  // [TT][nq][XSTRIDE] (+ MF: 16 zero bytes)
-  __shared__ __align__(16) uint8_t s_lds[kGemvScaleBytes];          // the block's scale rows
-  __shared__ float pieces[kGemvPieces];                             // [TT][rows][passes]
+  constexpr int SBYTES = WIDE ? kGemvMfWideScaleBytes : kGemvScaleBytes;
+  __shared__ __align__(16) uint8_t s_lds[SBYTES];                   // the block's scale rows
+  __shared__ float pieces[WIDE ? 1 : kGemvPieces];                  // [TT][rows][passes]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -235,10 +250,24 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
   // ---- small loads first: x slice, codebook entries, the block's scales ----
   const int xcols = nq * 16 * D;                        // columns of the slice
   const uint32_t xbytes = (uint32_t)xcols * 2u;
-  constexpr int XL = (XBYTES + NT * 16 - 1) / (NT * 16);
-  u32x4 xg[TT][XL];
+  constexpr int XL = WIDE ? 0 : (XBYTES + NT * 16 - 1) / (NT * 16);
+  u32x4 xg[WIDE ? 1 : TT][XL > 0 ? XL : 1];
+  // 16-token mode: the slice's x of all tokens as one flat run of 16-byte
+  // pieces, [token][XBYTES]
+  constexpr int XLW = WIDE ? (TT * XBYTES + NT * 16 - 1) / (NT * 16) : 1;
+  u32x4 xw[XLW];
+  if constexpr (WIDE) {
+    const rsrc_t rx = make_rsrc(xb, (uint64_t)ntok * cols * 2);
 #pragma unroll
-  for (int t = 0; t < TT; ++t) {
+    for (int q = 0; q < XLW; ++q) {
+      const uint32_t o = (uint32_t)(tid + q * NT) * 16u;
+      const uint32_t t = o / (uint32_t)XBYTES, w = o % (uint32_t)XBYTES;
+      xw[q] = buf_load_b128(rx, (t < (uint32_t)ntok && w < xbytes)
+                                    ? t * (uint32_t)cols * 2u + (uint32_t)q0 * 32u * D + w : kOutOfRange);
+    }
+  }
+#pragma unroll TTU
+  for (int t = 0; t < (WIDE ? 0 : TT); ++t) {
     if (MF && t >= ntok) break;  // MF: four token slots; only the slice's tokens are staged
     // a token past the slice's count gets an empty buffer: its x reads zeros
     const rsrc_t rx = make_rsrc(xb + (int64_t)t * cols, t < ntok ? (uint64_t)cols * 2 : 0);
@@ -273,7 +302,7 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
   const uint32_t s_total = (uint32_t)((uint64_t)rows * spr * 2u);  // bytes of this expert's scales
   const rsrc_t rsb = MF ? make_rsrc(scales, s_total)
                         : make_rsrc(reinterpret_cast<const uint8_t*>(scales) + (s_first - s_skew), s_avail);
-  constexpr int SL = (kGemvScaleBytes + NT * 16 - 1) / (NT * 16);
+  constexpr int SL = (SBYTES + NT * 16 - 1) / (NT * 16);
   u32x4 sg[SL];
 #pragma unroll
   for (int q = 0; q < SL; ++q) {
@@ -282,7 +311,7 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
     if constexpr (MF) {
       const uint32_t i = (uint32_t)(tid + q * NT);
       const uint32_t r = i / spp, k = i - r * spp;
-      live = r < (uint32_t)brows && i * 16u < (uint32_t)kGemvScaleBytes;
+      live = r < (uint32_t)brows && i * 16u < (uint32_t)SBYTES;
       o = ((((uint32_t)(brow0 + (int)r) * (uint32_t)spr + sg0) * 2u) & ~15u) + 16u * k;
       lim = s_total;
     } else {
@@ -400,8 +429,17 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
     }
   }
   const bool x_bf16 = a.x_bf16 != 0;
+  if constexpr (WIDE) {
 #pragma unroll
-  for (int t = 0; t < TT; ++t) {
+    for (int q = 0; q < XLW; ++q) {
+      const uint32_t o = (uint32_t)(tid + q * NT) * 16u;
+      const uint32_t t = o / (uint32_t)XBYTES, w = o % (uint32_t)XBYTES;
+      if (t < (uint32_t)TT)
+        *reinterpret_cast<u32x4*>(x_lds + t * XTOK + w + w / XCB * 16u) = x_bf16 ? bf16x8_to_f16x8(xw[q]) : xw[q];
+    }
+  }
+#pragma unroll TTU
+  for (int t = 0; t < (WIDE ? 0 : TT); ++t) {
     if (MF && t >= ntok) break;
 #pragma unroll
     for (int q = 0; q < XL; ++q) {
@@ -415,7 +453,7 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
 #pragma unroll
   for (int q = 0; q < SL; ++q) {
     const uint32_t o = (uint32_t)(tid + q * NT) * 16u;
-    if (o < (uint32_t)kGemvScaleBytes) *reinterpret_cast<u32x4*>(s_lds + o) = sg[q];
+    if (o < (uint32_t)SBYTES) *reinterpret_cast<u32x4*>(s_lds + o) = sg[q];
   }
   if constexpr (!LY::kReplicated) stage_codebook<D, B>(cb_lds, cb, tid, NT);
   lds_barrier();
@@ -433,9 +471,11 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
   // four separate output rows instead of summing them.
   constexpr int KS = MF ? 2 * D : 1;  // k-steps (8 fp16 of A and B each) per chunk
   u32x4 xa[MF ? C : 1][KS];
+  // 16-token mode: A row m is token m, lane (m, p) holds its x for chunk
+  // position p.
   auto load_xa = [&](int pass) {
-    const int m = lane & 15, tk = m >> 2;
-    const bool mine = (m & 3) == (lane >> 4) && tk < ntok;
+    const int m = lane & 15, tk = WIDE ? m : m >> 2;
+    const bool mine = (WIDE || (m & 3) == (lane >> 4)) && tk < ntok;
     const int lim = min(PW, nq - pass * PW);
 #pragma unroll
     for (int j = 0; j < (MF ? C : 1); ++j) {
@@ -466,7 +506,10 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
             mf_sq[j][i] = (((uint32_t)(q0 + pass * PW + qp) * 16u * D) / G - sg0) * 2u;
             mf_ok[j][i] = qp < lim ? 0xffffffffu : 0u;
           }
-          lane_csh[j] = chunk_shift<B>((uint32_t)(q0 + pass * PW + j * 4 + li));
+          const int qp = j * 4 + li;  // this lane's chunk (16-token mode: its scales)
+          lane_sq[j] = (((uint32_t)(q0 + pass * PW + qp) * 16u * D) / G - sg0) * 2u;
+          lane_ok[j] = qp < lim ? 0xffffffffu : 0u;
+          lane_csh[j] = chunk_shift<B>((uint32_t)(q0 + pass * PW + qp));
         }
       }
       const int rb = g * 16 + rsub;                       // this lane's row within the block
@@ -494,8 +537,36 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
           load_chunk(rs[j], j, nl);
           __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (WIDE) {  // dequantize: entry times its group scale, one fp16 rounding (v_pk_mul_f16)
+          const uint32_t keep = lane_ok[j] & rowok;
+          const uint32_t so = srow + lane_sq[j] + 2u * (uint32_t)((s2 * 8) / G);
+          const uint32_t sb = (uint32_t)*reinterpret_cast<const uint16_t*>(s_lds + (so & keep)) & keep;
+          const half2_t sc = as_half2(sb | (sb << 16));
+#pragma unroll
+          for (int k = 0; k < 4; ++k) w[k] = as_u32(as_half2(w[k]) * sc);
+        }
         return __builtin_bit_cast(half8_t, u32x4{w[0], w[1], w[2], w[3]});
       };
+      if constexpr (WIDE) {
+        // the item's sums over the slice: lane l holds tokens 4 (l / 16) + i of row rsub
+        half8_t bw[2];
+        bw[0] = issue(0);
+        float4_t dw[2] = {float4_t{0.f, 0.f, 0.f, 0.f}, float4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int t = 0; t < C * KS; ++t) {
+          if (t + 1 < C * KS) bw[(t + 1) & 1] = issue(t + 1);
+          dw[t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, xa[t / KS][t % KS]),
+                                                             bw[t & 1], dw[t & 1], 0, 0, 0);
+        }
+        if (rb < brows) {
+          float* yf = reinterpret_cast<float*>(a.y) + yrow * rows + brow0 + rb;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tok = 4 * (lane >> 4) + i;
+            if (tok < ntok) atomicAdd(yf + (int64_t)tok * rows, dw[0][i] + dw[1][i]);
+          }
+        }
+      } else {
       float acc = 0.f;
       half8_t bq[2];
       bq[0] = issue(0);
@@ -520,6 +591,7 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
       }
       const int tk = lane >> 4;
       if (tk < ntok && rb < brows) pieces[(tk * brows + rb) * passes + pass] = acc;
+      }
     } else {
       if (pass != cur_pass) {  // x of this pass into VGPRs (zeros past the slice)
         cur_pass = pass;
@@ -639,9 +711,9 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
   }
 items_done:
 
-  {  // y: each row's pass pieces added in pass order (deterministic)
+  if constexpr (!WIDE) {  // y: each row's pass pieces added in pass order (deterministic)
     __syncthreads();
-#pragma unroll
+#pragma unroll TTU
     for (int u = 0; u < TT; ++u) {
       if (u >= ntok) break;
       auto row_sum = [&](int r) {
@@ -855,7 +927,10 @@ hipError_t gemv_launch(const GemvArgs& a, int C, dim3 grid, hipStream_t s) {
 // slice, for dense calls of two or more tokens (gemv_mf_takes).  Longer rows
 // are split into column slices run side by side (blockIdx.z), each staging
 // only its own x and scales, their sums added atomically into a zeroed fp32 y.
-// Returns false when the call is not one it takes.
+// Above four tokens, the 16-token mode: one pass per column slice (every
+// wave of a block on the same columns, so the block stages the 16 tokens' x
+// once), each item's sums added into y.  Returns false when the call is not
+// one it takes.
 template <int D, int B, int G, bool MOE>
 bool gemv_run_mf(GemvArgs a, int P, int ycount, hipStream_t s, hipError_t* err) {
   if constexpr (MOE) {
@@ -863,8 +938,11 @@ bool gemv_run_mf(GemvArgs a, int P, int ycount, hipStream_t s, hipError_t* err) 
   } else {
     const bool plain_out = a.epi == kEpiNone && a.y_kind == kOutF32;
     if (!gemv_mf_takes(a.rows, a.cols, D, ycount, num_cus(), plain_out)) return false;
-    constexpr int MC = gemv_mf_max_c(D);
-    const int n_sl = (P + kGemvWaves * 4 * MC - 1) / (kGemvWaves * 4 * MC);
+    const bool wide = ycount > kGemvMfTokens;
+    const int tt = wide ? kGemvMfWideTokens : kGemvMfTokens;
+    const int MC = gemv_mf_max_c(D);
+    const int max_passes = wide ? 1 : kGemvWaves;
+    const int n_sl = (P + max_passes * 4 * MC - 1) / (max_passes * 4 * MC);
     const int per = (P + n_sl - 1) / n_sl;                // chunks per column slice
     int passes = 1;
     while ((per + passes - 1) / passes > 4 * MC) passes *= 2;
@@ -876,27 +954,30 @@ bool gemv_run_mf(GemvArgs a, int P, int ycount, hipStream_t s, hipError_t* err) 
     a.accumulate = 0;
     a.lanes_log2 = 2;
     a.passes = passes;
-    const int ny = (ycount + kGemvMfTokens - 1) / kGemvMfTokens;
+    const int ny = (ycount + tt - 1) / tt;
     const int blocks_fill = std::max(1, num_cus() / std::max(1, ny * n_sl));
     // a block stages the scale groups of its slice, up to two partial ones included
     const int64_t groups = ((int64_t)per * 16 * D + G - 1) / G + 1;
     const int64_t spp = (groups * 2 + 30) / 16;
-    const int64_t by_scales = std::max<int64_t>(1, kGemvScaleBytes / (16 * spp));
-    const int64_t by_pieces = std::max<int64_t>(1, kGemvPieces / ((int64_t)passes * kGemvMfTokens));
+    const int64_t by_scales = std::max<int64_t>(1, (wide ? kGemvMfWideScaleBytes : kGemvScaleBytes) / (16 * spp));
+    const int64_t by_pieces =
+        wide ? by_scales : std::max<int64_t>(1, kGemvPieces / ((int64_t)passes * kGemvMfTokens));
     const int unit = a.epi == kEpiSwiglu ? 2 : 1;
     const int64_t rows_max = std::max<int64_t>(unit, std::min(by_scales, by_pieces) / unit * unit);
     const int64_t units = a.rows / unit;
     const int64_t blocks = std::min<int64_t>(units, std::max<int64_t>(blocks_fill, (a.rows + rows_max - 1) / rows_max));
     a.rows_base = (int)(units / blocks) * unit;
     a.rows_extra = (int)(units - units / blocks * blocks) | (unit == 2 ? 1 << 30 : 0);
-    if (n_sl > 1) {  // the slices add into y
+    if (n_sl > 1 || wide) {  // the slices (16-token mode: the items) add into y
       *err = launch_zero(a.y, (size_t)ycount * a.rows * sizeof(float), s);
       if (*err != hipSuccess) return true;
     }
     for (int y0 = 0; y0 < ny; y0 += 65535) {
       const int yc = std::min(65535, ny - y0);
-      a.tok0 = y0 * kGemvMfTokens;
-      *err = gemv_launch<D, B, G, 2, false, kGemvMfTokens, true>(a, C, dim3((unsigned)blocks, (unsigned)yc, (unsigned)n_sl), s);
+      a.tok0 = y0 * tt;
+      const dim3 grid((unsigned)blocks, (unsigned)yc, (unsigned)n_sl);
+      *err = wide ? gemv_launch<D, B, G, 2, false, kGemvMfWideTokens, true>(a, C, grid, s)
+                  : gemv_launch<D, B, G, 2, false, kGemvMfTokens, true>(a, C, grid, s);
       if (*err != hipSuccess) break;
     }
     return true;

@@ -58,8 +58,10 @@ hipError_t launch_gemm(const TensorView& w, const IoSpec& io, const void* x, int
 // 4096) run as column slices added into y, so they need a plain fp32 output
 // (plain_out: fp32 y and no fused output step).
 __host__ __device__ inline int gemv_mf_max_cols(int d) { return d == 2 ? 5120 : (d == 4 ? 6144 : 4096); }
+// Above four tokens it runs its 16-token mode, whose items add into y: a
+// plain fp32 output again.
 inline bool gemv_mf_takes(int rows, int cols, int d, int T, int cus, bool plain_out) {
-  return T >= 2 && rows >= 16 * cus && (cols <= gemv_mf_max_cols(d) || plain_out);
+  return T >= 2 && rows >= 16 * cus && ((T <= 4 && cols <= gemv_mf_max_cols(d)) || plain_out);
 }
 // Compute units of the current device (cached on first use).
 int device_cus();
