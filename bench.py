@@ -137,9 +137,8 @@ SWEEP_REPLICAS = 16                                   # 16 x 25 MB per matrix: e
 
 def sweep_rooflines(profile_only=None):
     """Config-4 kernels on one GPU: W_A [17408][5120] and W_B [5120][17408],
-    d=4 K=256 g=64, vq_gemv at T = 1 and T = 4 (HBM-bound; at T = 4 the
-    matrix-core GEMV on A, the MFMA GEMM on B) and the GEMM at T = 4096
-    (MFMA-bound).  Per-launch durations from bursts of back-to-back launches
+    d=4 K=256 g=64, vq_gemv at T = 1, 4 and 16 (HBM-bound; 4 and 16 on the
+    matrix-core GEMV) and the GEMM at T = 256 and 4096 (MFMA-bound).  Per-launch durations from bursts of back-to-back launches
     in one graph (16 GEMVs / 4 GEMMs, rotating over weight replicas), timed
     with events on the launch stream, median of 5 bursts."""
     import re
@@ -157,22 +156,29 @@ def sweep_rooflines(profile_only=None):
         x1 = torch.from_numpy(synth.activations((1, spec.cols), SWEEP, name, "x", 1)).to(dev)
         x4 = torch.from_numpy(synth.activations((4, spec.cols), SWEEP, name, "x", 4)).to(dev)
         y4 = torch.empty((4, spec.rows), dtype=torch.float32, device=dev)
+        x16 = torch.from_numpy(synth.activations((16, spec.cols), SWEEP, name, "x", 16)).to(dev)
+        y16 = torch.empty((16, spec.rows), dtype=torch.float32, device=dev)
+        x256 = torch.from_numpy(synth.activations((256, spec.cols), SWEEP, name, "x", 256)).to(dev)
+        y256 = torch.empty((256, spec.rows), dtype=torch.float32, device=dev)
         xT = torch.from_numpy(synth.activations((4096, spec.cols), SWEEP, name, "x", 4096)).to(dev)
         y1 = torch.empty((1, spec.rows), dtype=torch.float32, device=dev)
         yT = torch.empty((4096, spec.rows), dtype=torch.float32, device=dev)
         gemv = [lambda w=reps[i % SWEEP_REPLICAS]: binding.gemv(w, x1, y1) for i in range(16)]
         gemv4 = [lambda w=reps[i % SWEEP_REPLICAS]: binding.gemv(w, x4, y4) for i in range(16)]
+        gemv16 = [lambda w=reps[i % SWEEP_REPLICAS]: binding.gemv(w, x16, y16) for i in range(16)]
+        gemm256 = [lambda w=reps[i % SWEEP_REPLICAS]: binding.gemm(w, x256, y256) for i in range(8)]
         gemm = [lambda w=reps[i % SWEEP_REPLICAS]: binding.gemm(w, xT, yT) for i in range(4)]
         if profile_only:
             for c in gemv[:4] + gemv4[:4] + gemm[:2]:
                 c()
             torch.cuda.synchronize()
             continue
-        for c in gemv + gemv4 + gemm:   # warm
+        for c in gemv + gemv4 + gemv16 + gemm256 + gemm:   # warm
             c()
         torch.cuda.synchronize()
         res = {}
-        for key, calls in (("gemv_T1", gemv), ("gemv_T4", gemv4), ("gemm_T4096", gemm)):
+        for key, calls in (("gemv_T1", gemv), ("gemv_T4", gemv4), ("gemv_T16", gemv16), ("gemm_T256", gemm256),
+                           ("gemm_T4096", gemm)):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for c in calls:
@@ -190,6 +196,9 @@ def sweep_rooflines(profile_only=None):
             del g
         nb = tensor_bytes(spec, 1)
         nb4 = tensor_bytes(spec, 4)
+        nb16 = tensor_bytes(spec, 16)
+        gbps16 = nb16 / res["gemv_T16"] / 1e9
+        tflops256 = 2.0 * 256 * spec.rows * spec.cols / res["gemm_T256"] / 1e12
         flops = 2.0 * 4096 * spec.rows * spec.cols
         gbps = nb / res["gemv_T1"] / 1e9
         gbps4 = nb4 / res["gemv_T4"] / 1e9
@@ -205,13 +214,20 @@ def sweep_rooflines(profile_only=None):
                         "algorithmic_bytes": nb4,
                         "traffic": measured_traffic(re.compile(r"vq_gemv_kernel<4, 8, 64, \d+, \d+, false, 4, true>"),
                                                     SWEEP_TAG + "_" + name)},
+            "gemv_T16": {"bound": "hbm", "us": round(res["gemv_T16"] * 1e6, 2), "achieved": round(gbps16, 2),
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps16 / HBM_PEAK_GBPS, 4),
+                         "algorithmic_bytes": nb16},
+            "gemm_T256": {"bound": "mfma", "us": round(res["gemm_T256"] * 1e6, 2), "achieved": round(tflops256, 2),
+                          "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(tflops256 / MFMA_F16_PEAK_TFLOPS, 4),
+                          "algorithmic_bytes": tensor_bytes(spec, 256)},
             "gemm_T4096": {"bound": "mfma", "us": round(res["gemm_T4096"] * 1e6, 2), "achieved": round(tflops, 2),
                            "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
                            "algorithmic_bytes": tensor_bytes(spec, 4096),
                            "traffic": measured_traffic("vq_gemm_kernel<4, 8, 64, GemmShape<8, 2, 4>",
                                                        SWEEP_TAG + "_" + name)}}
-        del reps, base, xT, yT, x4, y4
+        del reps, base, xT, yT, x4, y4, x16, y16, x256, y256
         torch.cuda.empty_cache()
     if profile_only:
         print(f"profile-sweep {profile_only}: 4 GEMVs (T=1), 4 GEMVs (T=4) and 2 GEMMs (T=4096)", flush=True)

@@ -65,33 +65,44 @@ def _assert_columns(y, wdq, columns):
 
 
 @pytest.mark.parametrize("d,b,g", GEOMS)
-def test_gemm_one_hot_rows_give_the_dequantized_columns(d, b, g):
-    """x = identity (T = cols, 128-token tiles) and a 32-row one-hot slice
-    spread over the row (32-token tiles)."""
+def test_gemm_one_hot_rows_give_the_dequantized_columns(d, b, g, monkeypatch):
+    """x = identity (T = cols) on 128-token tiles (forced: at this size the
+    time model takes 32-token ones) and on the tiles the model picks, and a
+    32-row one-hot slice spread over the row (32-token tiles)."""
     from vq_dequant_matmul_gemv_amd import binding
     rows, cols = 301, _cols_for(d, g, 6)
     spec, arrs, w, wdq = _dense(d, b, g, rows, cols, ("onehot", d, b, g))
     assert np.any((np.abs(wdq.astype(np.float32)) < 2.0 ** -14) & (wdq != 0)), "no subnormal weight drawn"
-    for columns in (np.arange(cols), (np.arange(32) * (cols // 32) + np.arange(32) % 7) % cols):
+    for columns, tile in ((np.arange(cols), "128"), (np.arange(cols), None),
+                          ((np.arange(32) * (cols // 32) + np.arange(32) % 7) % cols, None)):
+        if tile:
+            monkeypatch.setenv("VQMI_GEMM_TILE", tile)
+        else:
+            monkeypatch.delenv("VQMI_GEMM_TILE", raising=False)
         T = len(columns)
         x = _one_hot(T, cols, columns)
-        announce("gemm one-hot", d, b, g, rows, cols, T)
+        announce("gemm one-hot", d, b, g, rows, cols, T, tile)
         y = binding.gemm(w, to_dev(x)).cpu().numpy()
         _assert_columns(y, wdq, columns)
 
 
 @pytest.mark.parametrize("d,b,g", [(2, 8, 64), (4, 12, 128), (8, 12, 64), (4, 8, 64)])
-def test_gemm_one_hot_split_k_tiles(d, b, g):
+def test_gemm_one_hot_split_k_tiles(d, b, g, monkeypatch):
     """2048 columns and too few tiles to fill the GPU: the tiles are split
-    along K and their slices added atomically into a zeroed y."""
+    along K and their slices added atomically into a zeroed y (32-token
+    tiles, and 128-token ones forced)."""
     from vq_dequant_matmul_gemv_amd import binding
     rows, cols = 700, 2048
     spec, arrs, w, wdq = _dense(d, b, g, rows, cols, ("onehot-split", d, b, g))
     rng = synth.rng("onehot-split-cols", d, b, g)
-    for T in (8, 200):
+    for T, tile in ((8, None), (200, None), (200, "128")):
+        if tile:
+            monkeypatch.setenv("VQMI_GEMM_TILE", tile)
+        else:
+            monkeypatch.delenv("VQMI_GEMM_TILE", raising=False)
         columns = rng.integers(0, cols, size=T)
         x = _one_hot(T, cols, columns)
-        announce("gemm one-hot split-K", d, b, g, rows, cols, T)
+        announce("gemm one-hot split-K", d, b, g, rows, cols, T, tile)
         y = binding.gemm(w, to_dev(x)).cpu().numpy()
         _assert_columns(y, wdq, columns)
 

@@ -101,11 +101,14 @@ def test_dense_exact_inputs_bit_identical(fn, d, b, g):
 
 
 @pytest.mark.parametrize("d,b,g", GEOMS)
-def test_gemm_128_token_tiles_all_geometries(d, b, g):
-    """The 128-token tiles (T > 32) in every geometry: ragged rows and
-    tokens, an odd number of super-steps, and a K split whose slices hold an
-    odd number of super-steps (the main loop's second half-step is skipped)."""
+def test_gemm_128_token_tiles_all_geometries(d, b, g, monkeypatch):
+    """The 128-token tiles (forced: at these sizes the time model takes
+    32-token ones) in every geometry: ragged rows and tokens, an odd number of
+    super-steps, and a K split whose slices hold an odd number of super-steps
+    (the main loop's second half-step is skipped).  Then the tiles the model
+    picks at T = 129."""
     from vq_dequant_matmul_gemv_amd import binding
+    monkeypatch.setenv("VQMI_GEMM_TILE", "128")
     ss = 64 if d == 2 else 128                      # columns per super-step
     for rows, cols, Ts in ((301, _cols_for(d, g, 7), (40, 129)),
                            (1030, ss * (25 if d == 2 else 13 if d == 4 else 18), (130,))):
@@ -119,6 +122,11 @@ def test_gemm_128_token_tiles_all_geometries(d, b, g):
             ref = O.gemv_ref(arrs["codes"][0], arrs["codebook"], arrs["scales"][0], x, cols, d, b, g)
             err = row_rel_err(y, ref)
             assert err <= TOL, (rows, cols, T, err)
+            if T == 129:
+                monkeypatch.delenv("VQMI_GEMM_TILE")
+                y = binding.gemm(w, to_dev(x)).cpu().numpy()
+                monkeypatch.setenv("VQMI_GEMM_TILE", "128")
+                assert row_rel_err(y, ref) <= TOL, (rows, cols, T)
 
 
 @pytest.mark.parametrize("fn", ["gemv", "gemm"])

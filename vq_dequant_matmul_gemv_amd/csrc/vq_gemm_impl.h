@@ -51,6 +51,7 @@
 #include "vq_kernels.h"
 
 #include <algorithm>
+#include <cstdlib>
 #include <mutex>
 
 namespace vqmi {
@@ -416,38 +417,60 @@ GemmArgs base_args(const TensorView& w, const IoSpec& io, const void* x, void* y
   return a;
 }
 
+// Time model of a dense call, fitted to calls measured on MI355X (17408x5120
+// and 5120x17408, d = 2 and 4, T = 64 ... 1024, every split of 1 ... 6): a
+// tile over the whole K costs 3 us plus, per column, 0.0095 us (32-token
+// tiles, d = 4 and 8), 0.0147 us (32-token, d = 2), 0.0200 us (128-token, d =
+// 4 and 8) or 0.0240 us (128-token, d = 2); whole rounds of tiles run one
+// after another; the K slices of a last, partial round add every sum into a
+// zeroed y with fp32 atomics, ~4 ps per add, plus ~5 us for the zeroing
+// launch.  The atomic adds are what a flat per-slice charge missed: at T =
+// 512 (17408x5120 d = 4, 136 tiles of 128 tokens) three slices took 164 us,
+// one 113 us.
+struct GemmPlan {
+  int split;
+  double us;
+};
+
+inline double gemm_tile_us(bool thin, int D, int cols) {
+  const double per_col = thin ? (D == 2 ? 0.0147 : 0.0095) : (D == 2 ? 0.0240 : 0.0200);
+  return 3.0 + per_col * cols;
+}
+
+// Best K split of the last partial round for tiles of `rows_t` rows x
+// `tok_t` tokens (split 1 when the output cannot take atomic adds).
+inline GemmPlan gemm_plan(int T, int rows, int cols, int D, bool thin, int rows_t, int tok_t, int cus,
+                          bool split_ok) {
+  const int n_row_tiles = (rows + rows_t - 1) / rows_t;
+  const int n_tok_tiles = (T + tok_t - 1) / tok_t;
+  const int tiles = n_row_tiles * n_tok_tiles;
+  const double t_tile = gemm_tile_us(thin, D, cols);
+  const int full = (tiles / cus) * cus, rem = tiles - full;
+  GemmPlan best{1, (double)((tiles + cus - 1) / cus) * t_tile};
+  if (rem == 0 || !split_ok) return best;
+  // each K slice keeps at least 512 columns (1024 for d = 8)
+  const int max_split = std::max(1, cols / (D == 8 ? 1024 : 512));
+  const double rem_outputs = (double)rem / tiles * (double)T * rows;  // outputs of the split tiles
+  for (int sp = 2; sp <= std::min(32, max_split); ++sp) {
+    const double us = (double)(full / cus) * t_tile + (double)((rem * sp + cus - 1) / cus) * t_tile / sp + 5.0 +
+                      4e-6 * rem_outputs * sp;
+    if (us < best.us - 1e-9) best = GemmPlan{sp, us};
+  }
+  return best;
+}
+
+// Whole rounds of tiles run as whole tiles; with split > 1, the tiles of a
+// last, partial round are split along K over the CUs and added atomically
+// into a zeroed y (their fp32 addition order then varies between runs).
 template <int D, int B, int G, class SH>
-hipError_t gemm_dense(GemmArgs a, hipStream_t s) {
+hipError_t gemm_dense(GemmArgs a, int split, hipStream_t s) {
   a.n_row_tiles = (a.rows + SH::kRows - 1) / SH::kRows;
   a.n_tok_tiles = (a.T + SH::kTokens - 1) / SH::kTokens;
   const int tiles = a.n_row_tiles * a.n_tok_tiles;
-  // each K slice keeps at least 512 columns (1024 for d = 8), whatever the
-  // super-step length
-  const int max_split = std::max(1, a.cols / (D == 8 ? 1024 : 512));
   const int cus = num_cus();
-  // Whole rounds of tiles run as whole tiles; the tiles of a last, partial
-  // round are split along K over the CUs and added atomically into a zeroed
-  // y (their fp32 addition order then varies between runs).
-  // The split minimises the partial round's time in tile rounds,
-  // ceil(rem * split / cus) / split, plus a small charge per extra slice for
-  // the atomic traffic.
-  int full = (tiles / cus) * cus, rem = tiles - full, split = 1;
-  if (rem > 0) {
-    double best = 1e30;
-    // the charge per slice scales with the tokens of a tile: the atomic adds
-    // are T x rows per slice, negligible next to the weight stream at small T
-    const double charge = 0.03 * std::min(1.0, (double)a.T / SH::kTokens);
-    for (int sp = 1; sp <= std::min(32, max_split); ++sp) {
-      const double c = (double)((rem * sp + cus - 1) / cus) / sp + charge * (sp - 1);
-      if (c < best - 1e-9) {
-        best = c;
-        split = sp;
-      }
-    }
-  }
-  // K slices add fp32 partial sums: only a plain fp32 output can take them
-  if (a.epi != kEpiNone || a.y_kind != kOutF32) split = 1;
-  if (split == 1) {
+  int full = (tiles / cus) * cus, rem = tiles - full;
+  if (split <= 1 || rem == 0) {
+    split = 1;
     full = tiles;
     rem = 0;
   }
@@ -463,12 +486,27 @@ hipError_t gemm_dense(GemmArgs a, hipStream_t s) {
   return gemm_launch<D, B, G, SH>(a, dim3((unsigned)(full + rem * split)), s);
 }
 
+// Up to 32 tokens the 32-token tiles; above, the tile shape and split the
+// time model rates faster (32-token tiles keep winning up to a few hundred
+// tokens: 17408x5120 d = 4 at T = 64 / 128 / 256 in 36 / 52 / 77 us against
+// 49 / 62 / 86 us for the best split of 128-token tiles).
+// The environment variable VQMI_GEMM_TILE = 32 or 128 forces a tile shape
+// (the split still by the model), so each shape can be tested at sizes where
+// the model would take the other.
 template <int D, int B, int G>
 hipError_t gemm_geom(const TensorView& w, const IoSpec& io, const void* x, int T, void* y, hipStream_t s) {
   GemmArgs a = base_args(w, io, x, y, G, D, B);
   a.T = T;
-  if (T <= 32) return gemm_dense<D, B, G, GemmSmallT>(a, s);
-  return gemm_dense<D, B, G, GemmLargeT>(a, s);
+  const int cus = num_cus();
+  const bool split_ok = io.epi == kEpiNone && io.y_kind == kOutF32;  // K slices add fp32 sums
+  const char* force = getenv("VQMI_GEMM_TILE");
+  const int forced = force ? atoi(force) : 0;
+  const GemmPlan thin = gemm_plan(T, w.rows, w.cols, D, true, GemmSmallT::kRows, GemmSmallT::kTokens, cus, split_ok);
+  const GemmPlan large = gemm_plan(T, w.rows, w.cols, D, false, GemmLargeT::kRows, GemmLargeT::kTokens, cus, split_ok);
+  if (forced == GemmLargeT::kTokens) return gemm_dense<D, B, G, GemmLargeT>(a, large.split, s);
+  if (forced == GemmSmallT::kTokens || T <= GemmSmallT::kTokens || thin.us < large.us)
+    return gemm_dense<D, B, G, GemmSmallT>(a, thin.split, s);
+  return gemm_dense<D, B, G, GemmLargeT>(a, large.split, s);
 }
 
 // The routed kernel variant (32-token tiles with 128-column super-steps for
