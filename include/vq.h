@@ -181,12 +181,17 @@ vq_status vq_dequant(const vq_tensor *w, int32_t expert, uint16_t *w_out, void *
  *   x: device [T][cols] fp16 bits, 16-byte aligned;
  *   y: device [T][rows] fp32, 16-byte aligned.
  * T >= 0 (T == 0 enqueues nothing).  Any T is accepted.  The streaming
- * kernel reads every code once per token, or once per two tokens when a
- * row's x fits 16 KiB: the fast path for T = 1 and 2 (the fused
- * decode-and-matmul of paper §3.4; two tokens: a two-token speculative
- * verify step, 35B card, Experimental MTP); above a token count measured per shape (2 for d = 2/4
- * matrices, 4 for d = 8, 6 for matrices of at most 16M weights) vq_gemv runs
- * the MFMA kernel of vq_gemm instead, with the same result contract.
+ * kernel reads every code once per token slice: the fast path for small T
+ * (the fused decode-and-matmul of paper §3.4; two tokens: a two-token
+ * speculative verify step, 35B card, Experimental MTP).  On matrices of at
+ * least 16 rows per compute unit, 2 to 4 tokens (up to 16 when y is plain
+ * fp32) run on its matrix-core variant, whose partial sums of long rows'
+ * column slices (and, above four tokens, of every item) are added
+ * atomically into y, zeroed first: those outputs may differ in the last
+ * bits from run to run.  Above a token count measured per shape (16 or 4
+ * there; otherwise 2 for d = 2/4 matrices, 4 for d = 8, 6 for matrices of at
+ * most 16M weights) vq_gemv runs the MFMA kernel of vq_gemm instead, with
+ * the same result contract.
  */
 vq_status vq_gemv(const vq_tensor *w, const uint16_t *x, int32_t T, float *y, void *stream);
 
@@ -194,12 +199,14 @@ vq_status vq_gemv(const vq_tensor *w, const uint16_t *x, int32_t T, float *y, vo
  * Prefill-shaped product, same arguments and result as vq_gemv: dequantized
  * weight tiles feed fp16 MFMA instructions with fp32 accumulation.  Any T is
  * accepted; it is the fast path for large T (paper §2.5: scoring runs a
- * prefill-shaped path; §3.4 prefill).  When the output tiles do not fill
+ * prefill-shaped path; §3.4 prefill).  Tiles of 32 or 128 tokens, whichever
+ * a time model of the call rates faster.  When the output tiles do not fill
  * whole rounds of the GPU's compute units, the tiles of the last, partial
- * round are split along the columns and their partial sums added atomically
- * into y (zeroed first on the same stream): those outputs may differ in the
- * last bits from run to run (fp32 addition order), within the stated
- * tolerance; all others are deterministic.
+ * round may be split along the columns and their partial sums added
+ * atomically into y (zeroed first on the same stream): those outputs may
+ * differ in the last bits from run to run (fp32 addition order), within the
+ * stated tolerance; all others are deterministic.  The environment variable
+ * VQMI_GEMM_TILE = 32 or 128 forces the tile shape (for tests).
  */
 vq_status vq_gemm(const vq_tensor *w, const uint16_t *x, int32_t T, float *y, void *stream);
 
