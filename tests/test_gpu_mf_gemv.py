@@ -69,6 +69,7 @@ def test_mf_gemv_widths_passes_and_slices(rows, cols, d, b, g, Ts):
     (4096, 8192, 8, 8, 64, (4, 7)),        # 64 chunks: 2 slices of 32; 32M weights, 2 token slices at T = 7
 ])
 def test_mf_gemv_long_rows_in_column_slices(rows, cols, d, b, g, Ts):
+    # (4096 x 8192 d = 8 has 16 one-pass slices: up to 10 tokens in the 16-token mode)
     """Rows longer than one block's passes: column slices side by side in
     one launch, each staging its own x and scale groups (slices starting
     inside a scale group included), added into a zeroed y."""
@@ -82,7 +83,7 @@ def test_mf_gemv_long_rows_in_column_slices(rows, cols, d, b, g, Ts):
 
 
 @pytest.mark.parametrize("rows,cols,d,b,g,Ts", [
-    (ROWS, 2048, 4, 8, 64, (5, 16, 21)),    # 32 chunks: 3 slices of 11, 11, 10; T = 21 in two token slices
+    (ROWS, 2048, 4, 8, 64, (5, 16, 21)),    # 32 chunks: 3 slices of 11, 11, 10; T = 21 past the limit: the GEMM
     (ROWS, 2048, 2, 12, 128, (9,)),          # 64 chunks: 4 slices of 16
     (ROWS, 1024, 8, 8, 64, (16,)),           # 8 chunks: 2 slices of 4, two scale groups per chunk
     (ROWS, 10240, 2, 8, 64, (12,)),          # 320 chunks: 16 slices of 20

@@ -222,20 +222,19 @@ vq_status vq_dequant(const vq_tensor* w, int32_t expert, uint16_t* w_out, void* 
 // Largest token count for which the streaming GEMV beats the MFMA GEMM,
 // measured on MI355X at the benchmark shapes: the GEMV reads every code once
 // per grid slice, the GEMM once per 32- or 128-token tile, split along K to
-// fill the GPU.  Where the matrix-core GEMV takes the call it wins up to 16
-// tokens for a plain fp32 output (its 16-token mode; 17408x5120 d = 4: 14.2,
-// 15.3 and 20.8 us at T = 5, 8 and 16 against 18.4, 19.1 and 22.1 us for the
-// GEMM; 5120x17408 d = 2, 28 column slices: 34.7 against 38.9 us at T = 16)
-// and up to 4 tokens otherwise (11.6-12.9 us at T = 2-4 against 17.7-18.2
-// us).  Elsewhere small matrices and d = 8 keep a few tokens on the scalar
+// fill the GPU.  Where the matrix-core GEMV takes the call it wins up to the
+// token count gemv_mf_max_tokens gives (16-token mode; 17408x5120 d = 4:
+// 14.2, 15.1 and 20.9 us at T = 5, 8 and 16 against 17.9, 18.8 and 22.1 us
+// for the GEMM; d = 2: 18.8 against 24.8 us at T = 16) and up to 4 tokens
+// otherwise (12.6-13.1 us at T = 3-4 against 17.7-17.9 us).  Elsewhere small matrices and d = 8 keep a few tokens on the scalar
 // GEMV, and the rest wins up to T = 2 (two tokens per slice; 17408x5120 and
 // 5120x17408, d = 2 and 4: 15.9-18.6 us against 17.3-21.7 us for the GEMM).
 static int gemv_token_limit(const vqmi::TensorView& v, const vqmi::IoSpec& io) {
   const bool small = (int64_t)v.rows * v.cols <= (int64_t)16 << 20;
   const bool plain_out = io.epi == vqmi::kEpiNone && io.y_kind == vqmi::kOutF32;
-  const int cus = vqmi::device_cus();
-  if (vqmi::gemv_mf_takes(v.rows, v.cols, v.d, 16, cus, plain_out)) return 16;
-  if (vqmi::gemv_mf_takes(v.rows, v.cols, v.d, 2, cus, plain_out)) return small ? 6 : 4;
+  const int mf = vqmi::gemv_mf_max_tokens(v.rows, v.cols, v.d, vqmi::device_cus(), plain_out);
+  if (mf > 4) return mf;
+  if (mf == 4) return small ? 6 : 4;
   if (small) return 6;
   if (v.d == 8) return 4;
   return 2;

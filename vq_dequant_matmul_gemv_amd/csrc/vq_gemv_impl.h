@@ -126,6 +126,10 @@ constexpr int kGemvMfTokens = 4;
 // rounding) into the B operand, each item's sums added into y.
 constexpr int kGemvMfWideTokens = 16;
 __host__ __device__ constexpr int gemv_mf_max_c(int D) { return D == 2 ? 5 : (D == 4 ? 3 : 1); }
+static_assert(gemv_mf_slice_cols(2) == 4 * gemv_mf_max_c(2) * 16 * 2 &&
+                  gemv_mf_slice_cols(4) == 4 * gemv_mf_max_c(4) * 16 * 4 &&
+                  gemv_mf_slice_cols(8) == 4 * gemv_mf_max_c(8) * 16 * 8,
+              "gemv_mf_slice_cols: one pass of 4 lanes x gemv_mf_max_c chunks per row");
 // x bytes per token a block stages (the longest rows MF takes: 8 passes of 4 * C chunks)
 __host__ __device__ constexpr int gemv_mf_x_bytes(int D) { return 8 * 4 * gemv_mf_max_c(D) * 32 * D; }
 #ifndef VQMI_MF_RING_EXTRA

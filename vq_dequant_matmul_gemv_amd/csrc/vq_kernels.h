@@ -53,15 +53,27 @@ hipError_t launch_gemv(const TensorView& w, const IoSpec& io, const void* x, int
 hipError_t launch_gemm(const TensorView& w, const IoSpec& io, const void* x, int T, void* y, hipStream_t s);
 
 // The matrix-core GEMV (vq_gemv_impl.h, MF) takes dense calls of two or more
-// tokens whose rows give every CU at least one 16-row group.  Rows longer
-// than its passes hold in one block (d = 2: 5120 columns, d = 4: 6144, d = 8:
-// 4096) run as column slices added into y, so they need a plain fp32 output
-// (plain_out: fp32 y and no fused output step).
+// tokens whose rows give every CU at least one 16-row group: up to four
+// tokens on rows that fit one block's passes (d = 2: 5120 columns, d = 4:
+// 6144, d = 8: 4096), and, for a plain fp32 output (fp32 y, no fused output
+// step), longer rows in column slices added into y and up to 16 tokens in its
+// 16-token mode.  That mode's column slices are one pass wide (d = 2: 640
+// columns, d = 4: 768, d = 8: 512) and every slice adds each output once
+// more, atomically; the tokens it takes are capped at 160 / slices (measured:
+// 5120x17408, 23 slices at d = 4: 16.3 against 18.2 us for the GEMM at T = 5,
+// 26.6 against 22.3 at T = 16; 17408x5120, 7 slices: 20.9 against 22.1 at T =
+// 16).
 __host__ __device__ inline int gemv_mf_max_cols(int d) { return d == 2 ? 5120 : (d == 4 ? 6144 : 4096); }
-// Above four tokens it runs its 16-token mode, whose items add into y: a
-// plain fp32 output again.
+__host__ __device__ constexpr int gemv_mf_slice_cols(int d) { return d == 2 ? 640 : (d == 4 ? 768 : 512); }
+inline int gemv_mf_max_tokens(int rows, int cols, int d, int cus, bool plain_out) {
+  if (rows < 16 * cus) return 0;
+  if (!plain_out) return cols <= gemv_mf_max_cols(d) ? 4 : 0;
+  const int n_sl = (cols + gemv_mf_slice_cols(d) - 1) / gemv_mf_slice_cols(d);
+  const int wide = 160 / n_sl;
+  return wide > 16 ? 16 : (wide < 4 ? 4 : wide);
+}
 inline bool gemv_mf_takes(int rows, int cols, int d, int T, int cus, bool plain_out) {
-  return T >= 2 && rows >= 16 * cus && ((T <= 4 && cols <= gemv_mf_max_cols(d)) || plain_out);
+  return T >= 2 && T <= gemv_mf_max_tokens(rows, cols, d, cus, plain_out);
 }
 // Compute units of the current device (cached on first use).
 int device_cus();
