@@ -185,13 +185,14 @@ vq_status vq_dequant(const vq_tensor *w, int32_t expert, uint16_t *w_out, void *
  * (the fused decode-and-matmul of paper §3.4; two tokens: a two-token
  * speculative verify step, 35B card, Experimental MTP).  On matrices of at
  * least 16 rows per compute unit, 2 to 4 tokens (up to 16 when y is plain
- * fp32) run on its matrix-core variant, whose partial sums of long rows'
- * column slices (and, above four tokens, of every item) are added
+ * fp32: 160 / its one-pass column slices, d = 2: 640 columns, d = 4: 768,
+ * d = 8: 512) run on its matrix-core variant, whose partial sums of long
+ * rows' column slices (and, above four tokens, of every item) are added
  * atomically into y, zeroed first: those outputs may differ in the last
- * bits from run to run.  Above a token count measured per shape (16 or 4
- * there; otherwise 2 for d = 2/4 matrices, 4 for d = 8, 6 for matrices of at
- * most 16M weights) vq_gemv runs the MFMA kernel of vq_gemm instead, with
- * the same result contract.
+ * bits from run to run.  Above a token count measured per shape (that cap
+ * there; otherwise 2 for d = 2/4 matrices, 4 for d = 8, 6 for matrices of
+ * at most 16M weights) vq_gemv runs the MFMA kernel of vq_gemm instead,
+ * with the same result contract.
  */
 vq_status vq_gemv(const vq_tensor *w, const uint16_t *x, int32_t T, float *y, void *stream);
 
