@@ -7,7 +7,8 @@ weights = 4.25 bits per weight):
   decode : gate and up (which share their input) as one vq_moe_gemv launch
            over the two-expert stack of them, ids {0, 1}; vq_gemv on down;
            T = 1 token
-  prefill: vq_gemm on gate, up, down at T = 2048 tokens
+  prefill: vq_gemm on the same gate+up stack (one launch, y [T][2][rows]) and
+           on down, at T = 2048 tokens
 Inputs are seeded synthetic tensors (codes uniform, codebook N(0, 0.02), scales
 U[0.5, 1.5], x N(0, 1)) already resident in HBM.  The weights are replicated
 so the per-step rotation touches >= 1 GiB and every call streams from HBM, not
@@ -55,7 +56,7 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=1024,
                     help="rows of the gate matrix the CPU oracle sample covers")
     ap.add_argument("--profile-gate", action="store_true",
-                    help="run only a few gate GEMV and GEMM launches (for rocprofv3 --pmc passes)")
+                    help="run only a few gate GEMV and gate+up stacked GEMM launches (for rocprofv3 --pmc passes)")
     ap.add_argument("--profile-sweep", choices=["A", "B"], default=None,
                     help="run only a few config-4 launches of matrix A (17408x5120) or B (5120x17408), d=4 K=256: "
                          "GEMV at T=1 and GEMM at T=4096 (for rocprofv3 --pmc passes)")
@@ -641,7 +642,8 @@ def main():
 
     # Gate and up share their input, so they are stored as one two-expert
     # stack (per-expert codebooks) and decoded by one routed launch with ids
-    # {0, 1}; the prefill GEMMs take per-expert views of the same stack.
+    # {0, 1}, and run by one vq_gemm launch over the stack in prefill; the
+    # single-tensor figures take per-expert views of the same stack.
     def stack_gate_up(src_gate, src_up):
         t = [binding.VQTensor.from_host(h, sg) for h in (src_gate, src_up)]
         return binding.VQTensor(torch.stack([t[0].codes, t[1].codes]), torch.stack([t[0].codebook, t[1].codebook]),
@@ -672,6 +674,7 @@ def main():
     yd_g = torch.empty((DECODE_T, sg.rows), dtype=torch.float32, device=dev)
     yd_dn = torch.empty((DECODE_T, sd.rows), dtype=torch.float32, device=dev)
     yp = {n: torch.empty((PREFILL_T, specs[n].rows), dtype=torch.float32, device=dev) for n in names}
+    yp_gu = torch.empty((PREFILL_T, 2, sg.rows), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     def dec_gate_up(i):
@@ -687,9 +690,11 @@ def main():
     def pre_gate(i):
         binding.gemm(reps[i]["gate"], xp_gu, yp["gate"])
 
+    def pre_gate_up(i):
+        binding.gemm(reps[i]["gate_up"], xp_gu, yp_gu)
+
     def pre_pass(i):
-        pre_gate(i)
-        binding.gemm(reps[i]["up"], xp_gu, yp["up"])
+        pre_gate_up(i)
         binding.gemm(reps[i]["down"], xp_dn, yp["down"])
 
     if args.profile_gate:
@@ -698,10 +703,10 @@ def main():
         for i in range(4):
             dec_gate(i % REPLICAS)
         for i in range(2):
-            pre_gate(i % REPLICAS)
+            pre_gate_up(i % REPLICAS)
         torch.cuda.synchronize()
-        print("profile-gate: 4 gate+up routed GEMVs (T=1), 4 gate GEMVs (T=1), 2 gate GEMMs (T=2048)",
-              flush=True)
+        print("profile-gate: 4 gate+up routed GEMVs (T=1), 4 gate GEMVs (T=1), 2 gate+up stacked GEMMs "
+              "(T=2048)", flush=True)
         return
 
     dec_bytes = {n: tensor_bytes(specs[n], DECODE_T) for n in names}
@@ -727,13 +732,15 @@ def main():
         dec_pass(i)
         dec_gate(i)
         pre_pass(i)
+        pre_gate(i)
     torch.cuda.synchronize()
     g_dec = [capture([(dec_pass, i)]) for i in range(REPLICAS)]
     g_dec_all = capture([(dec_pass, i) for i in range(REPLICAS)])
     g_pre = [capture([(pre_pass, i)]) for i in range(REPLICAS)]
     g_burst = {"gate_up": (capture([(dec_gate_up, i % REPLICAS) for i in range(BURST)]), BURST),
                "gate": (capture([(dec_gate, i % REPLICAS) for i in range(BURST)]), BURST),
-               "gemm": (capture([(pre_gate, i) for i in range(REPLICAS)]), REPLICAS)}
+               "gemm": (capture([(pre_gate_up, i) for i in range(REPLICAS)]), REPLICAS),
+               "gemm_gate": (capture([(pre_gate, i) for i in range(REPLICAS)]), REPLICAS)}
     torch.cuda.synchronize()
 
     def decode_passes(n):
@@ -790,7 +797,9 @@ def main():
     gu_bytes = dec_bytes["gate"] + dec_bytes["up"]
     gu_gbps = gu_bytes / bursts["gate_up"] / 1e9
     gate_gbps = dec_bytes["gate"] / bursts["gate"] / 1e9
-    gate_tflops = pre_flops["gate"] / bursts["gemm"] / 1e12
+    gu_tflops = (pre_flops["gate"] + pre_flops["up"]) / bursts["gemm"] / 1e12
+    # the stacked launch reads x once and writes both outputs
+    gu_pre_bytes = 2 * tensor_bytes(sg, PREFILL_T) - PREFILL_T * sg.cols * 2
 
     out = {
         "metric": "VQ-GEMV effective HBM GB/s (% of peak) at batch 1; prefill VQ-GEMM TFLOP/s",
@@ -808,7 +817,7 @@ def main():
         "config": {"workload": WORKLOAD, "decode_tokens": DECODE_T, "prefill_tokens": PREFILL_T,
                    "tensors": "gate,up [17408x5120]; down [5120x17408]; d=2 K=256 group=64 (4.25 bpw)",
                    "decode_calls": "gate+up: one routed GEMV over the two-expert stack, ids {0,1}; down: GEMV",
-                   "prefill_calls": "gate, up, down: one GEMM each",
+                   "prefill_calls": "gate+up: one GEMM over the two-expert stack; down: GEMM",
                    "weight_replicas": REPLICAS, "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * dec_gbps / HBM_PEAK_GBPS, 2),
         "decode_ms_per_step": round(dec_time / args.steps * 1e3, 4),
@@ -817,7 +826,8 @@ def main():
                     "ms_per_step": round(pre_time / args.steps * 1e3, 4)},
         "kernel_us": {"gemv_gate_up_T1": round(bursts["gate_up"] * 1e6, 2),
                       "gemv_gate_T1": round(bursts["gate"] * 1e6, 2),
-                      "gemm_gate_T2048": round(bursts["gemm"] * 1e6, 2)},
+                      "gemm_gate_up_T2048": round(bursts["gemm"] * 1e6, 2),
+                      "gemm_gate_T2048": round(bursts["gemm_gate"] * 1e6, 2)},
         "roofline": {"bound": "hbm", "kernel": "vq_moe_gemv over the gate+up stack (T=1, ids {0,1})",
                      "achieved": round(gu_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
@@ -828,11 +838,11 @@ def main():
                                    "frac": round(gate_gbps / HBM_PEAK_GBPS, 4),
                                    "traffic": measured_traffic("vq_gemv_kernel<2, 8, 64, 5, 2, false,", GATE_TAG),
                                    "algorithmic_bytes": dec_bytes["gate"]},
-        "roofline_prefill": {"bound": "mfma", "kernel": "vq_gemm (gate, T=2048)",
-                             "achieved": round(gate_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
-                             "unit": "TFLOP/s", "frac": round(gate_tflops / MFMA_F16_PEAK_TFLOPS, 4),
+        "roofline_prefill": {"bound": "mfma", "kernel": "vq_gemm over the gate+up stack (T=2048)",
+                             "achieved": round(gu_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(gu_tflops / MFMA_F16_PEAK_TFLOPS, 4),
                              "traffic": measured_traffic("vq_gemm_kernel<2, 8, 64", GATE_TAG),
-                             "algorithmic_bytes": tensor_bytes(specs["gate"], PREFILL_T)},
+                             "algorithmic_bytes": gu_pre_bytes},
     }
     if not args.no_sweep:
         # config 4 (the 17408x5120 / 5120x17408 d=4 K=256 sweep): its barred

@@ -208,6 +208,16 @@ vq_status vq_gemv(const vq_tensor *w, const uint16_t *x, int32_t T, float *y, vo
  * differ in the last bits from run to run (fp32 addition order), within the
  * stated tolerance; all others are deterministic.  The environment variable
  * VQMI_GEMM_TILE = 32 or 128 forces the tile shape (for tests).
+ * A stack of E experts (num_experts = E > 1; codebook_per_expert = 1 keeps
+ * each tensor's own codebook) multiplies every expert by the same x: y is
+ * [T][E][rows] (rows / 2 under SWIGLU), y[t][e] = W_e x[t], each expert's
+ * rows computed exactly as a call on that expert alone with the same tile
+ * shape and split.  This runs an MLP's gate and up projections, which share
+ * their input (paper §2.1: the MLP trio), as one launch whose tiles fill the
+ * GPU's rounds together instead of leaving two partial last rounds.  The
+ * tile shape and split are chosen for the whole stack, so they (and, for
+ * split tiles, the last bits) can differ from separate calls.  T * E at most
+ * 2^24; vq_gemv takes no stack (VQ_ERR_SHAPE).
  */
 vq_status vq_gemm(const vq_tensor *w, const uint16_t *x, int32_t T, float *y, void *stream);
 

@@ -251,9 +251,11 @@ def _dense(fn, fn_ex, w: VQTensor, x, y, stream, y_dtype=None, epilogue=None):
     ycols = w.rows // 2 if epilogue == "swiglu" else w.rows
     if epilogue == "combine":
         raise ValueError("the combine applies to routed calls only")
+    # a stack of experts (vq_gemm only): y[t][e] = W_e x[t]
+    yshape = (T, ycols) if w.num_experts == 1 else (T, w.num_experts, ycols)
     if y is None:
-        y = torch.empty((T, ycols), dtype=y_dtype, device=x.device)
-    _check_out(y, y_dtype, (T, ycols))
+        y = torch.empty(yshape, dtype=y_dtype, device=x.device)
+    _check_out(y, y_dtype, yshape)
     _dev_check(x, y, device=w.device)
     cs = w.cstruct()
     io = _io(x, y_dtype, epilogue, None)
@@ -271,7 +273,8 @@ def gemv(w: VQTensor, x, y=None, stream=None, y_dtype=None, epilogue=None):
 
 
 def gemm(w: VQTensor, x, y=None, stream=None, y_dtype=None, epilogue=None):
-    """y = x W^T through vq_gemm (MFMA); options as for gemv."""
+    """y = x W^T through vq_gemm (MFMA); options as for gemv.  On a stack of
+    E experts, y is [T][E][rows]: every expert times the same x."""
     return _dense(LIB.vq_gemm, LIB.vq_gemm_ex, w, x, y, stream, y_dtype, epilogue)
 
 

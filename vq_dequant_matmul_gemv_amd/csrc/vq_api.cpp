@@ -246,15 +246,21 @@ static vq_status dense_call(const vq_tensor* w, const vq_io* io, const void* x, 
   vq_status st = check_tensor(w, &v);
   if (st != VQ_OK) return st;
   const char* name = gemv ? "vq_gemv" : "vq_gemm";
-  if (w->num_experts != 1)
-    return fail(VQ_ERR_SHAPE, "%s needs a dense tensor (num_experts=%d); use the routed call", name,
-                w->num_experts);
+  if (gemv && w->num_experts != 1)
+    return fail(VQ_ERR_SHAPE,
+                "vq_gemv needs a dense tensor (num_experts=%d); vq_gemm takes a stack, the routed calls pick "
+                "experts per token", w->num_experts);
+  if ((int64_t)w->num_experts * w->rows > (1 << 28))
+    return fail(VQ_ERR_SHAPE, "vq_gemm: a stack of %d x %d rows is too large", w->num_experts, w->rows);
   vqmi::IoSpec ios;
   st = check_io(io, w, gemv ? Call::kGemv : Call::kGemm, &ios);
   if (st != VQ_OK) return st;
   if (T < 0) return fail(VQ_ERR_SHAPE, "T=%d must be >= 0", T);
-  if (T > (1 << 24)) return fail(VQ_ERR_SHAPE, "T=%d too large", T);
+  if ((int64_t)T * w->num_experts > (1 << 24))
+    return fail(VQ_ERR_SHAPE, "T=%d too large (times %d stacked experts)", T, w->num_experts);
   if (T == 0) return VQ_OK;
+  if ((int64_t)w->num_experts * ((w->rows + 31) / 32) * ((T + 31) / 32) > (1 << 30))
+    return fail(VQ_ERR_SHAPE, "%s: T=%d x %d x %d rows makes too many tiles", name, T, w->num_experts, w->rows);
   st = check_xy(x, y, "y");
   if (st != VQ_OK) return st;
   if (!gemv || T > gemv_token_limit(v, ios))  // above the crossover the MFMA kernel is faster

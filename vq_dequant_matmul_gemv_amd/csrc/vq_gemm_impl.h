@@ -161,6 +161,10 @@ struct GemmArgs {
   // each own one of rem_split K slices of a remaining tile and add into y
   // (zeroed beforehand) atomically.
   int n_full, rem_split;
+  // dense stack of n_stack experts sharing x: the row tiles of expert e follow
+  // those of expert e - 1 (n_row_tiles counts them all) and token t's outputs
+  // of expert e are y row t * n_stack + e
+  int n_stack;
 };
 
 // Tile t -> (row tile, token tile): groups of 4 row tiles x all token tiles,
@@ -241,11 +245,14 @@ __global__ __launch_bounds__(SH::kThreads, 1) void vq_gemm_kernel(GemmArgs a) {
   }
   int rt, tt;
   gemm_tile_coords(tile, a.n_row_tiles, a.n_tok_tiles, rt, tt);
+  const int nrt_e = a.n_row_tiles / a.n_stack;  // row tiles per expert of a stack
+  const int expert = rt / nrt_e;
+  rt -= expert * nrt_e;
   const int tok_base = tt * SH::kTokens;
   const int count = min(SH::kTokens, a.T - tok_base);
   using TS = SH;
   constexpr bool MOE = false, TW = WIDE;
-  constexpr int expert = 0, first = 0;
+  constexpr int first = 0;
 #include "vq_gemm_tile.inc"
 }
 
@@ -330,18 +337,23 @@ __global__ __launch_bounds__(SH::kThreads, 1) void vq_moe_gemm_kernel(GemmArgs a
 
 // Zero the y region of tiles [first, first + gridDim.x), gridDim.y blocks per
 // tile, 16-byte stores where the rows allow (a kernel rather than
-// hipMemsetAsync, so it can sit in a graph).
+// hipMemsetAsync, so it can sit in a graph).  Tiles and y rows of a stack of
+// n_stack experts as in the dense kernel.
 static __global__ __launch_bounds__(256) void vq_zero_tiles_kernel(float* y, int rows, int T, int first, int n_row_tiles,
-                                                            int n_tok_tiles, int tile_rows, int tile_tokens) {
+                                                            int n_tok_tiles, int tile_rows, int tile_tokens,
+                                                            int n_stack) {
   int rt, tt;
   gemm_tile_coords(first + (int)blockIdx.x, n_row_tiles, n_tok_tiles, rt, tt);
+  const int nrt_e = n_row_tiles / n_stack;
+  const int e = rt / nrt_e;
+  rt -= e * nrt_e;
   const int r0 = rt * tile_rows, nr = min(tile_rows, rows - r0);
   const int t0 = tt * tile_tokens, nt = min(tile_tokens, T - t0);
   const bool vec = (rows & 3) == 0;  // r0 is a multiple of tile_rows (of 32)
   const int per_row = vec ? (nr + 3) / 4 : nr;
   for (int i = blockIdx.y * blockDim.x + threadIdx.x; i < nt * per_row; i += gridDim.y * blockDim.x) {
     const int t = i / per_row, k = i - t * per_row;
-    float* yr = y + (int64_t)(t0 + t) * rows + r0;
+    float* yr = y + ((int64_t)(t0 + t) * n_stack + e) * rows + r0;
     if (vec && 4 * k + 3 < nr) {
       *reinterpret_cast<float4_t*>(yr + 4 * k) = float4_t{0.f, 0.f, 0.f, 0.f};
     } else if (vec) {
@@ -414,6 +426,7 @@ GemmArgs base_args(const TensorView& w, const IoSpec& io, const void* x, void* y
   a.spr = w.cols / G;
   a.n_full = 0;
   a.rem_split = 1;
+  a.n_stack = 1;
   return a;
 }
 
@@ -440,8 +453,8 @@ inline double gemm_tile_us(bool thin, int D, int cols) {
 // Best K split of the last partial round for tiles of `rows_t` rows x
 // `tok_t` tokens (split 1 when the output cannot take atomic adds).
 inline GemmPlan gemm_plan(int T, int rows, int cols, int D, bool thin, int rows_t, int tok_t, int cus,
-                          bool split_ok) {
-  const int n_row_tiles = (rows + rows_t - 1) / rows_t;
+                          bool split_ok, int n_stack) {
+  const int n_row_tiles = n_stack * ((rows + rows_t - 1) / rows_t);
   const int n_tok_tiles = (T + tok_t - 1) / tok_t;
   const int tiles = n_row_tiles * n_tok_tiles;
   const double t_tile = gemm_tile_us(thin, D, cols);
@@ -450,7 +463,7 @@ inline GemmPlan gemm_plan(int T, int rows, int cols, int D, bool thin, int rows_
   if (rem == 0 || !split_ok) return best;
   // each K slice keeps at least 512 columns (1024 for d = 8)
   const int max_split = std::max(1, cols / (D == 8 ? 1024 : 512));
-  const double rem_outputs = (double)rem / tiles * (double)T * rows;  // outputs of the split tiles
+  const double rem_outputs = (double)rem / tiles * (double)T * rows * n_stack;  // outputs of the split tiles
   for (int sp = 2; sp <= std::min(32, max_split); ++sp) {
     const double us = (double)(full / cus) * t_tile + (double)((rem * sp + cus - 1) / cus) * t_tile / sp + 5.0 +
                       4e-6 * rem_outputs * sp;
@@ -464,7 +477,7 @@ inline GemmPlan gemm_plan(int T, int rows, int cols, int D, bool thin, int rows_
 // into a zeroed y (their fp32 addition order then varies between runs).
 template <int D, int B, int G, class SH>
 hipError_t gemm_dense(GemmArgs a, int split, hipStream_t s) {
-  a.n_row_tiles = (a.rows + SH::kRows - 1) / SH::kRows;
+  a.n_row_tiles = a.n_stack * ((a.rows + SH::kRows - 1) / SH::kRows);
   a.n_tok_tiles = (a.T + SH::kTokens - 1) / SH::kTokens;
   const int tiles = a.n_row_tiles * a.n_tok_tiles;
   const int cus = num_cus();
@@ -479,7 +492,7 @@ hipError_t gemm_dense(GemmArgs a, int split, hipStream_t s) {
   if (rem > 0) {
     hipLaunchKernelGGL(vq_zero_tiles_kernel, dim3(rem, std::max(1, 2 * cus / rem)), dim3(256), 0, s,
                        static_cast<float*>(a.y), a.rows,
-                       a.T, full, a.n_row_tiles, a.n_tok_tiles, SH::kRows, SH::kTokens);
+                       a.T, full, a.n_row_tiles, a.n_tok_tiles, SH::kRows, SH::kTokens, a.n_stack);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -497,12 +510,15 @@ template <int D, int B, int G>
 hipError_t gemm_geom(const TensorView& w, const IoSpec& io, const void* x, int T, void* y, hipStream_t s) {
   GemmArgs a = base_args(w, io, x, y, G, D, B);
   a.T = T;
+  a.n_stack = w.num_experts;  // a stack: every expert times the same x
   const int cus = num_cus();
   const bool split_ok = io.epi == kEpiNone && io.y_kind == kOutF32;  // K slices add fp32 sums
   const char* force = getenv("VQMI_GEMM_TILE");
   const int forced = force ? atoi(force) : 0;
-  const GemmPlan thin = gemm_plan(T, w.rows, w.cols, D, true, GemmSmallT::kRows, GemmSmallT::kTokens, cus, split_ok);
-  const GemmPlan large = gemm_plan(T, w.rows, w.cols, D, false, GemmLargeT::kRows, GemmLargeT::kTokens, cus, split_ok);
+  const GemmPlan thin = gemm_plan(T, w.rows, w.cols, D, true, GemmSmallT::kRows, GemmSmallT::kTokens, cus, split_ok,
+                                  a.n_stack);
+  const GemmPlan large = gemm_plan(T, w.rows, w.cols, D, false, GemmLargeT::kRows, GemmLargeT::kTokens, cus,
+                                   split_ok, a.n_stack);
   if (forced == GemmLargeT::kTokens) return gemm_dense<D, B, G, GemmLargeT>(a, large.split, s);
   if (forced == GemmSmallT::kTokens || T <= GemmSmallT::kTokens || thin.us < large.us)
     return gemm_dense<D, B, G, GemmSmallT>(a, thin.split, s);
