@@ -68,6 +68,35 @@ def test_dense_mlp_trio(name, fn, T):
     _dense_case("dense_mlp_5120x17408_d2k256", name, fn, T)
 
 
+@pytest.mark.parametrize("fn,T", [("moe_gemv", 1), ("gemm", 2048)])
+def test_dense_mlp_gate_up_stack(fn, T):
+    """Gate and up as the benchmark runs them: one two-expert stack with
+    per-expert codebooks, decoded by one routed GEMV with ids {0, 1} and
+    prefilled by one vq_gemm over the stack (y [T][2][rows])."""
+    import torch
+    from vq_dequant_matmul_gemv_amd import binding
+    wl = "dense_mlp_5120x17408_d2k256"
+    spec = synth.WORKLOADS[wl]["tensors"]["gate"]
+    arrs = {n: synth.tensor(spec, wl, n) for n in ("gate", "up")}
+    t = [upload(arrs[n], spec) for n in ("gate", "up")]
+    w = binding.VQTensor(torch.stack([t[0].codes, t[1].codes]), torch.stack([t[0].codebook, t[1].codebook]),
+                         torch.stack([t[0].scales, t[1].scales]), spec.rows, spec.cols, spec.d, spec.log2_k,
+                         spec.group, 2, True)
+    del t
+    x = synth.activations((T, spec.cols), wl, "x", "gate_up", T)
+    announce(wl, "gate+up stack", fn, "T", T)
+    if fn == "moe_gemv":
+        ids = torch.tensor([[0, 1]] * T, dtype=torch.int32, device="cuda")
+        y = binding.moe_gemv(w, to_dev(x), ids).cpu().numpy()
+    else:
+        y = binding.gemm(w, to_dev(x)).cpu().numpy()
+    assert y.shape == (T, 2, spec.rows) and np.isfinite(y).all()
+    for e, n in enumerate(("gate", "up")):
+        rsel = _sample_rows(spec.rows, wl, "stack", n, T)
+        err = row_rel_err(y[:, e][:, rsel], _dense_ref(arrs[n], spec, x, rsel))
+        assert err <= TOL, (n, err)
+
+
 @pytest.mark.parametrize("name", ["A", "B"])
 @pytest.mark.parametrize("fn,T", [("gemv", 1), ("gemv", 2), ("gemv", 3), ("gemv", 4), ("gemv", 16), ("gemm", 16),
                                   ("gemm", 256), ("gemm", 4096)])
