@@ -180,6 +180,9 @@ vq_status vq_dequant(const vq_tensor *w, int32_t expert, uint16_t *w_out, void *
  * Decode-shaped product y = x W^T for a dense tensor (num_experts == 1):
  *   x: device [T][cols] fp16 bits, 16-byte aligned;
  *   y: device [T][rows] fp32, 16-byte aligned.
+ * A stack of E experts (num_experts = E > 1) multiplies every expert by the
+ * same x in one launch, y [T][E][rows] (y[t][e] = W_e x[t]), as vq_gemm
+ * describes: an MLP's gate and up for a few decode tokens.
  * T >= 0 (T == 0 enqueues nothing).  Any T is accepted.  The streaming
  * kernel reads every code once per token slice: the fast path for small T
  * (the fused decode-and-matmul of paper §3.4; two tokens: a two-token
@@ -217,7 +220,7 @@ vq_status vq_gemv(const vq_tensor *w, const uint16_t *x, int32_t T, float *y, vo
  * GPU's rounds together instead of leaving two partial last rounds.  The
  * tile shape and split are chosen for the whole stack, so they (and, for
  * split tiles, the last bits) can differ from separate calls.  T * E at most
- * 2^24; vq_gemv takes no stack (VQ_ERR_SHAPE).
+ * 2^24.
  */
 vq_status vq_gemm(const vq_tensor *w, const uint16_t *x, int32_t T, float *y, void *stream);
 

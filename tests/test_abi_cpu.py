@@ -74,7 +74,7 @@ def _gemv(b, t, x=0x40000, T=1, y=0x50000):
     (dict(cols=192, d=4, codebook_elems=1024), "VQ_ERR_SHAPE"),   # (cols/d) % 32
     (dict(codebook_elems=256), "VQ_ERR_SHAPE"),          # sliced codebook fails loudly
     (dict(codebook_elems=1024), "VQ_ERR_SHAPE"),
-    (dict(num_experts=2), "VQ_ERR_SHAPE"),               # dense entry point, stacked tensor
+    (dict(num_experts=1 << 25), "VQ_ERR_SHAPE"),         # a stack of more than 2^28 rows
     (dict(codebook_per_expert=2), "VQ_ERR_SHAPE"),
     (dict(code_words=16 * 48), "VQ_ERR_SHAPE"),          # codes packed with 12-bit codes
     (dict(code_words=511), "VQ_ERR_SHAPE"),              # short code buffer
@@ -88,6 +88,13 @@ def test_gemv_rejects(b, kw, status):
     assert b.STATUS_NAMES[st] == status, b.LIB.vq_last_error()
     assert b.LIB.vq_last_error()
     assert b.LIB.vq_status_name(st).decode() == status
+
+
+def test_stack_token_limit(b):
+    # a stack multiplies the tokens by its experts: T * E at most 2^24
+    st = _gemv(b, _t(b, num_experts=2), T=(1 << 23) + 1)
+    assert b.STATUS_NAMES[st] == "VQ_ERR_SHAPE", b.LIB.vq_last_error()
+    assert "stacked" in b.LIB.vq_last_error().decode()
 
 
 def test_sliced_codebook_message(b):

@@ -1,6 +1,6 @@
-"""GPU parity of vq_gemm on a stack of experts: every expert times the same x,
-y[t][e] = W_e x[t] (an MLP's gate and up projections, which share their
-input, in one launch).
+"""GPU parity of vq_gemm and vq_gemv on a stack of experts: every expert
+times the same x, y[t][e] = W_e x[t] (an MLP's gate and up projections,
+which share their input, in one launch).
 
 Each row tile takes its own expert's codes, scales and codebook, and writes
 row t * E + e of y; split tiles of a last, partial round zero and add into
@@ -9,7 +9,11 @@ filled with NaN beforehand (every output must be written), over ragged row
 counts, token counts spanning several tiles with a ragged tail, both tile
 shapes, shared and per-expert codebooks, split last rounds, fp16 / bf16
 outputs (never split: bit-identical to one call per expert) and the SwiGLU
-step within each expert."""
+step within each expert.  The GEMV's stack runs the experts' row blocks
+side by side in one grid: its streaming path (one and two tokens per grid
+slice, column slices added in turn), its matrix-core path (block-diagonal
+and 16-token modes, column slices added atomically) and the hand-off to the
+stacked GEMM above its token limit."""
 import numpy as np
 import pytest
 
@@ -95,10 +99,53 @@ def test_stack_gemm_swiglu_within_each_expert():
         assert row_rel_err(h[:, e], O.swiglu_ref(_ref(arrs, spec, e, x, True))) <= TOL + 2.0 ** -8, e
 
 
-def test_stack_rejected_by_gemv():
-    """vq_gemv takes no stack: a clear error, nothing launched."""
+@pytest.mark.parametrize("E,rows,cols,d,b,g,cbpe,Ts", [
+    (2, 4133, 2048, 4, 8, 64, True, (1, 2, 3, 4, 9, 16, 21)),  # matrix-core modes; T = 21: the stacked GEMM
+    (2, 1000, 2048, 2, 8, 64, True, (1, 2, 5)),                # streaming path, two-token slices
+    (3, 1500, 10240, 2, 12, 128, False, (1, 3)),               # shared codebook; two matrix-core column slices
+    (2, 512, 24576, 4, 8, 64, True, (1, 2)),                   # streaming path in two column slices
+])
+def test_stack_gemv_matches_oracle(E, rows, cols, d, b, g, cbpe, Ts):
+    import torch
     from vq_dequant_matmul_gemv_amd import binding
-    spec, arrs, w = _stack(2, 64, 512, 2, 8, 64, True, ("stack-gemv",))
-    x = to_dev(synth.activations((1, 512), "stack-gemv"))
-    with pytest.raises(Exception, match="stack"):
-        binding.gemv(w, x)
+    spec, arrs, w = _stack(E, rows, cols, d, b, g, cbpe, ("stack-gemv", E, rows, cols, d, b, g))
+    for T in Ts:
+        x = synth.activations((T, cols), "stack-gemv", E, rows, cols, T)
+        announce("stack-gemv", E, rows, cols, d, b, g, T)
+        y = torch.full((T, E, rows), float("nan"), device="cuda")
+        binding.gemv(w, to_dev(x), y)
+        got = y.cpu().numpy()
+        assert not np.isnan(got).any(), T
+        for e in range(E):
+            assert row_rel_err(got[:, e], _ref(arrs, spec, e, x, cbpe)) <= TOL, (T, e)
+
+
+def test_stack_gemv_one_token_bit_identical_to_per_expert_and_routed_calls():
+    """One token on the streaming path: every row's arithmetic is that of a
+    call on its expert alone, and of the routed call with ids {0, 1}."""
+    import torch
+    from vq_dequant_matmul_gemv_amd import binding
+    E, rows, cols = 2, 4133, 5120
+    spec, arrs, w = _stack(E, rows, cols, 2, 8, 64, True, ("stack-gemv-bits",))
+    x = to_dev(synth.activations((1, cols), "stack-gemv-bits"))
+    announce("stack-gemv-bits")
+    y = binding.gemv(w, x)
+    yr = binding.moe_gemv(w, x, torch.tensor([[0, 1]], dtype=torch.int32, device="cuda"))
+    assert torch.equal(y.view(torch.int32), yr.view(torch.int32))
+    for e in range(E):
+        assert torch.equal(y[:, e].view(torch.int32), binding.gemv(_expert(w, e), x).view(torch.int32)), e
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_stack_gemv_swiglu_bf16(T):
+    """SwiGLU within each expert and a bf16 y on the stacked GEMV."""
+    import torch
+    from vq_dequant_matmul_gemv_amd import binding
+    E, rows, cols = 2, 4134, 2048
+    spec, arrs, w = _stack(E, rows, cols, 4, 8, 64, True, ("stack-gemv-swiglu",))
+    x = synth.activations((T, cols), "stack-gemv-swiglu", T)
+    announce("stack-gemv-swiglu", T)
+    h = binding.gemv(w, to_dev(x), y_dtype=torch.bfloat16, epilogue="swiglu").float().cpu().numpy()
+    assert h.shape == (T, E, rows // 2)
+    for e in range(E):
+        assert row_rel_err(h[:, e], O.swiglu_ref(_ref(arrs, spec, e, x, True))) <= TOL + 2.0 ** -8, e

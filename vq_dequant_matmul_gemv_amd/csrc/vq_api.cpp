@@ -230,9 +230,10 @@ vq_status vq_dequant(const vq_tensor* w, int32_t expert, uint16_t* w_out, void* 
 // GEMV, and the rest wins up to T = 2 (two tokens per slice; 17408x5120 and
 // 5120x17408, d = 2 and 4: 15.9-18.6 us against 17.3-21.7 us for the GEMM).
 static int gemv_token_limit(const vqmi::TensorView& v, const vqmi::IoSpec& io) {
-  const bool small = (int64_t)v.rows * v.cols <= (int64_t)16 << 20;
+  const int rows = v.rows * v.num_experts;  // a stack counts all its experts' rows
+  const bool small = (int64_t)rows * v.cols <= (int64_t)16 << 20;
   const bool plain_out = io.epi == vqmi::kEpiNone && io.y_kind == vqmi::kOutF32;
-  const int mf = vqmi::gemv_mf_max_tokens(v.rows, v.cols, v.d, vqmi::device_cus(), plain_out);
+  const int mf = vqmi::gemv_mf_max_tokens(rows, v.cols, v.d, vqmi::device_cus(), plain_out);
   if (mf > 4) return mf;
   if (mf == 4) return small ? 6 : 4;
   if (small) return 6;
@@ -246,12 +247,8 @@ static vq_status dense_call(const vq_tensor* w, const vq_io* io, const void* x, 
   vq_status st = check_tensor(w, &v);
   if (st != VQ_OK) return st;
   const char* name = gemv ? "vq_gemv" : "vq_gemm";
-  if (gemv && w->num_experts != 1)
-    return fail(VQ_ERR_SHAPE,
-                "vq_gemv needs a dense tensor (num_experts=%d); vq_gemm takes a stack, the routed calls pick "
-                "experts per token", w->num_experts);
   if ((int64_t)w->num_experts * w->rows > (1 << 28))
-    return fail(VQ_ERR_SHAPE, "vq_gemm: a stack of %d x %d rows is too large", w->num_experts, w->rows);
+    return fail(VQ_ERR_SHAPE, "%s: a stack of %d x %d rows is too large", name, w->num_experts, w->rows);
   vqmi::IoSpec ios;
   st = check_io(io, w, gemv ? Call::kGemv : Call::kGemm, &ios);
   if (st != VQ_OK) return st;

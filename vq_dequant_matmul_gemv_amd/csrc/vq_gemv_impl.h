@@ -94,6 +94,10 @@ struct GemvArgs {
   int x_bf16;             // x holds bf16 (converted to fp16 as it is staged)
   int y_kind;             // OutKind
   int epi;                // Epilogue: none; swiglu (rows 2i, 2i + 1 -> y[i]); combine (y[token] += w * row)
+  // dense stack of n_stack experts sharing x: gridDim.x / n_stack row blocks
+  // per expert, expert e's blocks after those of e - 1; token t's outputs of
+  // expert e are y row t * n_stack + e (1 for a plain dense or a routed call)
+  int n_stack;
 };
 
 constexpr int kGemvWaves = 8;                  // two waves per SIMD
@@ -213,8 +217,13 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
   const int rsub = MF ? (lane & 15) : lane >> lg;    // this lane's row within the group
   const int li = MF ? (lane >> 4) : lane & (L - 1);  // this lane's position within the row
 
-  // ---- this block's rows ----
-  const int bid = blockIdx.x;
+  // ---- this block's rows (and, in a dense stack, its expert) ----
+  int bid = blockIdx.x, estack = 0;
+  if constexpr (!MOE) {
+    const int nbx = (int)gridDim.x / a.n_stack;
+    estack = bid / nbx;
+    bid -= estack * nbx;
+  }
   const int unit = 1 + (rows_extra >> 30);
   const int extra = rows_extra & 0x3fffffff;
   const int brow0 = bid * rows_base + min(bid, extra) * unit;
@@ -245,9 +254,14 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
     cb += (int64_t)e * a.cb_estride;
     xb = xs + (int64_t)(a.x_per_slot ? pair : pair / a.top_k) * cols;
   } else {
+    codes += (int64_t)estack * a.code_estride;
+    scales += (int64_t)estack * a.scale_estride;
+    cb += (int64_t)estack * a.cb_estride;
     xb = xs + (int64_t)blockIdx.y * TT * cols;  // TT tokens per grid slice
     yrow = a.tok0 + (int64_t)blockIdx.y * TT;
   }
+  // y row of this slice's token u (routed: the pair's row)
+  auto y_row = [&](int u) -> int64_t { return MOE ? yrow : (yrow + u) * a.n_stack + estack; };
   // tokens of this slice (an odd token count leaves the last slice one short)
   const int ntok = MOE ? 1 : min(TT, a.T - (int)yrow);
 
@@ -563,11 +577,11 @@ __global__ __launch_bounds__(kGemvThreads) void vq_gemv_kernel(
                                                              bw[t & 1], dw[t & 1], 0, 0, 0);
         }
         if (rb < brows) {
-          float* yf = reinterpret_cast<float*>(a.y) + yrow * rows + brow0 + rb;
+          float* yf = reinterpret_cast<float*>(a.y) + brow0 + rb;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int tok = 4 * (lane >> 4) + i;
-            if (tok < ntok) atomicAdd(yf + (int64_t)tok * rows, dw[0][i] + dw[1][i]);
+            if (tok < ntok) atomicAdd(yf + y_row(tok) * rows, dw[0][i] + dw[1][i]);
           }
         }
       } else {
@@ -725,7 +739,7 @@ items_done:
         for (int c = 0; c < passes; ++c) v += pieces[(u * brows + r) * passes + c];
         return v;
       };
-      const int64_t ybase = (yrow + u) * yrows;
+      const int64_t ybase = y_row(u) * yrows;
       if (a.epi == kEpiSwiglu) {  // rows 2i (gate) and 2i + 1 (up) -> y[i]
         for (int i = tid; 2 * i < brows; i += NT)
           store_out(a.y, ybase + (brow0 >> 1) + i, swiglu(row_sum(2 * i), row_sum(2 * i + 1)), a.y_kind);
@@ -941,7 +955,7 @@ bool gemv_run_mf(GemvArgs a, int P, int ycount, hipStream_t s, hipError_t* err) 
     return false;
   } else {
     const bool plain_out = a.epi == kEpiNone && a.y_kind == kOutF32;
-    if (!gemv_mf_takes(a.rows, a.cols, D, ycount, num_cus(), plain_out)) return false;
+    if (!gemv_mf_takes(a.rows * a.n_stack, a.cols, D, ycount, num_cus(), plain_out)) return false;
     const bool wide = ycount > kGemvMfTokens;
     const int tt = wide ? kGemvMfWideTokens : kGemvMfTokens;
     const int MC = gemv_mf_max_c(D);
@@ -959,6 +973,8 @@ bool gemv_run_mf(GemvArgs a, int P, int ycount, hipStream_t s, hipError_t* err) 
     a.lanes_log2 = 2;
     a.passes = passes;
     const int ny = (ycount + tt - 1) / tt;
+    // (a stack's experts each take this many: whole rounds of blocks, as
+    // calls one after another would, in one launch)
     const int blocks_fill = std::max(1, num_cus() / std::max(1, ny * n_sl));
     // a block stages the scale groups of its slice, up to two partial ones included
     const int64_t groups = ((int64_t)per * 16 * D + G - 1) / G + 1;
@@ -973,13 +989,13 @@ bool gemv_run_mf(GemvArgs a, int P, int ycount, hipStream_t s, hipError_t* err) 
     a.rows_base = (int)(units / blocks) * unit;
     a.rows_extra = (int)(units - units / blocks * blocks) | (unit == 2 ? 1 << 30 : 0);
     if (n_sl > 1 || wide) {  // the slices (16-token mode: the items) add into y
-      *err = launch_zero(a.y, (size_t)ycount * a.rows * sizeof(float), s);
+      *err = launch_zero(a.y, (size_t)ycount * a.n_stack * a.rows * sizeof(float), s);
       if (*err != hipSuccess) return true;
     }
     for (int y0 = 0; y0 < ny; y0 += 65535) {
       const int yc = std::min(65535, ny - y0);
       a.tok0 = y0 * tt;
-      const dim3 grid((unsigned)blocks, (unsigned)yc, (unsigned)n_sl);
+      const dim3 grid((unsigned)(blocks * a.n_stack), (unsigned)yc, (unsigned)n_sl);
       *err = wide ? gemv_launch<D, B, G, 2, false, kGemvMfWideTokens, true>(a, C, grid, s)
                   : gemv_launch<D, B, G, 2, false, kGemvMfTokens, true>(a, C, grid, s);
       if (*err != hipSuccess) break;
@@ -1001,7 +1017,7 @@ hipError_t gemv_run(GemvArgs a, int P, int ycount, hipStream_t s) {
   const int n_slices = (P + slice_max - 1) / slice_max;
   const int per_slice = (P + n_slices - 1) / n_slices;
   const int ny = (ycount + TT - 1) / TT;                 // grid slices along y
-  const int blocks_fill = std::max(1, num_cus() / std::max(1, ny));
+  const int blocks_fill = std::max(1, num_cus() / std::max(1, ny * a.n_stack));
   for (int sl = 0; sl < n_slices; ++sl) {
     a.q0 = sl * per_slice;
     a.nq = std::min(per_slice, P - a.q0);
@@ -1023,7 +1039,7 @@ hipError_t gemv_run(GemvArgs a, int P, int ycount, hipStream_t s) {
     for (int y0 = 0; y0 < ny; y0 += 65535) {
       const int yc = std::min(65535, ny - y0);
       if (!MOE) a.tok0 = y0 * TT;
-      const dim3 grid((unsigned)blocks, (unsigned)yc);
+      const dim3 grid((unsigned)(blocks * a.n_stack), (unsigned)yc);
       hipError_t e;
       if constexpr (!MOE) {
         if (two) e = gemv_launch<D, B, G, 2, MOE, 2>(a, t.C, grid, s);
@@ -1063,6 +1079,7 @@ hipError_t gemv_geom(const TensorView& w, const IoSpec& io, const void* x, int T
   a.top_k = top_k;
   a.num_experts = w.num_experts;
   a.x_per_slot = x_per_slot;
+  a.n_stack = ids ? 1 : w.num_experts;  // dense: a stack of experts sharing x
   if (ids) {
     a.T = T * top_k;
     return gemv_run<D, B, G, true>(a, P, T * top_k, s);
