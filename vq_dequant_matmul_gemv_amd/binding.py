@@ -268,7 +268,8 @@ def _dense(fn, fn_ex, w: VQTensor, x, y, stream, y_dtype=None, epilogue=None):
 
 def gemv(w: VQTensor, x, y=None, stream=None, y_dtype=None, epilogue=None):
     """y = x W^T through vq_gemv (vq_gemv_ex for bf16 x, a non-fp32 y or an
-    epilogue: "swiglu" on interleaved gate/up rows gives silu(gate) * up)."""
+    epilogue: "swiglu" on interleaved gate/up rows gives silu(gate) * up).
+    On a stack of E experts, y is [T][E][rows]: every expert times the same x."""
     return _dense(LIB.vq_gemv, LIB.vq_gemv_ex, w, x, y, stream, y_dtype, epilogue)
 
 
