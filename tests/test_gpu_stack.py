@@ -149,3 +149,19 @@ def test_stack_gemv_swiglu_bf16(T):
     assert h.shape == (T, E, rows // 2)
     for e in range(E):
         assert row_rel_err(h[:, e], O.swiglu_ref(_ref(arrs, spec, e, x, True))) <= TOL + 2.0 ** -8, e
+
+
+@pytest.mark.parametrize("fn,T", [("gemv", 1), ("gemv", 4), ("gemm", 130)])
+def test_stack_bf16_x(fn, T):
+    """bf16 x (converted to fp16 as it is staged) on both stacked calls."""
+    import torch
+    from vq_dequant_matmul_gemv_amd import binding
+    E, rows, cols = 2, 2080, 2048
+    spec, arrs, w = _stack(E, rows, cols, 4, 8, 64, True, ("stack-bf16",))
+    xb = synth.activations_bf16((T, cols), "stack-bf16", T)
+    xd = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+    announce("stack-bf16", fn, T)
+    y = getattr(binding, fn)(w, xd).cpu().numpy()
+    assert y.shape == (T, E, rows)
+    for e in range(E):
+        assert row_rel_err(y[:, e], _ref(arrs, spec, e, O.bf16_to_f64(xb), True)) <= TOL, e
