@@ -363,10 +363,11 @@ def configs_report(only=""):
         del reps
         torch.cuda.empty_cache()
 
-    def stacked_pair(wl, name, spec, keys, gemm_Ts=()):
+    def stacked_pair(wl, name, spec, keys, gemv_Ts=(), gemm_Ts=()):
         """Two tensors sharing x (gate and up), stacked as two experts with
         per-expert codebooks: at T = 1 one vq_moe_gemv launch with ids {0, 1},
-        at each of gemm_Ts one vq_gemm launch over the stack."""
+        at each of gemv_Ts / gemm_Ts one vq_gemv / vq_gemm launch over the
+        stack."""
         t = [binding.VQTensor.from_host(synth.tensor(spec, *k), spec, device=dev) for k in keys]
         base = binding.VQTensor(torch.stack([t[0].codes, t[1].codes]), torch.stack([t[0].codebook, t[1].codebook]),
                                 torch.stack([t[0].scales, t[1].scales]), spec.rows, spec.cols, spec.d,
@@ -382,14 +383,15 @@ def configs_report(only=""):
         calls = [(lambda w=reps[i % len(reps)]: binding.moe_gemv(w, x, ids, y=y)) for i in range(16)]
         us = timed(calls)
         row(wl, name, "vq_moe_gemv", 1, us, nbytes, 2.0 * 2 * spec.rows * spec.cols)
-        for T in gemm_Ts:
-            xg = torch.from_numpy(synth.activations((T, spec.cols), *keys[0], "x", T)).to(dev)
-            yg = torch.empty((T, 2, spec.rows), dtype=torch.float32, device=dev)
-            calls = [(lambda w=reps[i % len(reps)]: binding.gemm(w, xg, yg)) for i in range(4)]
-            us = timed(calls)
-            tb = 2 * tensor_bytes(spec, T) - T * spec.cols * 2   # x read once
-            row(wl, name.replace("ids {0,1}", "one GEMM"), "vq_gemm", T, us, tb, 2.0 * 2 * T * spec.rows * spec.cols)
-            del xg, yg
+        for fn, Ts, label, n in (("gemv", gemv_Ts, "one GEMV", 16), ("gemm", gemm_Ts, "one GEMM", 4)):
+            for T in Ts:
+                xg = torch.from_numpy(synth.activations((T, spec.cols), *keys[0], "x", T)).to(dev)
+                yg = torch.empty((T, 2, spec.rows), dtype=torch.float32, device=dev)
+                calls = [(lambda w=reps[i % len(reps)]: getattr(binding, fn)(w, xg, yg)) for i in range(n)]
+                us = timed(calls)
+                tb = 2 * tensor_bytes(spec, T) - T * spec.cols * 2   # x read once
+                row(wl, name.replace("ids {0,1}", label), "vq_" + fn, T, us, tb, 2.0 * 2 * T * spec.rows * spec.cols)
+                del xg, yg
         del reps
         torch.cuda.empty_cache()
 
@@ -471,7 +473,7 @@ def configs_report(only=""):
         dense(wl, n, W[wl]["tensors"][n], [1, 2, 4], [2, 4, 2048], (wl, n))
     if keep(wl):
         stacked_pair(wl, "gate+up (two-expert stack, ids {0,1})", W[wl]["tensors"]["gate"],
-                     ((wl, "gate"), (wl, "up")), gemm_Ts=(2048,))
+                     ((wl, "gate"), (wl, "up")), gemv_Ts=(2, 4, 16), gemm_Ts=(2048,))
         dequant_row(wl, "gate", W[wl]["tensors"]["gate"], (wl, "gate"))
     wl = "moe_e256_4096x1024_d4k256"
     for n in ("gate", "down") if keep(wl) else ():
